@@ -1,0 +1,177 @@
+"""Planted mistakes in the oracle must each fail at least one pin.
+
+Each mutation below is a copy of one oracle function with one plausible
+mistake (a dropped term, a wrong sign or index, a swapped operand, a wrong
+alignment).  It is swapped in with monkeypatch, on the CPU, and the full pin
+set is run: if every pin still passed, the pins would not be able to tell the
+mistake from the real thing.
+"""
+
+import numpy as np
+import pytest
+
+import oracle.attention as oa
+import oracle.metadata as om
+from tests import oracle_pins
+
+
+def _attend_factory(drop_scale=False, no_normalize=False, no_max=False,
+                    use_keys_as_values=False):
+    def attend(q_rows, keys, values, scale, visible):
+        rows = q_rows.shape[0]
+        n = keys.shape[0]
+        out = np.zeros((rows, values.shape[1]))
+        probs = np.zeros((rows, n))
+        if n == 0:
+            return out, probs
+        s = 1.0 if drop_scale else scale
+        logits = s * (q_rows @ keys.T)
+        with np.errstate(all="ignore"):
+            for r in range(rows):
+                m = int(visible[r])
+                if m == 0:
+                    continue
+                row = logits[r, :m]
+                e = np.exp(row if no_max else row - row.max())
+                p = e if no_normalize else e / e.sum()
+                probs[r, :m] = p
+                src = keys if use_keys_as_values else values
+                out[r] = p @ src[:m]
+        return out, probs
+    return attend
+
+
+def _gather_off_by_one(k_cache, v_cache, block_table, length, dtype):
+    bs = k_cache.shape[1]
+    keys = np.empty((length,) + k_cache.shape[2:])
+    values = np.empty((length,) + k_cache.shape[2:])
+    for t in range(length):
+        blk = int(block_table[t // bs])
+        off = (t + 1) % bs                      # planted: wrong offset
+        keys[t] = oa.to_f64(k_cache[blk, off], dtype)
+        values[t] = oa.to_f64(v_cache[blk, off], dtype)
+    return keys, values
+
+
+def _gather_physical_order(k_cache, v_cache, block_table, length, dtype):
+    bs = k_cache.shape[1]
+    used = sorted(int(b) for b in block_table[:-(-length // bs)])
+    keys = np.empty((length,) + k_cache.shape[2:])
+    values = np.empty((length,) + k_cache.shape[2:])
+    for t in range(length):
+        blk = used[t // bs]                     # planted: physical order
+        keys[t] = oa.to_f64(k_cache[blk, t % bs], dtype)
+        values[t] = oa.to_f64(v_cache[blk, t % bs], dtype)
+    return keys, values
+
+
+def _decode_gqa_modulo(q, k_cache, v_cache, block_tables, context_lens,
+                       scale, dtype, return_probs=False, seqs=None):
+    q64 = oa.to_f64(q, dtype)
+    bcount, hq, d = q64.shape
+    hkv = k_cache.shape[2]
+    out = np.zeros((bcount, hq, d))
+    probs_all = [None] * bcount
+    for b in range(bcount):
+        length = int(context_lens[b])
+        probs = np.zeros((hq, length))
+        if length:
+            keys, values = oa.gather_sequence_kv(k_cache, v_cache,
+                                                 block_tables[b], length,
+                                                 dtype)
+            for h in range(hq):
+                g = h % hkv                         # planted: wrong mapping
+                o, p = oa.attend(q64[b, h][None], keys[:, g], values[:, g],
+                                 scale, [length])
+                out[b, h] = o[0]
+                probs[h] = p[0]
+        probs_all[b] = probs
+    return (out, probs_all) if return_probs else out
+
+
+def _prefill_top_left(q, k_cache, v_cache, cu_q, cu_k, block_tables, scale,
+                      causal, dtype, seqs=None, rows=None):
+    q64 = oa.to_f64(q, dtype)
+    total, hq, d = q64.shape
+    hkv = k_cache.shape[2]
+    group = hq // hkv
+    out = np.zeros((total, hq, d))
+    for b in range(len(cu_q) - 1):
+        q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+        lq, lk = q1 - q0, int(cu_k[b + 1]) - int(cu_k[b])
+        if lq == 0:
+            continue
+        keys, values = oa.gather_sequence_kv(k_cache, v_cache,
+                                             block_tables[b], lk, dtype)
+        vis = [i + 1 for i in range(lq)] if causal else [lk] * lq  # planted
+        for h in range(hq):
+            o, _ = oa.attend(q64[q0:q1, h], keys[:, h // group],
+                             values[:, h // group], scale, vis)
+            out[q0:q1, h] = o
+    return out
+
+
+_ORIG_DECODE_META = om.decode_metadata
+_ORIG_PREFILL_META = om.prefill_metadata
+
+
+def _decode_meta_no_minus_one(seqs, block_size):
+    meta = _ORIG_DECODE_META(seqs, block_size)
+    meta["slot_mapping"] = [s + 1 for s in meta["slot_mapping"]]  # planted
+    return meta
+
+
+def _prefill_meta_cu_k_wrong(seqs, block_size):
+    meta = _ORIG_PREFILL_META(seqs, block_size)
+    cu_k = [0]
+    for s in seqs:                                   # planted: k = q lengths
+        cu_k.append(cu_k[-1] + s["num_scheduled"])
+    meta["cu_seqlens_k"] = cu_k
+    meta["needs_block_tables"] = cu_k[-1] > meta["cu_seqlens_q"][-1]
+    return meta
+
+
+def _store_no_skip(k_cache, v_cache, k, v, slot_mapping):
+    k_out = np.array(k_cache, copy=True)
+    v_out = np.array(v_cache, copy=True)
+    nb, bs = k_out.shape[:2]
+    fk = k_out.reshape(nb * bs, *k_out.shape[2:])
+    fv = v_out.reshape(nb * bs, *v_out.shape[2:])
+    for t, slot in enumerate(list(slot_mapping)):
+        fk[slot] = k[t]                              # planted: no skip
+        fv[slot] = v[t]
+    return k_out, v_out
+
+
+def _blocks_floor(num_tokens, block_size):
+    return num_tokens // block_size                  # planted: floor
+
+
+MUTATIONS = {
+    "drop_scale": (oa, "attend", _attend_factory(drop_scale=True)),
+    "no_normalize": (oa, "attend", _attend_factory(no_normalize=True)),
+    "no_max_subtract": (oa, "attend", _attend_factory(no_max=True)),
+    "keys_as_values": (oa, "attend", _attend_factory(use_keys_as_values=True)),
+    "gather_offset": (oa, "gather_sequence_kv", _gather_off_by_one),
+    "gather_physical_order": (oa, "gather_sequence_kv",
+                              _gather_physical_order),
+    "gqa_modulo": (oa, "decode_attention", _decode_gqa_modulo),
+    "causal_top_left": (oa, "prefill_attention", _prefill_top_left),
+    "decode_slot": (om, "decode_metadata", _decode_meta_no_minus_one),
+    "prefill_cu_k": (om, "prefill_metadata", _prefill_meta_cu_k_wrong),
+    "store_no_skip": (oa, "store_kv", _store_no_skip),
+    "blocks_floor": (om, "blocks_needed", _blocks_floor),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    module, attr, bad = MUTATIONS[name]
+    monkeypatch.setattr(module, attr, bad)
+    failed = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check()
+        except Exception as exc:  # noqa: BLE001 - any failure counts
+            failed.append((check.__name__, type(exc).__name__))
+    assert failed, f"planted mistake {name!r} passed every pin"
