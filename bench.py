@@ -1,0 +1,208 @@
+"""Benchmark of the paged KV-cache hot path on one MI355X.
+
+One step = one decode step of an 8B-shaped attention layer: pa_store_kv of
+the 256 newest K/V rows (one per sequence), then pa_decode of 256 sequences
+with contexts uniform in [512, 8192], 32 query / 8 KV heads, head_dim 128,
+bf16, block size 16 -- on one HIP stream, inputs resident in HBM.
+
+Prints one JSON line.  ``value`` is the step's algorithmic HBM throughput in
+TB/s (KV bytes the decode must read + q/out/block ids + the store's bytes,
+over the step time); ``tokens_per_s`` is sequences decoded per second for
+this one layer.  ``roofline`` covers pa_decode (partition + merge kernels)
+timed with HIP events on its stream inside the timed region;
+``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
+sequences on the host cores.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+WORKLOAD = "decode8b"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget for the oracle CPU baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counters", default=os.environ.get("PA_BENCH_COUNTERS"),
+                    help="JSON file with FETCH_SIZE/WRITE_SIZE per launch "
+                         "(KiB) of the decode partition kernel")
+    return ap.parse_args()
+
+
+def decode_bytes(lens, hq, hkv, d, elem, bs=16):
+    row = 2 * hkv * d * elem
+    kv = int(sum(int(n) for n in lens)) * row
+    qo = len(lens) * hq * d * elem * 2
+    ids = 4 * int(sum(-(-int(n) // bs) for n in lens)) + 4 * len(lens)
+    return kv + qo + ids
+
+
+def cpu_baseline(case_tables, lens, h_q, h_kc, h_vc, hq, scale, budget_s):
+    """Time the oracle on whole sequences until ~budget_s seconds pass."""
+    import numpy as np
+    import oracle.attention as oa
+    import oracle.metadata as om
+    order = np.random.default_rng(0).permutation(len(lens)).tolist()
+    done, seqs_bytes, t0 = 0, 0, time.perf_counter()
+    for b in order:
+        meta = om.decode_metadata([{"block_table": [int(x) for x in
+                                                    case_tables[b]],
+                                    "length": int(lens[b])}], 16)
+        oa.decode_attention(h_q[b:b + 1], h_kc, h_vc, meta["block_tables"],
+                            meta["context_lens"], scale, "bf16")
+        done += 1
+        seqs_bytes += int(lens[b])
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return done, seqs_bytes, dt
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from paged_kv_cache_slot_amd import metadata as pm
+    from paged_kv_cache_slot_amd import ops
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    cfg = wl.get_config(WORKLOAD)
+    lay = wl.config_decode_layout(cfg)
+    hq, hkv, d, bs = cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, 16
+    b = len(lay.lens)
+    elem = 2
+    print(f"[bench] workload {cfg.title}; pool {lay.num_blocks} blocks",
+          file=sys.stderr, flush=True)
+
+    kc, vc = wl.fill_pool(lay.num_blocks, bs, hkv, d, "bf16", cfg.seed, dev)
+    q = wl.make_values((b, hq, d), "bf16", cfg.seed + 1, dev)
+    k_new = wl.make_values((b, hkv, d), "bf16", cfg.seed + 2, dev)
+    v_new = wl.make_values((b, hkv, d), "bf16", cfg.seed + 3, dev)
+    meta = pm.decode_inputs(lay.tables, lay.lens, bs)
+    slot = torch.as_tensor(meta["slot_mapping"], device=dev)
+    bt = torch.as_tensor(meta["block_tables"], device=dev)
+    cl = torch.as_tensor(meta["context_lens"], device=dev)
+    maxlen = meta["max_context_len"]
+    scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q)
+    ws_bytes = ops.decode_workspace_bytes(b, hq, hkv, d, maxlen)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        ops.store_kv(k_new, v_new, kc, vc, slot)
+        if ev is not None:
+            ev[0].record()
+        ops.decode(q, kc, vc, bt, cl, maxlen, scale=scale, out=out,
+                   workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        step(events[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = start.elapsed_time(stop) / args.steps
+    dec_ms = [e[0].elapsed_time(e[1]) for e in events]
+    dec_ms_avg = sum(dec_ms) / len(dec_ms)
+
+    dbytes = decode_bytes(lay.lens, hq, hkv, d, elem)
+    row = 2 * hkv * d * elem
+    sbytes = 2 * b * row + 4 * b
+    step_bytes = dbytes + sbytes
+    value_tbs = step_bytes / (step_ms * 1e-3) / 1e12
+    dec_gbs = dbytes / (dec_ms_avg * 1e-3) / 1e9
+
+    traffic = None
+    if args.counters and os.path.exists(args.counters):
+        with open(args.counters) as f:
+            traffic = json.load(f).get("traffic_bytes")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        # bounded oracle sample: host copies of the touched sequences' pool
+        h_kc = wl.host_bits(kc)
+        h_vc = wl.host_bits(vc)
+        h_q = wl.host_bits(q)
+        done, toks, dt = cpu_baseline(lay.tables, lay.lens, h_q, h_kc, h_vc,
+                                      hq, scale, args.cpu_seconds)
+        cpu_bytes = toks * row
+        cores = len(os.sched_getaffinity(0))
+        cpu = {"value": cpu_bytes / dt / 1e12, "unit": "TB/s",
+               "cores": cores, "kind": "oracle",
+               "tokens_per_s": done / dt,
+               "sample": f"{done} of {b} sequences ({toks} context tokens), "
+                         f"fp64 numpy oracle, {dt:.1f} s"}
+
+    line = {
+        "metric": "paged decode attention achieved HBM TB/s (% of peak) + "
+                  "decode tokens/s",
+        "value": round(value_tbs, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.title, "num_seqs": b,
+                   "context_lens": "uniform [512, 8192], seed 3",
+                   "heads_q_kv": [hq, hkv], "head_dim": d, "block_size": bs,
+                   "pool_blocks": lay.num_blocks},
+        "tokens_per_s": round(b / (step_ms * 1e-3), 1),
+        "frac_of_hbm_peak": round(value_tbs * 1e3 / HBM_PEAK_GBS, 4),
+        "decode_ms": round(dec_ms_avg, 4),
+        "roofline": {"kernel": "pa_decode (decode_partition_kernel + "
+                               "decode_merge_kernel)",
+                     "bound": "hbm", "achieved": round(dec_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes": dbytes},
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,201 @@
+/*
+ * pa.h -- C ABI of libpa, the MI355X (gfx950) paged KV-cache hot path.
+ *
+ * Three operations over a block-table-indexed KV cache:
+ *
+ *   pa_store_kv        scatter new K/V rows into their physical slots
+ *   pa_decode          one query row per sequence against its paged context
+ *   pa_prefill_varlen  packed variable-length (chunked) prefill, causal,
+ *                      history read through block tables
+ *
+ * Sources.  The data contract follows "3.6 ModelRunner, CUDA Graph, and
+ * benchmarks" (a source reading of nano-vllm): section 2 (prepare_prefill /
+ * prepare_decode: slot_mapping, cu_seqlens_q / cu_seqlens_k, max_seqlen_q /
+ * max_seqlen_k, context_lens, -1 padded block_tables), section 3 (the
+ * per-step attention context), section 4 (the cache tensor layout) and
+ * section 5 (padding: slot -1 writes nothing, context length 0 reads
+ * nothing, stale block-table entries are never read).  Paging itself is the
+ * "Warmup Guide -- Inference Serving Internals", Chapter 3.  The attention
+ * each row computes is out = softmax(scale * q K^T) V (the pages name the
+ * kernels but do not write the formula out).
+ *
+ * Layouts (all row-major, contiguous, element type `pa_dtype`):
+ *   q, out (decode)        [num_seqs, num_heads, head_dim]
+ *   q, out (prefill)       [total_q, num_heads, head_dim], sequences packed
+ *                          end to end as cu_seqlens_q says
+ *   k, v (store)           [num_tokens, num_kv_heads, head_dim]
+ *   k_cache, v_cache       [num_blocks, block_size, num_kv_heads, head_dim],
+ *                          i.e. flat [num_slots, num_kv_heads, head_dim] with
+ *                          slot = block_id * block_size + offset
+ *   block_tables           int32 [num_seqs, max_blocks_per_seq]; row b lists
+ *                          sequence b's physical blocks in logical order;
+ *                          entries past ceil(len / block_size) are padding
+ *                          (-1 or stale) and are never read
+ *
+ * GQA: query head h reads KV head h / (num_heads / num_kv_heads).
+ *
+ * Pointers.  Every tensor pointer is a device pointer, 16-byte aligned.  The
+ * caller owns every buffer; the library never allocates, frees, or keeps a
+ * pointer after the call returns.  Scratch space is a caller-provided
+ * workspace sized by the *_workspace_bytes queries.
+ *
+ * Streams.  Every call only enqueues work on `stream` (a hipStream_t; NULL
+ * is the default stream) and returns; it never synchronises, allocates or
+ * copies to the host, so it can be captured in a HIP graph.  Ordering
+ * between calls (store before attend) is the caller's, by stream order.
+ *
+ * Errors.  Host-side checks of the scalar arguments return a status code;
+ * nothing aborts and nothing throws across the ABI.  Device-side data
+ * (slots, block ids, lengths, cu_seqlens) are preconditions -- see each
+ * call -- but the kernels clamp or skip values that would address memory
+ * outside the buffers described by the scalar arguments, so a violated
+ * precondition gives wrong numbers, never an out-of-bounds access.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,         /* a required pointer is NULL                    */
+  PA_ERR_SHAPE = 2,        /* a size is negative / inconsistent             */
+  PA_ERR_UNSUPPORTED = 3,  /* head_dim, block_size, GQA ratio, dtype or
+                              pointer alignment not supported               */
+  PA_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than the query says */
+  PA_ERR_LAUNCH = 5        /* the HIP runtime rejected a kernel launch      */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* pa_status_string(pa_status status);
+
+/* ABI version of this header; bumps on any signature change. */
+int32_t pa_abi_version(void);
+
+/*
+ * pa_store_kv -- write new K/V rows into the cache at their slots.
+ *
+ * For every t in [0, num_tokens): if slot_mapping[t] >= 0, the whole row
+ * k[t] (num_kv_heads * head_dim elements) is copied bit for bit to flat slot
+ * slot_mapping[t] of k_cache, and v[t] likewise to v_cache.  A negative slot
+ * (batch padding) writes nothing.  ModelRunner page, sections 2 and 5.
+ *
+ *   k, v          device, [num_tokens, num_kv_heads, head_dim]
+ *   k_cache,
+ *   v_cache       device, [num_slots, num_kv_heads, head_dim] (any block size)
+ *   slot_mapping  device int32 [num_tokens]
+ *   num_slots     num_blocks * block_size of the cache
+ *
+ * Preconditions: non-negative slots are distinct (a duplicate leaves one of
+ * the rows, unspecified which).  Slots >= num_slots are skipped.
+ * Requires num_kv_heads * head_dim * element size to be a multiple of 16.
+ * num_tokens == 0 is a no-op returning PA_OK.
+ */
+pa_status pa_store_kv(const void* k, const void* v, void* k_cache,
+                      void* v_cache, const int32_t* slot_mapping,
+                      int64_t num_tokens, int32_t num_kv_heads,
+                      int32_t head_dim, int64_t num_slots, pa_dtype dtype,
+                      void* stream);
+
+/*
+ * Bytes of workspace pa_decode needs for these sizes (0 when one context
+ * partition covers max_context_len and no merge pass is needed).
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_context_len);
+
+/*
+ * pa_decode -- decode attention over a paged cache.
+ *
+ * For sequence b with L = context_lens[b] (the count includes the token being
+ * decoded, whose K/V the caller stored first) and each query head h:
+ *   out[b, h] = softmax_j(scale * q[b, h] . K_b[j]) V_b[j],  j in [0, L)
+ * where K_b[j] is k_cache[block_tables[b, j / block_size], j % block_size,
+ * h / G] and G = num_heads / num_kv_heads.  L == 0 (batch padding) gives a
+ * zero row.  ModelRunner page, section 2 (prepare_decode) and section 5.
+ *
+ * Split-context: the context is cut into fixed partitions processed in
+ * parallel, each keeping its own running max and sum; a second pass merges
+ * the partitions (the merge is skipped when one partition covers
+ * max_context_len).
+ *
+ *   out, q         device, [num_seqs, num_heads, head_dim]
+ *   k_cache,
+ *   v_cache        device, [num_blocks, block_size, num_kv_heads, head_dim]
+ *   block_tables   device int32 [num_seqs, max_blocks_per_seq]
+ *   context_lens   device int32 [num_seqs]
+ *   max_context_len  host-known upper bound of context_lens (sizes the grid
+ *                  without a device-to-host copy)
+ *   workspace      device, >= pa_decode_workspace_bytes(...) bytes (may be
+ *                  NULL when that is 0); contents on entry do not matter
+ *
+ * Supported: head_dim in {64, 128}; block_size == 16; num_heads /
+ * num_kv_heads in {1, 2, 4, 8}; dtype F32 or BF16 (fp32 accumulation,
+ * bf16 output rounded to nearest even).
+ * Preconditions: context_lens[b] <= max_context_len and
+ * <= max_blocks_per_seq * block_size (larger values are clamped); the first
+ * ceil(L / block_size) block ids of row b lie in [0, num_blocks) (an id
+ * outside that range contributes nothing).
+ */
+pa_status pa_decode(void* out, const void* q, const void* k_cache,
+                    const void* v_cache, int64_t num_blocks,
+                    int32_t block_size, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* context_lens,
+                    int32_t max_context_len, int32_t num_seqs,
+                    int32_t num_heads, int32_t num_kv_heads,
+                    int32_t head_dim, float scale, void* workspace,
+                    size_t workspace_bytes, pa_dtype dtype, void* stream);
+
+/* Bytes of workspace pa_prefill_varlen needs for these sizes. */
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_seqlen_q, int32_t max_seqlen_k);
+
+/*
+ * pa_prefill_varlen -- varlen (chunked) prefill attention, K/V read from the
+ * paged cache.
+ *
+ * Sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ * (Lq rows) and Lk = cu_seqlens_k[b+1] - cu_seqlens_k[b] keys, the first Lk
+ * tokens of its block table (history and this round's tokens, which the
+ * caller stored first).  With causal != 0 query row i sits at absolute
+ * position Lk - Lq + i and sees keys 0 .. Lk - Lq + i (bottom-right
+ * alignment: a chunk continues after its cached history); otherwise every
+ * row sees all Lk keys.  ModelRunner page, section 2 (prepare_prefill), and
+ * "10 Serving Engines", section 10.3 (chunked prefill).
+ *
+ *   out, q          device, [total_q, num_heads, head_dim]
+ *   cu_seqlens_q/k  device int32 [num_seqs + 1], non-decreasing, from 0
+ *   max_seqlen_q/k  host-known upper bounds of Lq / Lk
+ *   block_tables    device int32 [num_seqs, max_blocks_per_seq]
+ *   workspace       device, >= pa_prefill_workspace_bytes(...) bytes
+ *
+ * Supported: as pa_decode.  Preconditions: Lq <= Lk when causal; Lq <=
+ * max_seqlen_q, Lk <= max_seqlen_k and <= max_blocks_per_seq * block_size
+ * (larger values are clamped); rows past total_q are never touched.
+ */
+pa_status pa_prefill_varlen(void* out, const void* q, int64_t total_q,
+                            const void* k_cache, const void* v_cache,
+                            int64_t num_blocks, int32_t block_size,
+                            const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, int32_t max_seqlen_q,
+                            int32_t max_seqlen_k, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, int32_t num_seqs,
+                            int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, float scale, int32_t causal,
+                            void* workspace, size_t workspace_bytes,
+                            pa_dtype dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,206 @@
+// C ABI of libpa: host-side validation of scalar arguments, then dispatch to
+// the kernel launchers.  Declarations and the contract live in include/pa.h.
+#include "../../include/pa.h"
+
+#include <hip/hip_runtime.h>
+
+#include "pa_internal.h"
+
+namespace {
+
+constexpr int32_t kAbiVersion = 1;
+
+bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+int elem_bytes(pa_dtype dtype) { return dtype == PA_BF16 ? 2 : 4; }
+
+bool dtype_ok(pa_dtype dtype) { return dtype == PA_F32 || dtype == PA_BF16; }
+
+bool group_ok(int32_t num_heads, int32_t num_kv_heads) {
+  if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return false;
+  const int g = num_heads / num_kv_heads;
+  return g == 1 || g == 2 || g == 4 || g == 8;
+}
+
+// Shared checks of the attention entry points.
+pa_status check_attention(int32_t block_size, int32_t num_seqs,
+                          int32_t num_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t max_blocks_per_seq,
+                          int64_t num_blocks, pa_dtype dtype) {
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_blocks_per_seq < 0 || num_blocks < 0 || block_size <= 0)
+    return PA_ERR_SHAPE;
+  if (num_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (block_size != 16) return PA_ERR_UNSUPPORTED;
+  if (!group_ok(num_heads, num_kv_heads)) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: a size is negative or inconsistent";
+    case PA_ERR_UNSUPPORTED:
+      return "PA_ERR_UNSUPPORTED: head_dim, block_size, GQA ratio, dtype or "
+             "alignment not supported";
+    case PA_ERR_WORKSPACE:
+      return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: kernel launch failed";
+  }
+  return "PA_ERR_?: unknown status";
+}
+
+int32_t pa_abi_version(void) { return kAbiVersion; }
+
+pa_status pa_store_kv(const void* k, const void* v, void* k_cache,
+                      void* v_cache, const int32_t* slot_mapping,
+                      int64_t num_tokens, int32_t num_kv_heads,
+                      int32_t head_dim, int64_t num_slots, pa_dtype dtype,
+                      void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_slots < 0)
+    return PA_ERR_SHAPE;
+  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
+  const int64_t row_bytes =
+      static_cast<int64_t>(num_kv_heads) * head_dim * elem_bytes(dtype);
+  if (row_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return PA_ERR_UNSUPPORTED;
+  hipError_t e = pa::launch_store_kv(k, v, k_cache, v_cache, slot_mapping,
+                                     num_tokens, row_bytes, num_slots,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_context_len) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0)
+    return 0;
+  return pa::plan_decode(num_seqs, num_heads, num_kv_heads, head_dim,
+                         max_context_len)
+      .workspace_bytes;
+}
+
+pa_status pa_decode(void* out, const void* q, const void* k_cache,
+                    const void* v_cache, int64_t num_blocks,
+                    int32_t block_size, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* context_lens,
+                    int32_t max_context_len, int32_t num_seqs,
+                    int32_t num_heads, int32_t num_kv_heads,
+                    int32_t head_dim, float scale, void* workspace,
+                    size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  pa_status st = check_attention(block_size, num_seqs, num_heads, num_kv_heads,
+                                 head_dim, max_blocks_per_seq, num_blocks,
+                                 dtype);
+  if (st != PA_OK) return st;
+  if (max_context_len < 0) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !context_lens) return PA_ERR_NULL;
+  if (max_context_len > 0 && (!k_cache || !v_cache || !block_tables))
+    return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return PA_ERR_UNSUPPORTED;
+  pa::DecodePlan plan = pa::plan_decode(num_seqs, num_heads, num_kv_heads,
+                                        head_dim, max_context_len);
+  if (plan.workspace_bytes > 0 &&
+      (!workspace || workspace_bytes < plan.workspace_bytes))
+    return PA_ERR_WORKSPACE;
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_blocks = num_blocks;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.max_context_len = max_context_len;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.scale = scale;
+  a.workspace = workspace;
+  a.bf16 = dtype == PA_BF16;
+  hipError_t e = pa::launch_decode(a, plan, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_seqlen_q, int32_t max_seqlen_k) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_seqlen_q <= 0 || max_seqlen_k <= 0)
+    return 0;
+  return pa::prefill_workspace_bytes(num_seqs, num_heads, num_kv_heads,
+                                     head_dim, max_seqlen_q, max_seqlen_k);
+}
+
+pa_status pa_prefill_varlen(void* out, const void* q, int64_t total_q,
+                            const void* k_cache, const void* v_cache,
+                            int64_t num_blocks, int32_t block_size,
+                            const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, int32_t max_seqlen_q,
+                            int32_t max_seqlen_k, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, int32_t num_seqs,
+                            int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, float scale, int32_t causal,
+                            void* workspace, size_t workspace_bytes,
+                            pa_dtype dtype, void* stream) {
+  pa_status st = check_attention(block_size, num_seqs, num_heads, num_kv_heads,
+                                 head_dim, max_blocks_per_seq, num_blocks,
+                                 dtype);
+  if (st != PA_OK) return st;
+  if (total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return PA_OK;
+  if (!out || !q || !cu_seqlens_q || !cu_seqlens_k) return PA_ERR_NULL;
+  if (max_seqlen_k > 0 && (!k_cache || !v_cache || !block_tables))
+    return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return PA_ERR_UNSUPPORTED;
+  const size_t need = pa_prefill_workspace_bytes(
+      num_seqs, num_heads, num_kv_heads, head_dim, max_seqlen_q, max_seqlen_k);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return PA_ERR_WORKSPACE;
+  pa::PrefillArgs a{};
+  a.out = out;
+  a.q = q;
+  a.total_q = total_q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_blocks = num_blocks;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.cu_seqlens_k = cu_seqlens_k;
+  a.max_seqlen_q = max_seqlen_q;
+  a.max_seqlen_k = max_seqlen_k;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  a.bf16 = dtype == PA_BF16;
+  hipError_t e = pa::launch_prefill(a, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// Device helpers shared by the gfx950 kernels of libpa.
+//
+// Element types: float, and bfloat16 carried as its raw 16 bits (uint16_t).
+// A bfloat16 is the high half of a float32, so widening is a shift; packed
+// pairs of bfloat16 in one dword feed v_dot2_f32_bf16 directly.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+
+struct bf16_t {
+  uint16_t bits;
+};
+
+template <typename T>
+struct ElemTraits;
+template <>
+struct ElemTraits<float> {
+  static constexpr int kBytes = 4;
+};
+template <>
+struct ElemTraits<bf16_t> {
+  static constexpr int kBytes = 2;
+};
+
+// Low / high bfloat16 of a packed dword, widened exactly to float.
+__device__ __forceinline__ float bf16_lo(uint32_t w) {
+  return __uint_as_float(w << 16);
+}
+__device__ __forceinline__ float bf16_hi(uint32_t w) {
+  return __uint_as_float(w & 0xffff0000u);
+}
+
+// float -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// dot of two packed bfloat16 pairs, accumulated in float (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), acc,
+                                         false);
+}
+
+// DPP quad permutations: lane i of each group of 4 reads lane perm[i].
+// Control byte = sel0 | sel1 << 2 | sel2 << 4 | sel3 << 6.
+constexpr int kQuadSwap1 = 0xB1;  // [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;  // [2,3,0,1]
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(
+      __builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, true));
+}
+
+// Sum over the 4 lanes of a quad; every lane of the quad gets the total.
+__device__ __forceinline__ float quad_sum(float x) {
+  x += dpp_f32<kQuadSwap1>(x);
+  x += dpp_f32<kQuadSwap2>(x);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+
+// 2^x (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) {
+  return __builtin_amdgcn_exp2f(x);
+}
+
+// 16-byte global load / store.
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, uint4 v) {
+  *reinterpret_cast<uint4*>(p) = v;
+}
+
+}  // namespace pa

@@ -1,0 +1,81 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernel
+// translation units.  Arguments are already validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+// ---- store -------------------------------------------------------------
+hipError_t launch_store_kv(const void* k, const void* v, void* k_cache,
+                           void* v_cache, const int32_t* slot_mapping,
+                           int64_t num_tokens, int64_t row_bytes,
+                           int64_t num_slots, hipStream_t stream);
+
+// ---- decode ------------------------------------------------------------
+struct DecodePlan {
+  int partition_tokens;  // tokens per context partition (multiple of 64)
+  int num_partitions;    // ceil(max_context_len / partition_tokens), >= 1
+  size_t workspace_bytes;
+  size_t off_max, off_sum, off_acc;  // byte offsets inside the workspace
+};
+
+DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads,
+                       int head_dim, int max_context_len);
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  int64_t num_blocks;
+  const int32_t* block_tables;
+  int max_blocks_per_seq;
+  const int32_t* context_lens;
+  int max_context_len;
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int head_dim;
+  float scale;
+  void* workspace;
+  bool bf16;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan,
+                         hipStream_t stream);
+
+// ---- prefill -----------------------------------------------------------
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  int64_t total_q;
+  const void* k_cache;
+  const void* v_cache;
+  int64_t num_blocks;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  int max_seqlen_q;
+  int max_seqlen_k;
+  const int32_t* block_tables;
+  int max_blocks_per_seq;
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int head_dim;
+  float scale;
+  bool causal;
+  void* workspace;
+  size_t workspace_bytes;
+  bool bf16;
+};
+
+size_t prefill_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads,
+                               int head_dim, int max_seqlen_q,
+                               int max_seqlen_k);
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,165 @@
+"""Torch-tensor front end of libpa: argument marshalling only.
+
+Each function checks that the tensors are on the GPU, contiguous and of the
+types the C ABI expects, takes their device pointers and the current HIP
+stream, and calls the library.  All computation happens in the HIP kernels;
+there is no CPU fallback.  Outputs and workspaces are allocated with torch
+when the caller does not pass them.
+"""
+
+import math
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float32: _lib.PA_F32, torch.bfloat16: _lib.PA_BF16}
+
+
+def _dtype_code(t):
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32 or "
+                        "bfloat16") from None
+
+
+def _need_gpu(*tensors):
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("libpa operates on GPU tensors only")
+        if not t.is_contiguous():
+            raise ValueError("libpa needs contiguous tensors")
+
+
+def _i32(t, name):
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+    return t
+
+
+def _stream(t):
+    return ctypes_void(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def ctypes_void(x):
+    return x if x else None
+
+
+def _ptr(t):
+    return t.data_ptr() if t is not None and t.numel() else None
+
+
+def store_kv(k, v, k_cache, v_cache, slot_mapping):
+    """Write rows of k / v ([T, Hkv, D]) to flat slots of the caches
+    ([NB, bs, Hkv, D]); negative slots are skipped."""
+    _need_gpu(k, v, k_cache, v_cache, slot_mapping)
+    _i32(slot_mapping, "slot_mapping")
+    if k.shape != v.shape or k.dim() != 3:
+        raise ValueError("k and v must both be [T, Hkv, D]")
+    if k_cache.shape != v_cache.shape or k_cache.dim() != 4:
+        raise ValueError("caches must be [NB, bs, Hkv, D]")
+    if tuple(k_cache.shape[2:]) != tuple(k.shape[1:]):
+        raise ValueError("cache row shape differs from k/v row shape")
+    if k.dtype != k_cache.dtype or v.dtype != k.dtype:
+        raise TypeError("k, v and caches must share a dtype")
+    if slot_mapping.numel() != k.shape[0]:
+        raise ValueError("slot_mapping must have one entry per row")
+    lib = _lib.load()
+    st = lib.pa_store_kv(_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache),
+                         _ptr(slot_mapping), k.shape[0], k.shape[1],
+                         k.shape[2], k_cache.shape[0] * k_cache.shape[1],
+                         _dtype_code(k), _stream(k))
+    _lib.check("pa_store_kv", st)
+
+
+def decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                           max_context_len):
+    return int(_lib.load().pa_decode_workspace_bytes(
+        num_seqs, num_heads, num_kv_heads, head_dim, max_context_len))
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+           scale=None, out=None, workspace=None):
+    """Paged decode attention.  q [B, Hq, D]; caches [NB, 16, Hkv, D];
+    block_tables int32 [B, W]; context_lens int32 [B] (counting the new
+    token); max_context_len a host-side upper bound.  Returns out [B, Hq, D].
+    """
+    _need_gpu(q, k_cache, v_cache, block_tables, context_lens, out, workspace)
+    _i32(block_tables, "block_tables")
+    _i32(context_lens, "context_lens")
+    b, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if d2 != d or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shape does not match q")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b:
+        raise ValueError("block_tables must be [B, W]")
+    if context_lens.numel() != b:
+        raise ValueError("context_lens must be [B]")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and caches must share a dtype")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    need = decode_workspace_bytes(b, hq, hkv, d, max_context_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() \
+        if workspace is not None else 0
+    lib = _lib.load()
+    st = lib.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), nb,
+                       bs, _ptr(block_tables), block_tables.shape[1],
+                       _ptr(context_lens), int(max_context_len), b, hq, hkv,
+                       d, scale, _ptr(workspace), ws_bytes, _dtype_code(q),
+                       _stream(q))
+    _lib.check("pa_decode", st)
+    return out
+
+
+def prefill_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                            max_seqlen_q, max_seqlen_k):
+    return int(_lib.load().pa_prefill_workspace_bytes(
+        num_seqs, num_heads, num_kv_heads, head_dim, max_seqlen_q,
+        max_seqlen_k))
+
+
+def prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k,
+                   max_seqlen_q, max_seqlen_k, block_tables, scale=None,
+                   causal=True, out=None, workspace=None):
+    """Varlen chunked prefill.  q [total_q, Hq, D] packed by cu_seqlens_q;
+    keys are the first cu_seqlens_k[b+1]-cu_seqlens_k[b] tokens of each
+    sequence's block table.  Returns out [total_q, Hq, D]."""
+    _need_gpu(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_tables,
+              out, workspace)
+    for t, n in ((cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k"),
+                 (block_tables, "block_tables")):
+        _i32(t, n)
+    total_q, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    num_seqs = cu_seqlens_q.numel() - 1
+    if d2 != d or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shape does not match q")
+    if cu_seqlens_k.numel() != num_seqs + 1 or block_tables.shape[0] != num_seqs:
+        raise ValueError("cu_seqlens_k / block_tables do not match cu_seqlens_q")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and caches must share a dtype")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    need = prefill_workspace_bytes(num_seqs, hq, hkv, d, max_seqlen_q,
+                                   max_seqlen_k)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() \
+        if workspace is not None else 0
+    lib = _lib.load()
+    st = lib.pa_prefill_varlen(
+        _ptr(out), _ptr(q), total_q, _ptr(k_cache), _ptr(v_cache), nb, bs,
+        _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), int(max_seqlen_q),
+        int(max_seqlen_k), _ptr(block_tables), block_tables.shape[1],
+        num_seqs, hq, hkv, d, scale, 1 if causal else 0, _ptr(workspace),
+        ws_bytes, _dtype_code(q), _stream(q))
+    _lib.check("pa_prefill_varlen", st)
+    return out

@@ -1,0 +1,139 @@
+"""Builds GPU parity cases: the same seeded inputs go to the HIP path (through
+the package's metadata and the C ABI) and to the oracle (through the
+oracle's own metadata), and the results are compared.
+
+Nothing the HIP path computes is ever fed to the oracle: the oracle gets host
+copies of the generator's tensors taken *before* any kernel runs.
+"""
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import oracle.attention as oa
+import oracle.metadata as om
+import workloads as wl
+from paged_kv_cache_slot_amd import metadata as pm
+from paged_kv_cache_slot_amd import ops
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def say(*msg):
+    """Name the case before each GPU step (flushed, so a crash shows it)."""
+    print("[gpu-case]", *msg, file=sys.stderr, flush=True)
+
+
+def dev_i32(a, device="cuda"):
+    return torch.as_tensor(np.asarray(a, dtype=np.int32), device=device)
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def bits_equal(a, b):
+    return a.tobytes() == b.tobytes()
+
+
+class DecodeCase:
+    """One decode step: store each sequence's newest K/V row, then attend.
+
+    ``lay`` is a workloads.DecodeLayout; ``extra_pad`` appends that many
+    batch-padding rows (context 0, slot -1); ``stale_padding`` fills
+    block-table padding with ids of blocks no sequence owns (NaN blocks when
+    ``poison``)."""
+
+    def __init__(self, lay, hq, hkv, d, dtype, seed, poison=True,
+                 extra_pad=0, stale_padding=False, max_context_len=None,
+                 device="cuda"):
+        self.lay, self.hq, self.hkv, self.d = lay, hq, hkv, d
+        self.dtype = dtype
+        self.bs = lay.block_size
+        self.scale = 1.0 / math.sqrt(d)
+        tables = list(lay.tables) + [np.zeros(0, np.int64)] * extra_pad
+        lens = np.concatenate([lay.lens, np.zeros(extra_pad, np.int64)])
+        self.tables, self.lens = tables, lens
+        b = len(lens)
+        self.kc, self.vc = wl.fill_pool(lay.num_blocks, self.bs, hkv, d,
+                                        dtype, seed, device)
+        if poison:
+            mask = wl.valid_slot_mask(lay.num_blocks, self.bs, tables, lens)
+            wl.poison_unused(self.kc, self.vc, mask)
+        self.q = wl.make_values((b, hq, d), dtype, seed + 1, device)
+        self.k_new = wl.make_values((b, hkv, d), dtype, seed + 2, device)
+        self.v_new = wl.make_values((b, hkv, d), dtype, seed + 3, device)
+        # host copies for the oracle, taken before any kernel runs
+        self.h_kc = wl.host_bits(self.kc)
+        self.h_vc = wl.host_bits(self.vc)
+        self.h_q = wl.host_bits(self.q)
+        self.h_kn = wl.host_bits(self.k_new)
+        self.h_vn = wl.host_bits(self.v_new)
+        # HIP side: the package's metadata
+        meta = pm.decode_inputs(tables, lens, self.bs)
+        bt = meta["block_tables"]
+        if stale_padding:
+            used = set(np.concatenate([t for t in tables if len(t)]).tolist())
+            spare = [x for x in range(lay.num_blocks) if x not in used]
+            assert spare, "no spare block for stale padding"
+            bt = bt.copy()
+            bt[bt < 0] = spare[0]
+        self.meta = meta
+        self.slot_mapping = dev_i32(meta["slot_mapping"], device)
+        self.block_tables = dev_i32(bt, device)
+        self.context_lens = dev_i32(meta["context_lens"], device)
+        self.max_context_len = (meta["max_context_len"]
+                                if max_context_len is None else max_context_len)
+
+    # -- HIP path ---------------------------------------------------------
+    def run_store(self):
+        ops.store_kv(self.k_new, self.v_new, self.kc, self.vc,
+                     self.slot_mapping)
+
+    def run_decode(self, out=None, workspace=None):
+        return ops.decode(self.q, self.kc, self.vc, self.block_tables,
+                          self.context_lens, self.max_context_len,
+                          scale=self.scale, out=out, workspace=workspace)
+
+    # -- oracle -------------------------------------------------------------
+    def oracle_meta(self):
+        seqs = [{"block_table": [int(x) for x in t], "length": int(n)}
+                for t, n in zip(self.tables, self.lens) if n > 0]
+        return om.decode_metadata(seqs, self.bs)
+
+    def oracle_store(self):
+        om_meta = self.oracle_meta()
+        live = [i for i, n in enumerate(self.lens) if n > 0]
+        return oa.store_kv(self.h_kc, self.h_vc, self.h_kn[live],
+                           self.h_vn[live], om_meta["slot_mapping"])
+
+    def oracle_decode(self, kc, vc, seqs=None):
+        live = [i for i, n in enumerate(self.lens) if n > 0]
+        om_meta = self.oracle_meta()
+        # oracle rows of live sequences, scattered back to batch positions
+        sub = None
+        if seqs is not None:
+            pos = {b: j for j, b in enumerate(live)}
+            sub = [pos[b] for b in seqs if b in pos]
+        out_live = oa.decode_attention(self.h_q[live], kc, vc,
+                                       om_meta["block_tables"],
+                                       om_meta["context_lens"], self.scale,
+                                       self.dtype, seqs=sub)
+        out = np.zeros((len(self.lens), self.hq, self.d))
+        out[live] = out_live
+        return out
+
+
+def sample_seqs(lens, k, seed):
+    """Longest, shortest and k-2 random sequences."""
+    lens = np.asarray(lens)
+    rng = np.random.default_rng(seed)
+    pick = {int(np.argmax(lens)), int(np.argmin(lens))}
+    others = rng.permutation(len(lens)).tolist()
+    for b in others:
+        if len(pick) >= k:
+            break
+        pick.add(int(b))
+    return sorted(pick)

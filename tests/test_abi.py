@@ -1,0 +1,115 @@
+"""The C ABI library loads and exports every symbol include/pa.h declares;
+host-side argument validation returns the documented status codes.
+
+No test here reaches a kernel launch: every call either fails validation or
+is a documented no-op, so nothing touches a GPU (fake, aligned device
+addresses are never dereferenced on the host)."""
+
+import os
+import re
+
+import pytest
+
+from paged_kv_cache_slot_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include",
+                      "pa.h")
+FAKE = 1 << 20            # aligned non-NULL address, never dereferenced
+MISALIGNED = FAKE + 4
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    lib = _lib.load()
+    names = declared_symbols()
+    assert {"pa_store_kv", "pa_decode", "pa_prefill_varlen"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(_lib.SIGNATURES), "binding out of sync"
+
+
+def test_version_and_strings():
+    lib = _lib.load()
+    assert lib.pa_abi_version() == 1
+    for code, name in _lib.STATUS.items():
+        assert lib.pa_status_string(code).decode().startswith(name)
+    assert b"unknown" in lib.pa_status_string(99)
+
+
+def _decode(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, nb=64, bs=16, bt=FAKE, w=8,
+             cl=FAKE, maxlen=100, b=4, hq=8, hkv=2, d=64, scale=0.125,
+             ws=None, wsb=0, dtype=_lib.PA_F32, stream=None)
+    a.update(kw)
+    return lib.pa_decode(a["out"], a["q"], a["k"], a["v"], a["nb"], a["bs"],
+                         a["bt"], a["w"], a["cl"], a["maxlen"], a["b"],
+                         a["hq"], a["hkv"], a["d"], a["scale"], a["ws"],
+                         a["wsb"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), 3), (dict(d=0), 2), (dict(bs=32), 3), (dict(hq=6, hkv=4), 2),
+    (dict(hq=6, hkv=2), 3), (dict(hq=32, hkv=2), 3), (dict(dtype=7), 3),
+    (dict(b=-1), 2), (dict(maxlen=-5), 2), (dict(out=None), 1),
+    (dict(q=None), 1), (dict(cl=None), 1), (dict(bt=None), 1),
+    (dict(q=MISALIGNED), 3), (dict(k=MISALIGNED), 3),
+    (dict(maxlen=4096), 4),                       # needs a workspace
+    (dict(maxlen=4096, ws=FAKE, wsb=16), 4),       # workspace too small
+    (dict(b=0), 0),                                # empty batch: no-op
+])
+def test_decode_validation(kw, code):
+    assert _decode(_lib.load(), **kw) == code
+
+
+def test_decode_workspace_query():
+    lib = _lib.load()
+    assert lib.pa_decode_workspace_bytes(4, 8, 2, 64, 100) == 0
+    one = lib.pa_decode_workspace_bytes(256, 32, 8, 128, 8192)
+    assert one >= 256 * 32 * 16 * (128 + 2) * 4
+    assert lib.pa_decode_workspace_bytes(0, 8, 2, 64, 100) == 0
+
+
+def _store(lib, **kw):
+    a = dict(k=FAKE, v=FAKE, kc=FAKE, vc=FAKE, sm=FAKE, t=4, hkv=2, d=64,
+             s=1024, dtype=_lib.PA_F32, stream=None)
+    a.update(kw)
+    return lib.pa_store_kv(a["k"], a["v"], a["kc"], a["vc"], a["sm"], a["t"],
+                           a["hkv"], a["d"], a["s"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(t=-1), 2), (dict(hkv=0), 2), (dict(s=-1), 2), (dict(dtype=5), 3),
+    (dict(k=None), 1), (dict(sm=None), 1), (dict(vc=MISALIGNED), 3),
+    (dict(hkv=1, d=2), 3),                         # 8-byte rows
+    (dict(t=0), 0), (dict(t=0, k=None), 0),        # nothing to store
+])
+def test_store_validation(kw, code):
+    assert _store(_lib.load(), **kw) == code
+
+
+def _prefill(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, tq=16, k=FAKE, v=FAKE, nb=64, bs=16, cuq=FAKE,
+             cuk=FAKE, mq=8, mk=40, bt=FAKE, w=4, b=2, hq=8, hkv=2, d=128,
+             scale=0.1, causal=1, ws=None, wsb=0, dtype=_lib.PA_BF16,
+             stream=None)
+    a.update(kw)
+    return lib.pa_prefill_varlen(
+        a["out"], a["q"], a["tq"], a["k"], a["v"], a["nb"], a["bs"], a["cuq"],
+        a["cuk"], a["mq"], a["mk"], a["bt"], a["w"], a["b"], a["hq"],
+        a["hkv"], a["d"], a["scale"], a["causal"], a["ws"], a["wsb"],
+        a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=80), 3), (dict(bs=8), 3), (dict(hq=12, hkv=3), 3),
+    (dict(tq=-1), 2), (dict(mq=-2), 2), (dict(out=None), 1),
+    (dict(cuq=None), 1), (dict(bt=None), 1), (dict(q=MISALIGNED), 3),
+    (dict(b=0), 0), (dict(tq=0), 0), (dict(mq=0), 0),
+])
+def test_prefill_validation(kw, code):
+    assert _prefill(_lib.load(), **kw) == code

@@ -1,0 +1,133 @@
+"""pa_store_kv + pa_decode on the GPU against the oracle.
+
+Every case poisons all cache slots outside any context with NaN, so reading
+padding or masking by multiplying with zero shows up as a non-finite output.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from tests.gpu_harness import (TOL, DecodeCase, bits_equal, f64, sample_seqs,
+                               say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(case, seqs=None, check_store=True):
+    case.run_store()
+    out = case.run_decode()
+    torch.cuda.synchronize()
+    ek, ev = case.oracle_store()
+    if check_store:
+        assert bits_equal(wl.host_bits(case.kc), ek), "store mismatch"
+        assert bits_equal(wl.host_bits(case.vc), ev), "store mismatch"
+    want = case.oracle_decode(ek, ev, seqs=seqs)
+    got = f64(out)
+    rows = range(len(case.lens)) if seqs is None else seqs
+    rows = list(rows)
+    assert np.all(np.isfinite(got[rows]))
+    err = np.max(np.abs(got[rows] - want[rows]))
+    assert err <= TOL[case.dtype], f"max abs err {err}"
+    return got, want
+
+
+def test_tiny_decode():
+    """4 seqs, ctx {7,16,33,100}, 8q/2kv, D=64, fp32, pool of 64 blocks."""
+    cfg = wl.get_config("tiny")
+    say("decode tiny")
+    lay = wl.config_decode_layout(cfg)
+    case = DecodeCase(lay, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim,
+                      cfg.dtype, seed=cfg.seed)
+    _check(case)
+
+
+def test_small_decode_full():
+    """64 seqs, ctx U[128,4096], 16q/8kv, D=128, bf16: every row."""
+    cfg = wl.get_config("small")
+    say("decode small (full)")
+    lay = wl.config_decode_layout(cfg)
+    case = DecodeCase(lay, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim,
+                      cfg.dtype, seed=cfg.seed)
+    _check(case)
+
+
+@pytest.mark.parametrize("key", ["decode8b", "prefix"])
+def test_full_size_decode_sampled(key):
+    """Full-size pools and grids as the bench runs them; the oracle checks
+    sampled sequences (longest, shortest, random)."""
+    cfg = wl.get_config(key)
+    say("decode full-size sampled", key)
+    lay = wl.config_decode_layout(cfg)
+    case = DecodeCase(lay, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim,
+                      cfg.dtype, seed=cfg.seed)
+    _check(case, seqs=sample_seqs(lay.lens, 12, cfg.seed))
+
+
+@pytest.mark.parametrize("dtype,d,hq,hkv", [
+    ("f32", 64, 8, 2), ("f32", 128, 4, 4), ("bf16", 64, 16, 2),
+    ("bf16", 128, 8, 8), ("bf16", 128, 32, 8), ("f32", 128, 16, 2),
+])
+def test_edge_lengths(dtype, d, hq, hkv):
+    """Lengths at block and partition edges (1, 15, 16, 17, 511, 512, 513,
+    1024, 1500) in every supported dtype / head_dim / GQA ratio."""
+    say("decode edges", dtype, d, hq, hkv)
+    lens = [1, 15, 16, 17, 511, 512, 513, 1024, 1500]
+    lay = wl.decode_layout(lens, 16, seed=31)
+    case = DecodeCase(lay, hq, hkv, d, dtype, seed=41)
+    _check(case)
+
+
+def test_one_key_returns_v_exactly():
+    """Context of one token: the output is that token's V, bit for bit."""
+    say("decode one-key")
+    lay = wl.decode_layout([1, 1, 1], 16, seed=5)
+    for dtype in ("f32", "bf16"):
+        case = DecodeCase(lay, 8, 2, 128, dtype, seed=6)
+        case.run_store()
+        out = case.run_decode()
+        torch.cuda.synchronize()
+        v_new = wl.host_bits(case.v_new)     # [B, Hkv, D]
+        got = wl.host_bits(out)              # [B, Hq, D]
+        for h in range(8):
+            assert bits_equal(got[:, h], v_new[:, h // 4])
+
+
+def test_padding_rows_and_stale_tables():
+    """Batch padding (context 0, slot -1) gives zero rows; block-table
+    padding that names real (NaN-filled) blocks is never read; a grid sized
+    for a longer max_context_len than any row changes nothing."""
+    say("decode padding / stale / oversize grid")
+    lay = wl.decode_layout([100, 700, 33], 16, seed=8)
+    base = DecodeCase(lay, 8, 2, 128, "bf16", seed=9, extra_pad=3)
+    got, _ = _check(base)
+    assert np.all(got[3:] == 0.0)
+    stale = DecodeCase(lay, 8, 2, 128, "bf16", seed=9, extra_pad=3,
+                       stale_padding=True, max_context_len=4000)
+    got2, _ = _check(stale)
+    assert bits_equal(got.astype(np.float64), got2.astype(np.float64))
+
+
+def test_block_permutation_invariance():
+    """Same tokens, two different physical placements: identical outputs
+    (the kernel's reduction order does not depend on block ids)."""
+    say("decode placement invariance")
+    lens = [300, 1200, 77]
+    a = DecodeCase(wl.decode_layout(lens, 16, seed=1), 8, 2, 128, "bf16",
+                   seed=3, poison=False)
+    b = DecodeCase(wl.decode_layout(lens, 16, seed=2), 8, 2, 128, "bf16",
+                   seed=3, poison=False)
+    # copy a's logical token rows into b's physical blocks
+    for ta, tb, n in zip(a.tables, b.tables, lens):
+        for i in range(-(-n // 16)):
+            b.kc[int(tb[i])] = a.kc[int(ta[i])]
+            b.vc[int(tb[i])] = a.vc[int(ta[i])]
+    b.k_new.copy_(a.k_new)
+    b.v_new.copy_(a.v_new)
+    b.q.copy_(a.q)
+    for c in (a, b):
+        c.run_store()
+    oa_, ob_ = a.run_decode(), b.run_decode()
+    torch.cuda.synchronize()
+    assert torch.equal(oa_, ob_)
