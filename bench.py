@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the oracle CPU baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="before timing, copy 1 GiB once with a plain copy "
+                         "kernel, so HBM counters can be scaled against it")
     ap.add_argument("--counters", default=os.environ.get("PA_BENCH_COUNTERS"),
                     help="JSON file with FETCH_SIZE/WRITE_SIZE per launch "
                          "(KiB) of the decode partition kernel")
@@ -122,6 +125,13 @@ def main():
                    workspace=ws)
         if ev is not None:
             ev[1].record()
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

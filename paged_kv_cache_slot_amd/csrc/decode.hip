@@ -11,25 +11,30 @@
 // Design (MI355X-first; the work is an HBM stream, ~2 FLOP per byte):
 //  * one workgroup (4 waves) per (partition of P tokens, KV head, sequence):
 //    every K/V byte of a KV head is read once for all G query heads of its
-//    group;
-//  * pass 1, QK: 4 lanes per token, 16 tokens (one block) per wave step;
-//    each lane holds a quarter of the row in 16-byte chunks, dots against q
-//    kept in registers with v_dot2_f32_bf16 (bf16) or FMA (fp32), and the 4
-//    partial sums are combined with two DPP quad permutes -- no LDS traffic
-//    for the reduction;
-//  * the partition's logits (G x P floats) sit in LDS; the exact partition
-//    max is known before any exponent, so each partition needs one exp per
-//    logit and no rescaling;
-//  * pass 2, PV: lanes own head dimensions and walk the block's tokens, so
-//    every V load is a contiguous row segment; the weights come from LDS as
-//    broadcasts;
-//  * the 4 waves' partial outputs are summed through LDS; a partition writes
-//    (max, sum, unnormalised output) to the workspace, and a second small
-//    kernel merges the partitions with log-sum-exp weights.  With a single
-//    partition the first kernel writes the final output itself.
-//  * masking is by predicate only: tokens at or past L, and tokens of a
-//    block id outside the pool, take no part (never multiplied by zero), so
-//    garbage or NaN in unused slots cannot leak into the output.
+//    group; wave w takes blocks w, w+4, ... of the partition;
+//  * access pattern: 16 lanes cover one 256-byte (token, KV head) row, so
+//    every wave load instruction reads whole 128-byte lines of 4 rows; loads
+//    are non-temporal (each byte is used once) and address a wave-uniform
+//    block base held in SGPRs plus per-lane offsets fixed for the whole
+//    kernel; the next block is loaded while the current one is consumed;
+//  * pass 1, QK: each lane dots its 8 dimensions of 4 tokens against q held
+//    in registers (v_dot2_f32_bf16 for bf16, FMA for fp32); the 16 partial
+//    sums of a row are combined with four DPP steps (two quad swaps, half
+//    mirror, mirror) -- no LDS round trip for the reduction;
+//  * the partition's logits sit in LDS token-major; the exact partition max
+//    is known before any exponent, so each logit takes one exp and nothing
+//    is rescaled; the first V block is already in flight during the softmax;
+//  * pass 2, PV: same lane layout; each lane accumulates its 8 dimensions
+//    over its tokens with weights read from LDS as broadcasts; rows of a wave
+//    are summed with lane shuffles and the 4 waves through LDS;
+//  * a partition writes (max, sum, unnormalised output) to the workspace and
+//    a second small kernel merges the partitions with log-sum-exp weights;
+//    with a single partition the first kernel writes the output itself;
+//  * masking is by select only: tokens at or past L and blocks whose id is
+//    outside the pool contribute weight 0 *and* value 0 (loaded values are
+//    replaced, never multiplied by zero), so NaN or garbage in unused slots
+//    cannot reach the output.  Every slot of a valid block is in bounds, so
+//    whole blocks are loaded without per-token branches.
 #include <math.h>
 
 #include "pa_device.h"
@@ -44,20 +49,35 @@ constexpr int kWaves = 4;            // waves per workgroup
 constexpr int kThreads = kWaves * kWave;
 constexpr float kLog2e = 1.4426950408889634f;
 
+// How a wave covers one 16-token block of one KV head: kLpr lanes share a
+// row (token), each lane takes kCpl 16-byte chunks of it, and one load
+// instruction covers kRpi rows.  Every instruction reads whole 128-byte
+// lines (kLpr * 16 >= 128).
+template <int kRow, int kMaxLpr>
+struct BlockLayout {
+  static constexpr int kChunksPerRow = kRow / 16;
+  static constexpr int kLpr = kChunksPerRow < kMaxLpr ? kChunksPerRow : kMaxLpr;
+  static constexpr int kRpi = kWave / kLpr;          // rows per instruction
+  static constexpr int kCpl = kChunksPerRow / kLpr;  // chunks per lane per row
+  static constexpr int kTpl = kBlock / kRpi;         // tokens per lane
+  static_assert(kLpr * 16 >= 128, "whole cache lines per instruction");
+};
+
 template <typename T, int D, int G, int P>
 struct DecodeShape {
   static constexpr int kElem = ElemTraits<T>::kBytes;
-  static constexpr int kRow = D * kElem;     // bytes of one (token, KV head)
-  static constexpr int kChunks = kRow / 64;  // 16-byte chunks per QK lane
-  static constexpr int kBlocks = P / kBlock; // blocks per partition
-  // PV layout: each lane owns kPvVec contiguous bytes of a row.
-  static constexpr int kPvVec = kRow >= 256 ? kRow / 64 : 4;
-  static constexpr int kPvLanes = kRow / kPvVec;   // lanes per token
-  static constexpr int kPvSlots = kWave / kPvLanes;  // tokens per wave step
-  static constexpr int kPvElems = kPvVec / kElem;
-  static constexpr int kPvSteps = kBlock / kPvSlots;
-  static_assert(kRow % 64 == 0, "row must split into 4 lanes x 16 bytes");
-  static_assert(kPvSlots >= 1 && kBlock % kPvSlots == 0, "PV layout");
+  static constexpr int kRow = D * kElem;          // bytes of one (token, KV head)
+  static constexpr int kEpc = 16 / kElem;         // elements per 16-byte chunk
+  static constexpr int kBlocks = P / kBlock;      // blocks per partition
+  using K = BlockLayout<kRow, 8>;    // QK: 8 lanes per row, short reductions
+  using V = BlockLayout<kRow, 16>;   // PV: 16 lanes per row, few accumulators
+  // bf16 PV runs on v_dot2 over token pairs (i, i + 1 of a lane's tokens).
+  static constexpr bool kPairPv = sizeof(T) == 2 && V::kTpl % 2 == 0;
+  static constexpr int kPairsPerBlock = kBlock / 2;
+  // Register cap that keeps 5 waves per SIMD for the bf16 shapes that fit
+  // without spilling; the others keep what the compiler needs.
+  static constexpr int kMinWaves = (sizeof(T) == 2 && G <= 4) ? 5 : 1;
+  static_assert(kRow % 128 == 0, "rows must be whole 128-byte lines");
   static_assert(P % (kBlock * kWaves) == 0, "partition shape");
 };
 
@@ -98,44 +118,45 @@ struct ChunkDot<float, G> {
   }
 };
 
-// Load kPvVec bytes of V and widen to kPvElems floats.
-template <typename T, int kVec>
-struct PvLoad;
-
+// Widen one 16-byte chunk to floats.
+template <typename T>
+struct Widen;
 template <>
-struct PvLoad<bf16_t, 4> {
-  typedef uint32_t raw_t;
-  static __device__ __forceinline__ raw_t load(const char* p) {
-    return *reinterpret_cast<const uint32_t*>(p);
+struct Widen<bf16_t> {
+  static __device__ __forceinline__ void run(const uint4& c, float* v) {
+    v[0] = bf16_lo(c.x); v[1] = bf16_hi(c.x);
+    v[2] = bf16_lo(c.y); v[3] = bf16_hi(c.y);
+    v[4] = bf16_lo(c.z); v[5] = bf16_hi(c.z);
+    v[6] = bf16_lo(c.w); v[7] = bf16_hi(c.w);
   }
-  static __device__ __forceinline__ void widen(raw_t r, float* v) {
-    v[0] = bf16_lo(r);
-    v[1] = bf16_hi(r);
+};
+template <>
+struct Widen<float> {
+  static __device__ __forceinline__ void run(const uint4& c, float* v) {
+    v[0] = __uint_as_float(c.x); v[1] = __uint_as_float(c.y);
+    v[2] = __uint_as_float(c.z); v[3] = __uint_as_float(c.w);
   }
 };
 
-template <>
-struct PvLoad<float, 4> {
-  typedef uint32_t raw_t;
-  static __device__ __forceinline__ raw_t load(const char* p) {
-    return *reinterpret_cast<const uint32_t*>(p);
-  }
-  static __device__ __forceinline__ void widen(raw_t r, float* v) {
-    v[0] = __uint_as_float(r);
-  }
-};
+// Sum over the kLpr lanes of a DPP row group (kLpr = 4, 8 or 16); every
+// lane of the group gets the total.
+template <int kLpr>
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp_f32<kQuadSwap1>(x);
+  x += dpp_f32<kQuadSwap2>(x);
+  if (kLpr >= 8) x += dpp_f32<kRowHalfMirror>(x);
+  if (kLpr == 16) x += dpp_f32<kRowMirror>(x);
+  return x;
+}
 
-template <>
-struct PvLoad<float, 8> {
-  typedef uint2 raw_t;
-  static __device__ __forceinline__ raw_t load(const char* p) {
-    return *reinterpret_cast<const uint2*>(p);
-  }
-  static __device__ __forceinline__ void widen(raw_t r, float* v) {
-    v[0] = __uint_as_float(r.x);
-    v[1] = __uint_as_float(r.y);
-  }
-};
+// Pack the low (high) bfloat16 halves of two dwords: result low half from
+// x, high half from y.
+__device__ __forceinline__ uint32_t pack_lo(uint32_t x, uint32_t y) {
+  return __builtin_amdgcn_perm(y, x, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t x, uint32_t y) {
+  return __builtin_amdgcn_perm(y, x, 0x07060302u);
+}
 
 template <typename T>
 __device__ __forceinline__ void store_out(T* out, float x);
@@ -176,13 +197,18 @@ __device__ __forceinline__ int clamp_len(const DecodeParams& p, int b) {
 }
 
 template <typename T, int D, int G, int P>
-__global__ __launch_bounds__(kThreads) void decode_partition_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((
+    amdgpu_waves_per_eu(DecodeShape<T, D, G, P>::kMinWaves, 8))) void
+decode_partition_kernel(
     DecodeParams p) {
   using S = DecodeShape<T, D, G, P>;
+  using KL = typename S::K;
+  using VL = typename S::V;
   __shared__ int s_blk[S::kBlocks];
-  __shared__ float s_logit[G * P];
+  __shared__ float s_w[P * G];        // logits, then fp32 weights: [t][h]
+  __shared__ uint32_t s_wp[S::kPairPv ? P / 2 * G : 1];  // bf16 weight pairs
   __shared__ float s_red[kWaves][G];
-  __shared__ float s_acc[kWaves * S::kPvSlots][G][D];
+  __shared__ float s_acc[kWaves][G][D];
   __shared__ float s_m[G], s_l[G];
 
   const int part = blockIdx.x;
@@ -196,7 +222,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
   const int len = clamp_len(p, b);
   const int t0 = part * P;
   const int head0 = kvh * G;
-  const int64_t row_stride = static_cast<int64_t>(p.num_kv_heads) * S::kRow;
+  const int row_stride = p.num_kv_heads * S::kRow;   // bytes per slot
+  const int64_t blk_bytes = static_cast<int64_t>(kBlock) * row_stride;
 
   if (t0 >= len) {
     // Nothing to attend.  A single-partition launch owns the output row and
@@ -218,164 +245,271 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
                                 t0 / kBlock + tid];
   }
 
-  // ---- pass 1: logits -------------------------------------------------
-  const int tok = lane >> 2;      // token inside the block
-  const int quarter = lane & 3;   // which quarter of the row
-  uint4 qreg[S::kChunks][G];
+  // Wave-uniform block base (SGPRs).  An id outside the pool reads block 0
+  // and the whole block is then ignored.
+  auto block_base = [&](const char* cache, int j, bool& ok) {
+    int blk = __builtin_amdgcn_readfirstlane(s_blk[j]);
+    ok = blk >= 0 && blk < p.num_blocks;
+    blk = ok ? blk : 0;
+    return cache + static_cast<int64_t>(blk) * blk_bytes;
+  };
+  // Tokens of block j that lie inside the context (uniform).
+  auto valid_in = [&](int j) { return min(kBlock, ntok - j * kBlock); };
+
+  // ---- pass 1: logits -----------------------------------------------------
+  // Lane (krs, ke): token i * KL::kRpi + krs, chunks cc * KL::kLpr + ke.
+  const int krs = lane / KL::kLpr;
+  const int ke = lane % KL::kLpr;
+  uint32_t koff[KL::kTpl][KL::kCpl];
+#pragma unroll
+  for (int i = 0; i < KL::kTpl; ++i)
+#pragma unroll
+    for (int cc = 0; cc < KL::kCpl; ++cc)
+      koff[i][cc] = (i * KL::kRpi + krs) * row_stride + kvh * S::kRow +
+                    (cc * KL::kLpr + ke) * 16;
+  uint4 qreg[KL::kCpl][G];
   {
     const char* qbase = reinterpret_cast<const char*>(p.q) +
-                        (static_cast<int64_t>(b) * p.num_heads + head0) *
-                            S::kRow;
+                        (static_cast<int64_t>(b) * p.num_heads + head0) * S::kRow;
 #pragma unroll
-    for (int c = 0; c < S::kChunks; ++c)
+    for (int cc = 0; cc < KL::kCpl; ++cc)
 #pragma unroll
       for (int h = 0; h < G; ++h)
-        qreg[c][h] = ld16(qbase + h * S::kRow + (c * 4 + quarter) * 16);
+        qreg[cc][h] = ld16(qbase + h * S::kRow + (cc * KL::kLpr + ke) * 16);
   }
   __syncthreads();
+
+  auto load_k = [&](int j, uint4 (*r)[KL::kCpl], bool& ok) {
+    const char* base = block_base(p.k_cache, j, ok);
+#pragma unroll
+    for (int i = 0; i < KL::kTpl; ++i)
+#pragma unroll
+      for (int cc = 0; cc < KL::kCpl; ++cc) r[i][cc] = ld16_nt(base + koff[i][cc]);
+  };
 
   float mloc[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) mloc[h] = -INFINITY;
 
-  auto load_k = [&](int j, uint4* kr, bool& ok) {
-    const int blk = s_blk[j];
-    const int t = j * kBlock + tok;
-    ok = t < ntok && blk >= 0 && blk < p.num_blocks;
+  auto logits = [&](int j, const uint4 (*kr)[KL::kCpl], bool ok) {
+    const int nvalid = ok ? valid_in(j) : 0;
 #pragma unroll
-    for (int c = 0; c < S::kChunks; ++c) kr[c] = make_uint4(0, 0, 0, 0);
-    if (ok) {
-      const char* row = p.k_cache +
-                        (static_cast<int64_t>(blk) * kBlock + tok) * row_stride +
-                        static_cast<int64_t>(kvh) * S::kRow;
-#pragma unroll
-      for (int c = 0; c < S::kChunks; ++c)
-        kr[c] = ld16(row + (c * 4 + quarter) * 16);
-    }
-  };
-
-  {
-    uint4 cur[S::kChunks], nxt[S::kChunks];
-    bool cur_ok = false, nxt_ok = false;
-    int j = wave;
-    if (j < nblk) load_k(j, cur, cur_ok);
-    for (; j < nblk; j += kWaves) {
-      if (j + kWaves < nblk) load_k(j + kWaves, nxt, nxt_ok);
+    for (int i = 0; i < KL::kTpl; ++i) {
       float s[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) s[h] = 0.f;
 #pragma unroll
-      for (int c = 0; c < S::kChunks; ++c)
-        ChunkDot<T, G>::run(cur[c], &qreg[c][0], s);
+      for (int cc = 0; cc < KL::kCpl; ++cc) ChunkDot<T, G>::run(kr[i][cc], qreg[cc], s);
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float v = quad_sum(s[h]) * p.scale_log2;
-        s[h] = cur_ok ? v : -INFINITY;
-        mloc[h] = fmaxf(mloc[h], s[h]);
-        if ((h & 3) == quarter) s_logit[h * P + j * kBlock + tok] = s[h];
+      for (int h = 0; h < G; ++h) s[h] = row_sum<KL::kLpr>(s[h]) * p.scale_log2;
+      const int tb = i * KL::kRpi + krs;       // token inside the block
+      if (nvalid < kBlock) {                   // uniform: partial or bad block
+#pragma unroll
+        for (int h = 0; h < G; ++h) s[h] = tb < nvalid ? s[h] : -INFINITY;
       }
 #pragma unroll
-      for (int c = 0; c < S::kChunks; ++c) cur[c] = nxt[c];
-      cur_ok = nxt_ok;
+      for (int h = 0; h < G; ++h) mloc[h] = fmaxf(mloc[h], s[h]);
+      if (ke == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) s_w[(j * kBlock + tb) * G + h] = s[h];
+      }
+    }
+  };
+  {
+    uint4 ka[KL::kTpl][KL::kCpl], kb[KL::kTpl][KL::kCpl];
+    bool oka = false, okb = false;
+    int j = wave;
+    if (j < nblk) load_k(j, ka, oka);
+    while (j < nblk) {
+      if (j + kWaves < nblk) load_k(j + kWaves, kb, okb);
+      logits(j, ka, oka);
+      j += kWaves;
+      if (j >= nblk) break;
+      if (j + kWaves < nblk) load_k(j + kWaves, ka, oka);
+      logits(j, kb, okb);
+      j += kWaves;
     }
   }
 
-  // Partition max per head: wave, then workgroup.
+  // ---- first V block in flight; softmax over the partition ---------------
+  // Lane (vrs, ve): token i * VL::kRpi + vrs, chunks cc * VL::kLpr + ve.
+  const int vrs = lane / VL::kLpr;
+  const int ve = lane % VL::kLpr;
+  uint32_t voff[VL::kTpl][VL::kCpl];
+#pragma unroll
+  for (int i = 0; i < VL::kTpl; ++i)
+#pragma unroll
+    for (int cc = 0; cc < VL::kCpl; ++cc)
+      voff[i][cc] = (i * VL::kRpi + vrs) * row_stride + kvh * S::kRow +
+                    (cc * VL::kLpr + ve) * 16;
+  auto load_v = [&](int j, uint4 (*r)[VL::kCpl], bool& ok) {
+    const char* base = block_base(p.v_cache, j, ok);
+#pragma unroll
+    for (int i = 0; i < VL::kTpl; ++i)
+#pragma unroll
+      for (int cc = 0; cc < VL::kCpl; ++cc) r[i][cc] = ld16_nt(base + voff[i][cc]);
+  };
+  uint4 va[VL::kTpl][VL::kCpl], vb[VL::kTpl][VL::kCpl];
+  bool vok_a = false, vok_b = false;
+  if (wave < nblk) load_v(wave, va, vok_a);
+
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float m = wave_max(mloc[h]);
     if (lane == 0) s_red[wave][h] = m;
   }
   __syncthreads();
-  float mpart[G];
+  if (tid < G) {
+    float m = s_red[0][tid];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float m = s_red[0][h];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s_red[w][h]);
-    mpart[h] = m;
+    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s_red[w][tid]);
+    s_m[tid] = m;
   }
   __syncthreads();
-
-  // Weights 2^(s - m) in place, and their sums.  Slots of masked tokens
-  // inside the last block hold -inf and become 0; a head whose every token
-  // was masked (all block ids invalid) has m = -inf and gets all-zero
-  // weights and a zero sum.
-  const int nslot = nblk * kBlock;
-  float lsum[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float acc = 0.f;
-    const bool live = mpart[h] != -INFINITY;
-    for (int t = tid; t < nslot; t += kThreads) {
-      float* ptr = &s_logit[h * P + t];
-      const float w = (live && t < ntok) ? fast_exp2(*ptr - mpart[h]) : 0.f;
-      *ptr = w;
-      acc += w;
+  {
+    // Weights 2^(s - m); masked slots (-inf) become 0, and a head whose
+    // every token was masked (m = -inf) gets all-zero weights.  kThreads is a
+    // multiple of G, so each thread always works on the same head.
+    const int h = tid % G;
+    const float m = s_m[h];
+    float acc_l = 0.f;
+    auto weight = [&](float x) {
+      return (m == -INFINITY || x == -INFINITY) ? 0.f : fast_exp2(x - m);
+    };
+    if constexpr (S::kPairPv) {
+      // Pair q of block j joins the lane's tokens t and t + VL::kRpi of the
+      // PV layout; the pair is stored as two bfloat16 (low = t).
+      for (int i = tid; i < nblk * S::kPairsPerBlock * G; i += kThreads) {
+        const int pr = i / G;
+        const int j = pr / S::kPairsPerBlock;
+        const int q = pr % S::kPairsPerBlock;
+        const int ta = j * kBlock + (q / VL::kRpi) * 2 * VL::kRpi + q % VL::kRpi;
+        const float wa = weight(s_w[ta * G + h]);
+        const float wb = weight(s_w[(ta + VL::kRpi) * G + h]);
+        s_wp[i] = static_cast<uint32_t>(f32_to_bf16_rne(wa)) |
+                  (static_cast<uint32_t>(f32_to_bf16_rne(wb)) << 16);
+        acc_l += wa + wb;
+      }
+    } else {
+      for (int i = tid; i < nblk * kBlock * G; i += kThreads) {
+        const float w = weight(s_w[i]);
+        s_w[i] = w;
+        acc_l += w;
+      }
     }
-    acc = wave_sum(acc);
-    if (lane == 0) s_red[wave][h] = acc;
+#pragma unroll
+    for (int o = kWave / 2; o >= G; o >>= 1) acc_l += __shfl_xor(acc_l, o, kWave);
+    if (lane < G) s_red[wave][lane] = acc_l;
   }
   __syncthreads();
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
+  if (tid < G) {
     float l = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) l += s_red[w][h];
-    lsum[h] = l;
+    for (int w = 0; w < kWaves; ++w) l += s_red[w][tid];
+    s_l[tid] = l;
   }
 
-  // ---- pass 2: weighted sum of V ---------------------------------------
-  using L = PvLoad<T, S::kPvVec>;
-  const int pv_slot = lane / S::kPvLanes;
-  const int pv_lane = lane % S::kPvLanes;
-  float acc[G][S::kPvElems];
+  // ---- pass 2: weighted sum of V -----------------------------------------
+  float acc[G][VL::kCpl][S::kEpc];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < S::kPvElems; ++e) acc[h][e] = 0.f;
+    for (int cc = 0; cc < VL::kCpl; ++cc)
+#pragma unroll
+      for (int x = 0; x < S::kEpc; ++x) acc[h][cc][x] = 0.f;
 
-  for (int j = wave; j < nblk; j += kWaves) {
-    const int blk = s_blk[j];
-    if (blk < 0 || blk >= p.num_blocks) continue;  // uniform over the wave
-    const int nvalid = min(kBlock, ntok - j * kBlock);
-    const char* base = p.v_cache + static_cast<int64_t>(blk) * kBlock * row_stride +
-                       static_cast<int64_t>(kvh) * S::kRow + pv_lane * S::kPvVec;
-    typename L::raw_t vr[S::kPvSteps];
+  auto accumulate = [&](int j, uint4 (*vr)[VL::kCpl], bool ok) {
+    if (!ok) return;  // uniform: a block outside the pool adds nothing
+    const int nvalid = valid_in(j);
+    if (nvalid < kBlock) {
+      // Partial last block: replace slots past the context by zeros (they
+      // may hold anything, NaN included); their weights are 0 as well.
 #pragma unroll
-    for (int st = 0; st < S::kPvSteps; ++st) {
-      const int i = st * S::kPvSlots + pv_slot;
-      if (i < nvalid) vr[st] = L::load(base + i * row_stride);
+      for (int i = 0; i < VL::kTpl; ++i)
+#pragma unroll
+        for (int cc = 0; cc < VL::kCpl; ++cc)
+          if (i * VL::kRpi + vrs >= nvalid) vr[i][cc] = make_uint4(0, 0, 0, 0);
     }
+    if constexpr (S::kPairPv) {
 #pragma unroll
-    for (int st = 0; st < S::kPvSteps; ++st) {
-      const int i = st * S::kPvSlots + pv_slot;
-      if (i < nvalid) {
-        float v[S::kPvElems];
-        L::widen(vr[st], v);
+      for (int pi = 0; pi < VL::kTpl / 2; ++pi) {
+        const int q = pi * VL::kRpi + vrs;     // pair index inside the block
+        uint32_t wp[G];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float w = s_logit[h * P + j * kBlock + i];
+        for (int h = 0; h < G; ++h) wp[h] = s_wp[(j * S::kPairsPerBlock + q) * G + h];
 #pragma unroll
-          for (int e = 0; e < S::kPvElems; ++e) acc[h][e] = fmaf(w, v[e], acc[h][e]);
+        for (int cc = 0; cc < VL::kCpl; ++cc) {
+          const uint4 x = vr[2 * pi][cc];
+          const uint4 y = vr[2 * pi + 1][cc];
+          const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+          const uint32_t ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+          for (int dw = 0; dw < 4; ++dw) {
+            const uint32_t lo = pack_lo(xs[dw], ys[dw]);
+            const uint32_t hi = pack_hi(xs[dw], ys[dw]);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              acc[h][cc][2 * dw] = dot2_bf16(lo, wp[h], acc[h][cc][2 * dw]);
+              acc[h][cc][2 * dw + 1] = dot2_bf16(hi, wp[h], acc[h][cc][2 * dw + 1]);
+            }
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < VL::kTpl; ++i) {
+        const int t = j * kBlock + i * VL::kRpi + vrs;
+        float w[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) w[h] = s_w[t * G + h];
+#pragma unroll
+        for (int cc = 0; cc < VL::kCpl; ++cc) {
+          float v[S::kEpc];
+          Widen<T>::run(vr[i][cc], v);
+#pragma unroll
+          for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int x = 0; x < S::kEpc; ++x)
+              acc[h][cc][x] = fmaf(w[h], v[x], acc[h][cc][x]);
         }
       }
     }
-  }
-
-  // Sum the partial outputs of all waves (and token slots) through LDS.
-  if (tid == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      s_m[h] = mpart[h];
-      s_l[h] = lsum[h];
+  };
+  {
+    int j = wave;
+    while (j < nblk) {
+      if (j + kWaves < nblk) load_v(j + kWaves, vb, vok_b);
+      accumulate(j, va, vok_a);
+      j += kWaves;
+      if (j >= nblk) break;
+      if (j + kWaves < nblk) load_v(j + kWaves, va, vok_a);
+      accumulate(j, vb, vok_b);
+      j += kWaves;
     }
   }
+
+  // Sum the row groups of the wave (same dimensions, different tokens) with
+  // shuffles, then the waves through LDS.
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < S::kPvElems; ++e)
-      s_acc[wave * S::kPvSlots + pv_slot][h][pv_lane * S::kPvElems + e] = acc[h][e];
+    for (int cc = 0; cc < VL::kCpl; ++cc)
+#pragma unroll
+      for (int x = 0; x < S::kEpc; ++x) {
+        float a = acc[h][cc][x];
+#pragma unroll
+        for (int o = VL::kLpr; o < kWave; o <<= 1) a += __shfl_xor(a, o, kWave);
+        acc[h][cc][x] = a;
+      }
+  if (vrs == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int cc = 0; cc < VL::kCpl; ++cc)
+#pragma unroll
+        for (int x = 0; x < S::kEpc; ++x)
+          s_acc[wave][h][(cc * VL::kLpr + ve) * S::kEpc + x] = acc[h][cc][x];
+  }
   __syncthreads();
 
   for (int i = tid; i < G * D; i += kThreads) {
@@ -383,7 +517,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
     const int d = i % D;
     float o = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves * S::kPvSlots; ++w) o += s_acc[w][h][d];
+    for (int w = 0; w < kWaves; ++w) o += s_acc[w][h][d];
     const int64_t head = static_cast<int64_t>(b) * p.num_heads + head0 + h;
     if (single) {
       const float l = s_l[h];
@@ -455,7 +589,10 @@ hipError_t dispatch_group(const DecodeParams& prm, int num_seqs,
   }
 }
 
-constexpr int kPartitionTokens = 512;
+#ifndef PA_DECODE_PARTITION
+#define PA_DECODE_PARTITION 512
+#endif
+constexpr int kPartitionTokens = PA_DECODE_PARTITION;
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 

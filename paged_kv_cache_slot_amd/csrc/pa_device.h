@@ -59,6 +59,8 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
 // Control byte = sel0 | sel1 << 2 | sel2 << 4 | sel3 << 6.
 constexpr int kQuadSwap1 = 0xB1;  // [1,0,3,2]
 constexpr int kQuadSwap2 = 0x4E;  // [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;  // lane i <-> 7 - i in each 8 lanes
+constexpr int kRowMirror = 0x140;      // lane i <-> 15 - i in each 16 lanes
 
 template <int kCtrl>
 __device__ __forceinline__ float dpp_f32(float x) {
@@ -93,6 +95,12 @@ __device__ __forceinline__ float fast_exp2(float x) {
 // 16-byte global load / store.
 __device__ __forceinline__ uint4 ld16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
+}
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+// 16-byte load marked non-temporal: streamed data used once.
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+  u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ void st16(void* p, uint4 v) {
   *reinterpret_cast<uint4*>(p) = v;
