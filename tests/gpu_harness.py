@@ -137,3 +137,71 @@ def sample_seqs(lens, k, seed):
             break
         pick.add(int(b))
     return sorted(pick)
+
+
+class PrefillCase:
+    """One chunked-prefill step: store the chunk's new K/V rows, then run
+    varlen prefill over history + chunk read through the block tables.
+
+    ``lay`` is a workloads.PrefillLayout (history[b] cached tokens, chunk[b]
+    new ones)."""
+
+    def __init__(self, lay, hq, hkv, d, dtype, seed, causal=True, poison=True,
+                 device="cuda"):
+        self.lay, self.hq, self.hkv, self.d = lay, hq, hkv, d
+        self.dtype, self.causal = dtype, causal
+        self.bs = lay.block_size
+        self.scale = 1.0 / math.sqrt(d)
+        lens = lay.history + lay.chunk
+        self.kc, self.vc = wl.fill_pool(lay.num_blocks, self.bs, hkv, d, dtype,
+                                        seed, device)
+        if poison:
+            mask = wl.valid_slot_mask(lay.num_blocks, self.bs, lay.tables, lens)
+            wl.poison_unused(self.kc, self.vc, mask)
+        total = int(lay.chunk.sum())
+        self.total_q = total
+        self.q = wl.make_values((total, hq, d), dtype, seed + 1, device)
+        self.k_new = wl.make_values((total, hkv, d), dtype, seed + 2, device)
+        self.v_new = wl.make_values((total, hkv, d), dtype, seed + 3, device)
+        self.h_kc = wl.host_bits(self.kc)
+        self.h_vc = wl.host_bits(self.vc)
+        self.h_q = wl.host_bits(self.q)
+        self.h_kn = wl.host_bits(self.k_new)
+        self.h_vn = wl.host_bits(self.v_new)
+        meta = pm.prefill_inputs(lay.tables, lay.history, lay.chunk, self.bs)
+        self.meta = meta
+        self.slot_mapping = dev_i32(meta["slot_mapping"], device)
+        self.cu_q = dev_i32(meta["cu_seqlens_q"], device)
+        self.cu_k = dev_i32(meta["cu_seqlens_k"], device)
+        self.block_tables = dev_i32(meta["block_tables"], device)
+
+    def run_store(self):
+        ops.store_kv(self.k_new, self.v_new, self.kc, self.vc,
+                     self.slot_mapping)
+
+    def run_prefill(self, out=None):
+        return ops.prefill_varlen(
+            self.q, self.kc, self.vc, self.cu_q, self.cu_k,
+            self.meta["max_seqlen_q"], self.meta["max_seqlen_k"],
+            self.block_tables, scale=self.scale, causal=self.causal, out=out)
+
+    def oracle_meta(self):
+        seqs = [{"block_table": [int(x) for x in t], "num_cached": int(h),
+                 "num_scheduled": int(c)}
+                for t, h, c in zip(self.lay.tables, self.lay.history,
+                                   self.lay.chunk)]
+        return om.prefill_metadata(seqs, self.bs)
+
+    def oracle_store(self):
+        return oa.store_kv(self.h_kc, self.h_vc, self.h_kn, self.h_vn,
+                           self.oracle_meta()["slot_mapping"])
+
+    def oracle_prefill(self, kc, vc, seqs=None, rows=None):
+        meta = self.oracle_meta()
+        width = max(len(t) for t in self.lay.tables)
+        tables = [[int(x) for x in t] + [-1] * (width - len(t))
+                  for t in self.lay.tables]
+        return oa.prefill_attention(self.h_q, kc, vc, meta["cu_seqlens_q"],
+                                    meta["cu_seqlens_k"], tables, self.scale,
+                                    self.causal, self.dtype, seqs=seqs,
+                                    rows=rows)

@@ -1,0 +1,154 @@
+"""pa_store_kv + pa_prefill_varlen on the GPU against the oracle.
+
+All slots outside any sequence's context are NaN, so a read past Lk or a
+mask applied by multiplication shows up as a non-finite output."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from tests.gpu_harness import (TOL, DecodeCase, PrefillCase, bits_equal, f64,
+                               say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(case, seqs=None, rows=None):
+    case.run_store()
+    out = case.run_prefill()
+    torch.cuda.synchronize()
+    ek, ev = case.oracle_store()
+    assert bits_equal(wl.host_bits(case.kc), ek), "store mismatch"
+    want = case.oracle_prefill(ek, ev, seqs=seqs, rows=rows)
+    got = f64(out)
+    cu = case.meta["cu_seqlens_q"]
+    if seqs is None:
+        sel = np.arange(case.total_q)
+    else:
+        sel = []
+        for b in seqs:
+            local = range(cu[b + 1] - cu[b]) if rows is None or b not in rows \
+                else rows[b]
+            sel += [cu[b] + i for i in local]
+        sel = np.asarray(sel, dtype=np.int64)
+    assert np.all(np.isfinite(got[sel]))
+    err = np.max(np.abs(got[sel] - want[sel])) if len(sel) else 0.0
+    assert err <= TOL[case.dtype], f"max abs err {err}"
+    return got, want
+
+
+@pytest.mark.parametrize("dtype,d,hq,hkv", [
+    ("bf16", 128, 32, 8), ("bf16", 128, 8, 8), ("bf16", 64, 16, 2),
+    ("bf16", 128, 16, 2), ("f32", 64, 8, 2), ("f32", 128, 8, 4),
+])
+def test_mixed_chunks(dtype, d, hq, hkv):
+    """History 0..700 and chunks 1..130 rows, incl. partial tiles and a
+    no-history sequence, every supported shape."""
+    say("prefill mixed", dtype, d, hq, hkv)
+    lay = wl.prefill_layout([0, 5, 100, 700, 63], [17, 1, 64, 130, 65], 16,
+                            seed=11)
+    _check(PrefillCase(lay, hq, hkv, d, dtype, seed=12))
+
+
+def test_non_causal():
+    say("prefill non-causal")
+    lay = wl.prefill_layout([0, 40, 300], [33, 7, 100], 16, seed=13)
+    _check(PrefillCase(lay, 8, 2, 128, "bf16", seed=14, causal=False))
+
+
+def test_empty_chunks_in_batch():
+    """Sequences with no query rows this round (cu_q[b+1] == cu_q[b])."""
+    say("prefill empty chunks")
+    lay = wl.prefill_layout([10, 200, 0, 31], [0, 50, 9, 0], 16, seed=15)
+    _check(PrefillCase(lay, 8, 2, 128, "bf16", seed=16))
+
+
+def test_mixed_workload_full_size_sampled():
+    """8 chunks of 512 rows over history U[0, 8192] (both ends), 32q/8kv,
+    D=128, bf16 -- full grid as benchmarked; sampled rows of every chunk."""
+    cfg = wl.get_config("mixed")
+    say("prefill full-size mixed workload")
+    pre, _ = wl.mixed_layout(cfg)
+    case = PrefillCase(pre, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim,
+                       cfg.dtype, seed=cfg.seed)
+    rng = np.random.default_rng(5)
+    rows = {b: sorted({0, 1, 127, 128, 255, 511} |
+                      set(rng.integers(0, 512, 4).tolist()))
+            for b in range(len(pre.chunk))}
+    _check(case, seqs=list(range(len(pre.chunk))), rows=rows)
+
+
+def test_chunked_equals_unchunked():
+    """The same 300-token prompt prefilled at once and in 3 chunks gives the
+    same rows ("10 Serving Engines", section 10.3: chunking moves work in
+    time, it does not change it)."""
+    say("prefill chunked == unchunked")
+    lens = [300]
+    whole = PrefillCase(wl.prefill_layout([0], lens, 16, seed=21), 8, 2, 128,
+                        "bf16", seed=22, poison=False)
+    whole.run_store()
+    ref = whole.run_prefill()
+    torch.cuda.synchronize()
+    cuts = [0, 100, 101, 300]
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        lay = wl.PrefillLayout(history=np.array([a]), chunk=np.array([b - a]),
+                               tables=whole.lay.tables,
+                               num_blocks=whole.lay.num_blocks, block_size=16)
+        part = PrefillCase.__new__(PrefillCase)
+        # reuse the filled cache and the same q rows
+        part.__dict__.update(whole.__dict__)
+        from paged_kv_cache_slot_amd import metadata as pm
+        from tests.gpu_harness import dev_i32
+        meta = pm.prefill_inputs(lay.tables, lay.history, lay.chunk, 16)
+        part.lay, part.meta = lay, meta
+        part.q = whole.q[a:b].contiguous()
+        part.cu_q = dev_i32(meta["cu_seqlens_q"])
+        part.cu_k = dev_i32(meta["cu_seqlens_k"])
+        part.block_tables = dev_i32(meta["block_tables"])
+        got = part.run_prefill()
+        torch.cuda.synchronize()
+        diff = (got.float() - ref[a:b].float()).abs().max().item()
+        assert diff <= 1e-2, (a, b, diff)
+
+
+def test_decode_equals_prefill_row():
+    """A decode row equals the last row of a causal prefill over the same
+    context, and a one-row prefill of it (the 192 decode rows of the mixed
+    workload could take either kernel)."""
+    say("decode == prefill last row")
+    lens = [1, 40, 513, 2000]
+    lay = wl.decode_layout(lens, 16, seed=31)
+    dec = DecodeCase(lay, 32, 8, 128, "bf16", seed=32, poison=False)
+    dec.run_store()
+    dout = dec.run_decode()
+    pl = wl.PrefillLayout(history=lay.lens - 1, chunk=np.ones(len(lens),
+                                                              dtype=np.int64),
+                          tables=lay.tables, num_blocks=lay.num_blocks,
+                          block_size=16)
+    pre = PrefillCase.__new__(PrefillCase)
+    pre.__dict__.update(dict(lay=pl, hq=32, hkv=8, d=128, dtype="bf16",
+                             causal=True, bs=16, scale=dec.scale, kc=dec.kc,
+                             vc=dec.vc, q=dec.q, total_q=len(lens)))
+    from paged_kv_cache_slot_amd import metadata as pm
+    from tests.gpu_harness import dev_i32
+    meta = pm.prefill_inputs(pl.tables, pl.history, pl.chunk, 16)
+    pre.meta = meta
+    pre.cu_q = dev_i32(meta["cu_seqlens_q"])
+    pre.cu_k = dev_i32(meta["cu_seqlens_k"])
+    pre.block_tables = dev_i32(meta["block_tables"])
+    pout = pre.run_prefill()
+    torch.cuda.synchronize()
+    diff = (pout.float() - dout.float()).abs().max().item()
+    assert diff <= 1e-2, diff
+
+
+@pytest.mark.parametrize("lq", [2, 3, 5, 8])
+def test_multi_token_verify_rows(lq):
+    """Several new tokens per sequence over a long context (the shape of a
+    speculative-decoding verify pass): 64 sequences, ctx U[100, 3000]."""
+    say("prefill multi-token", lq)
+    rng = np.random.default_rng(lq)
+    hist = rng.integers(100, 3000, 64)
+    lay = wl.prefill_layout(hist, [lq] * 64, 16, seed=lq + 40)
+    _check(PrefillCase(lay, 32, 8, 128, "bf16", seed=lq + 41))
