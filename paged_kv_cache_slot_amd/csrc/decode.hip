@@ -149,14 +149,6 @@ __device__ __forceinline__ float row_sum(float x) {
   return x;
 }
 
-// Pack the low (high) bfloat16 halves of two dwords: result low half from
-// x, high half from y.
-__device__ __forceinline__ uint32_t pack_lo(uint32_t x, uint32_t y) {
-  return __builtin_amdgcn_perm(y, x, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t x, uint32_t y) {
-  return __builtin_amdgcn_perm(y, x, 0x07060302u);
-}
 
 template <typename T>
 __device__ __forceinline__ void store_out(T* out, float x);

@@ -48,6 +48,22 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// Two floats -> packed bfloat16 pair (low = lo), round to nearest even, one
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Pack the low (high) bfloat16 halves of two dwords: result low half from
+// x, high half from y.
+__device__ __forceinline__ uint32_t pack_lo(uint32_t x, uint32_t y) {
+  return __builtin_amdgcn_perm(y, x, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t x, uint32_t y) {
+  return __builtin_amdgcn_perm(y, x, 0x07060302u);
+}
+
 // dot of two packed bfloat16 pairs, accumulated in float (v_dot2_f32_bf16).
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),

@@ -25,7 +25,8 @@
 //  * masking is by select: keys past the causal limit or past Lk get weight
 //    exactly 0, and V rows past Lk are zeroed in LDS (a NaN there would
 //    survive a multiplication by zero);
-//  * only tiles that cross the causal diagonal or Lk evaluate the mask.
+//  * only tiles that cross the causal diagonal or Lk evaluate the mask; the
+//    running max moves lazily, so O is rescaled on few tiles.
 #include <math.h>
 
 #include "pa_device.h"
@@ -90,8 +91,14 @@ struct PrefillShape {
   static constexpr int kQSteps = D / Mma<T>::kK;          // MFMAs per S tile
   static constexpr int kPvSteps = kBN / Mma<T>::kK;       // MFMAs per O tile
   static constexpr int kDTiles = D / 32;                  // O^T M-tiles
+  // Tile staging: thread t moves chunk column t % kChunks of kKpt
+  // consecutive keys (kKpt = kLoadsPerThread), so a bf16 thread can write
+  // its 8 dims x kKpt keys of V^T as 8 runs of kKpt keys.
   static constexpr int kLoadsPerThread = kBN * kChunks / kThreads;
+  static constexpr int kKpt = kLoadsPerThread;
   static_assert(kBN * kChunks % kThreads == 0, "tile load split");
+  static_assert(kThreads % kChunks == 0, "chunk columns per thread");
+  static_assert(!kBf16 || kKpt == 2 || kKpt == 4, "bf16 V^T write width");
 };
 
 struct PrefillParams {
@@ -121,10 +128,8 @@ __device__ __forceinline__ void store4<float>(float* p, const float* v) {
 }
 template <>
 __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const float* v) {
-  uint2 w;
-  w.x = f32_to_bf16_rne(v[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(v[1])) << 16);
-  w.y = f32_to_bf16_rne(v[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(v[3])) << 16);
-  *reinterpret_cast<uint2*>(p) = w;
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]),
+                                             pack_bf16x2(v[2], v[3]));
 }
 
 template <typename T, int D, int G>
@@ -198,15 +203,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const int32_t* btab = p.block_tables +
                         static_cast<int64_t>(b) * p.max_blocks_per_seq;
 
-  // Tile staging: thread t moves chunks t + kThreads * u of the tile.
-  uint4 kst[S::kLoadsPerThread], vst[S::kLoadsPerThread];
+  // Tile staging (see PrefillShape): thread t owns chunk column c of keys
+  // kg * kKpt .. kg * kKpt + kKpt - 1 of the tile.
+  const int st_c = tid % S::kChunks;
+  const int st_k0 = (tid / S::kChunks) * S::kKpt;
+  uint4 kst[S::kKpt], vst[S::kKpt];
   auto load_tile = [&](int kt) {
 #pragma unroll
-    for (int u = 0; u < S::kLoadsPerThread; ++u) {
-      const int qidx = tid + kThreads * u;
-      const int key = qidx / S::kChunks;
-      const int c = qidx % S::kChunks;
-      const int kpos = kt * kBN + key;
+    for (int u = 0; u < S::kKpt; ++u) {
+      const int kpos = kt * kBN + st_k0 + u;
       kst[u] = make_uint4(0, 0, 0, 0);
       vst[u] = make_uint4(0, 0, 0, 0);
       if (kpos < lk) {
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         if (blk >= 0 && blk < p.num_blocks) {
           const int64_t off = (static_cast<int64_t>(blk) * kBlock + kpos % kBlock) *
                                   row_stride + static_cast<int64_t>(kvh) * S::kRow +
-                              c * 16;
+                              st_c * 16;
           kst[u] = ld16(p.k_cache + off);
           vst[u] = ld16(p.v_cache + off);
         }
@@ -223,22 +228,33 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   };
   auto store_tile = [&]() {
 #pragma unroll
-    for (int u = 0; u < S::kLoadsPerThread; ++u) {
-      const int qidx = tid + kThreads * u;
-      const int key = qidx / S::kChunks;
-      const int c = qidx % S::kChunks;
-      *reinterpret_cast<uint4*>(s_k + key * S::kKPitch + c * 16) = kst[u];
-      if constexpr (S::kBf16) {
-        // transpose: 8 dims of one key -> column `key` of 8 rows of V^T
-        const uint32_t w[4] = {vst[u].x, vst[u].y, vst[u].z, vst[u].w};
+    for (int u = 0; u < S::kKpt; ++u)
+      *reinterpret_cast<uint4*>(s_k + (st_k0 + u) * S::kKPitch + st_c * 16) = kst[u];
+    if constexpr (S::kBf16) {
+      // transpose kKpt keys x 8 dims in registers: dim 2w (2w+1) of key u is
+      // the low (high) half of dword w of vst[u].
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint16_t x = static_cast<uint16_t>(w[e / 2] >> ((e % 2) * 16));
-          *reinterpret_cast<uint16_t*>(s_v + (c * 8 + e) * S::kVPitch + key * 2) = x;
+      for (int w = 0; w < 4; ++w) {
+        uint32_t x[S::kKpt];
+#pragma unroll
+        for (int u = 0; u < S::kKpt; ++u)
+          x[u] = w == 0 ? vst[u].x : w == 1 ? vst[u].y : w == 2 ? vst[u].z : vst[u].w;
+        char* lo_row = s_v + (st_c * 8 + 2 * w) * S::kVPitch + st_k0 * 2;
+        char* hi_row = lo_row + S::kVPitch;
+        if constexpr (S::kKpt == 4) {
+          *reinterpret_cast<uint2*>(lo_row) =
+              make_uint2(pack_lo(x[0], x[1]), pack_lo(x[2], x[3]));
+          *reinterpret_cast<uint2*>(hi_row) =
+              make_uint2(pack_hi(x[0], x[1]), pack_hi(x[2], x[3]));
+        } else {
+          *reinterpret_cast<uint32_t*>(lo_row) = pack_lo(x[0], x[1]);
+          *reinterpret_cast<uint32_t*>(hi_row) = pack_hi(x[0], x[1]);
         }
-      } else {
-        *reinterpret_cast<uint4*>(s_v + key * S::kVPitch + c * 16) = vst[u];
       }
+    } else {
+#pragma unroll
+      for (int u = 0; u < S::kKpt; ++u)
+        *reinterpret_cast<uint4*>(s_v + (st_k0 + u) * S::kVPitch + st_c * 16) = vst[u];
     }
   };
 
@@ -247,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   for (int t = 0; t < S::kDTiles; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[t][r] = 0.f;
-  float run_max = -INFINITY;   // running max of this row (scaled, log2 domain)
+  float run_max = -INFINITY;   // reference max of this row (scaled, log2)
   float run_sum = 0.f;         // this lane half's share of the row sum
 
   if (ntiles > 0) load_tile(0);
@@ -277,41 +293,51 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     }
 
     // ---- online softmax for this lane's row ---------------------------
+    // Logits stay raw; scale * log2(e) > 0 enters through one FMA with the
+    // (scaled) running max.  Masked keys: raw -inf -> weight exactly 0.
     const int kbase = kt * kBN;
     const bool need_mask = kbase + kBN - 1 > wave_lim || kbase + kBN > lk;
     float tmax = -INFINITY;
+    if (need_mask) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kpos = kbase + t * 32 + (r / 4) * 8 + hh * 4 + r % 4;
+          sacc[t][r] = kpos <= lim ? sacc[t][r] : -INFINITY;
+        }
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = sacc[t][r] * p.scale_log2;
-        if (need_mask) {
-          const int kpos = kbase + t * 32 + (r / 4) * 8 + hh * 4 + r % 4;
-          x = kpos <= lim ? x : -INFINITY;
-        }
-        sacc[t][r] = x;
-        tmax = fmaxf(tmax, x);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    const float new_max = fmaxf(run_max, tmax);
-    // Rows that have seen no visible key yet keep max -inf: scale 1, p 0.
-    const float alpha = new_max == -INFINITY ? 1.f : fast_exp2(run_max - new_max);
-    run_max = new_max;
+      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[t][r]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave)) * p.scale_log2;
+    // The reference max moves only when it would grow by more than 2^8:
+    // weights stay <= 256 and the rescale of O is skipped on most tiles.
+    // Any reference gives the same O / l; this one keeps every term finite.
+    const bool grow = tmax > run_max + 8.f;
+    if (__any(grow)) {
+      const float new_max = grow ? tmax : run_max;
+      const float alpha = run_max == -INFINITY ? 0.f : fast_exp2(run_max - new_max);
+      run_max = new_max;
+      run_sum *= alpha;
+#pragma unroll
+      for (int t = 0; t < S::kDTiles; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
+    }
+    // A row that has seen no visible key yet keeps max -inf and weights 0.
+    const float neg_max = run_max == -INFINITY ? 0.f : -run_max;
     float psum = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float x = sacc[t][r];
-        const float pr = x == -INFINITY ? 0.f : fast_exp2(x - new_max);
+        const float pr = fast_exp2(fmaf(sacc[t][r], p.scale_log2, neg_max));
         sacc[t][r] = pr;
         psum += pr;
       }
-    run_sum = run_sum * alpha + psum;
-#pragma unroll
-    for (int t = 0; t < S::kDTiles; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
+    run_sum += psum;
 
     // ---- O^T += V^T P^T -------------------------------------------------
 #pragma unroll
@@ -322,13 +348,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         // registers (s % 2) * 8 .. + 7 of S^T M-tile s / 2.
         const int t = s / 2;
         const int r0 = (s % 2) * 8;
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = sacc[t][r0 + e];
-        bop.x = f32_to_bf16_rne(pv[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(pv[1])) << 16);
-        bop.y = f32_to_bf16_rne(pv[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(pv[3])) << 16);
-        bop.z = f32_to_bf16_rne(pv[4]) | (static_cast<uint32_t>(f32_to_bf16_rne(pv[5])) << 16);
-        bop.w = f32_to_bf16_rne(pv[6]) | (static_cast<uint32_t>(f32_to_bf16_rne(pv[7])) << 16);
+        bop.x = pack_bf16x2(sacc[t][r0 + 0], sacc[t][r0 + 1]);
+        bop.y = pack_bf16x2(sacc[t][r0 + 2], sacc[t][r0 + 3]);
+        bop.z = pack_bf16x2(sacc[t][r0 + 4], sacc[t][r0 + 5]);
+        bop.w = pack_bf16x2(sacc[t][r0 + 6], sacc[t][r0 + 7]);
       } else {
         // step s covers keys (r/4) * 8 + hh * 4 + r % 4 (+ 32 for M-tile 1)
         // with r = s % 16: one probability per lane.
