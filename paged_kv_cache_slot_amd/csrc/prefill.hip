@@ -132,8 +132,11 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const float* v) {
                                              pack_bf16x2(v[2], v[3]));
 }
 
+// Two waves per SIMD: one wave's softmax and LDS traffic overlap the other's
+// MFMAs.  Every shape fits the 256-register budget without spilling.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillParams p) {
   using S = PrefillShape<T, D>;
   using M = Mma<T>;
   typedef typename M::op_t op_t;
