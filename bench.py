@@ -5,6 +5,11 @@ the 256 newest K/V rows (one per sequence), then pa_decode of 256 sequences
 with contexts uniform in [512, 8192], 32 query / 8 KV heads, head_dim 128,
 bf16, block size 16 -- on one HIP stream, inputs resident in HBM.
 
+The same run also times the mixed step, which exercises every kernel of the
+path: one pa_store_kv of 4,288 rows, pa_prefill_varlen of 8 chunks of 512
+rows over 0..8192 cached tokens, and pa_decode of 192 rows; it is reported in
+``mixed_step`` with its own MFMA roofline for the prefill kernel.
+
 Prints one JSON line.  ``value`` is the step's algorithmic HBM throughput in
 TB/s (KV bytes the decode must read + q/out/block ids + the store's bytes,
 over the step time); ``tokens_per_s`` is sequences decoded per second for
@@ -27,7 +32,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 WORKLOAD = "decode8b"
+MIXED = "mixed"
 
 
 def parse():
@@ -41,6 +48,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before timing, copy 1 GiB once with a plain copy "
                          "kernel, so HBM counters can be scaled against it")
+    ap.add_argument("--mixed-steps", type=int, default=20,
+                    help="timed steps of the mixed chunked-prefill + decode "
+                         "workload (0 skips it)")
     ap.add_argument("--counters", default=os.environ.get("PA_BENCH_COUNTERS"),
                     help="JSON file with FETCH_SIZE/WRITE_SIZE per launch "
                          "(KiB) of the decode partition kernel")
@@ -53,6 +63,107 @@ def decode_bytes(lens, hq, hkv, d, elem, bs=16):
     qo = len(lens) * hq * d * elem * 2
     ids = 4 * int(sum(-(-int(n) // bs) for n in lens)) + 4 * len(lens)
     return kv + qo + ids
+
+
+def prefill_flops(lq, lk, hq, d):
+    """Algorithmic FLOPs of causal prefill: 4 * D * Hq per unmasked (q, k)
+    pair (QK^T and PV, multiply + add); row i of a chunk of Lq rows over Lk
+    keys sees Lk - Lq + i + 1 keys."""
+    pairs = sum(int(a) * (int(b) - int(a)) + int(a) * (int(a) + 1) // 2
+                for a, b in zip(lq, lk))
+    return 4 * d * hq * pairs
+
+
+def run_mixed(steps, warmup, dev):
+    """Mixed step: one pa_store_kv of every new row (8 x 512 chunk rows + 192
+    decode rows), then pa_prefill_varlen of the chunks, then pa_decode of the
+    decode rows, on one stream.  Returns a dict for the JSON line."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from paged_kv_cache_slot_amd import metadata as pm
+    from paged_kv_cache_slot_amd import ops
+
+    cfg = wl.get_config(MIXED)
+    pre, dec = wl.mixed_layout(cfg)
+    hq, hkv, d, bs = cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, 16
+    kc, vc = wl.fill_pool(pre.num_blocks, bs, hkv, d, "bf16", cfg.seed, dev)
+    tq = int(pre.chunk.sum())
+    nd = len(dec.lens)
+    qp = wl.make_values((tq, hq, d), "bf16", cfg.seed + 1, dev)
+    qd = wl.make_values((nd, hq, d), "bf16", cfg.seed + 2, dev)
+    k_new = wl.make_values((tq + nd, hkv, d), "bf16", cfg.seed + 3, dev)
+    v_new = wl.make_values((tq + nd, hkv, d), "bf16", cfg.seed + 4, dev)
+    mp = pm.prefill_inputs(pre.tables, pre.history, pre.chunk, bs)
+    md = pm.decode_inputs(dec.tables, dec.lens, bs)
+    slots = torch.as_tensor(np.concatenate([mp["slot_mapping"],
+                                            md["slot_mapping"]]), device=dev)
+    cu_q = torch.as_tensor(mp["cu_seqlens_q"], device=dev)
+    cu_k = torch.as_tensor(mp["cu_seqlens_k"], device=dev)
+    btp = torch.as_tensor(mp["block_tables"], device=dev)
+    btd = torch.as_tensor(md["block_tables"], device=dev)
+    cl = torch.as_tensor(md["context_lens"], device=dev)
+    scale = 1.0 / math.sqrt(d)
+    outp = torch.empty_like(qp)
+    outd = torch.empty_like(qd)
+    wsd = torch.empty(max(ops.decode_workspace_bytes(
+        nd, hq, hkv, d, md["max_context_len"]), 1), dtype=torch.uint8,
+        device=dev)
+    wsp = torch.empty(max(ops.prefill_workspace_bytes(
+        len(pre.chunk), hq, hkv, d, mp["max_seqlen_q"], mp["max_seqlen_k"]),
+        1), dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        ops.store_kv(k_new, v_new, kc, vc, slots)
+        if ev is not None:
+            ev[1].record()
+        ops.prefill_varlen(qp, kc, vc, cu_q, cu_k, mp["max_seqlen_q"],
+                           mp["max_seqlen_k"], btp, scale=scale, causal=True,
+                           out=outp, workspace=wsp)
+        if ev is not None:
+            ev[2].record()
+        ops.decode(qd, kc, vc, btd, cl, md["max_context_len"], scale=scale,
+                   out=outd, workspace=wsd)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+           for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    st = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    pf = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    dc = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
+    total = sum(e[0].elapsed_time(e[3]) for e in evs) / steps
+    flops = prefill_flops(pre.chunk, pre.history + pre.chunk, hq, d)
+    dbytes = decode_bytes(dec.lens, hq, hkv, d, 2)
+    row = 2 * hkv * d * 2
+    sbytes = 2 * (tq + nd) * row + 4 * (tq + nd)
+    tflops = flops / (pf * 1e-3) / 1e12
+    return {
+        "workload": cfg.title,
+        "steps": steps,
+        "ms_per_step": round(total, 4),
+        "store_us": round(st * 1e3, 2),
+        "store_gbs": round(sbytes / (st * 1e-3) / 1e9, 1),
+        "prefill_us": round(pf * 1e3, 2),
+        "prefill_gflop": round(flops / 1e9, 2),
+        "decode_us": round(dc * 1e3, 2),
+        "decode_tbs": round(dbytes / (dc * 1e-3) / 1e12, 4),
+        "decode_tokens_per_s": round(nd / (dc * 1e-3), 1),
+        "roofline": {"kernel": "pa_prefill_varlen (prefill_kernel)",
+                     "bound": "mfma", "achieved": round(tflops, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flops": flops},
+    }
 
 
 def cpu_baseline(case_tables, lens, h_q, h_kc, h_vc, hq, scale, budget_s):
@@ -164,12 +275,25 @@ def main():
         with open(args.counters) as f:
             traffic = json.load(f).get("traffic_bytes")
 
+    mixed = None
+    if args.mixed_steps > 0:
+        # free the 8B-shaped pool first; the mixed pool is ~3.5 GB
+        keep_cpu = not args.no_cpu_baseline
+        h_kc = wl.host_bits(kc) if keep_cpu else None
+        h_vc = wl.host_bits(vc) if keep_cpu else None
+        h_q = wl.host_bits(q) if keep_cpu else None
+        del kc, vc, ws
+        torch.cuda.empty_cache()
+        mixed = run_mixed(args.mixed_steps, max(2, args.warmup // 2), dev)
+    else:
+        h_kc = h_vc = h_q = None
+
     cpu = None
     if not args.no_cpu_baseline:
-        # bounded oracle sample: host copies of the touched sequences' pool
-        h_kc = wl.host_bits(kc)
-        h_vc = wl.host_bits(vc)
-        h_q = wl.host_bits(q)
+        # bounded oracle sample over host copies of the same pool
+        if h_kc is None:
+            h_kc, h_vc, h_q = wl.host_bits(kc), wl.host_bits(vc), \
+                wl.host_bits(q)
         done, toks, dt = cpu_baseline(lay.tables, lay.lens, h_q, h_kc, h_vc,
                                       hq, scale, args.cpu_seconds)
         cpu_bytes = toks * row
@@ -209,6 +333,7 @@ def main():
                      "traffic": traffic,
                      "algorithmic_bytes": dbytes},
         "cpu_baseline": cpu,
+        "mixed_step": mixed,
         "wall_s_timed": round(wall, 3),
     }
     print(json.dumps(line), flush=True)

@@ -139,7 +139,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads,
  *
  * Supported: head_dim in {64, 128}; block_size == 16; num_heads /
  * num_kv_heads in {1, 2, 4, 8}; dtype F32 or BF16 (fp32 accumulation,
- * bf16 output rounded to nearest even).
+ * bf16 output rounded to nearest even); scale positive and finite
+ * (PA_ERR_SHAPE otherwise; it is 1/sqrt(head_dim) in practice).
  * Preconditions: context_lens[b] <= max_context_len and
  * <= max_blocks_per_seq * block_size (larger values are clamped); the first
  * ceil(L / block_size) block ids of row b lie in [0, num_blocks) (an id

@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "pa_internal.h"
 
 namespace {
@@ -106,6 +108,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache,
                                  dtype);
   if (st != PA_OK) return st;
   if (max_context_len < 0) return PA_ERR_SHAPE;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return PA_ERR_SHAPE;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !context_lens) return PA_ERR_NULL;
   if (max_context_len > 0 && (!k_cache || !v_cache || !block_tables))
@@ -165,6 +168,7 @@ pa_status pa_prefill_varlen(void* out, const void* q, int64_t total_q,
                                  dtype);
   if (st != PA_OK) return st;
   if (total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return PA_ERR_SHAPE;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return PA_ERR_SHAPE;
   if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return PA_OK;
   if (!out || !q || !cu_seqlens_q || !cu_seqlens_k) return PA_ERR_NULL;
   if (max_seqlen_k > 0 && (!k_cache || !v_cache || !block_tables))

@@ -75,6 +75,8 @@ def _decode(lib, **kw):
     (dict(b=-1), 2), (dict(maxlen=-5), 2), (dict(out=None), 1),
     (dict(q=None), 1), (dict(cl=None), 1), (dict(bt=None), 1),
     (dict(q=MISALIGNED), 3), (dict(k=MISALIGNED), 3),
+    (dict(scale=0.0), 2), (dict(scale=-0.1), 2), (dict(scale=float("inf")), 2),
+    (dict(scale=float("nan")), 2),
     (dict(maxlen=4096), 4),                       # needs a workspace
     (dict(maxlen=4096, ws=FAKE, wsb=16), 4),       # workspace too small
     (dict(b=0), 0),                                # empty batch: no-op
@@ -125,6 +127,7 @@ def _prefill(lib, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(d=80), 3), (dict(bs=8), 3), (dict(hq=12, hkv=4), 3),
     (dict(tq=-1), 2), (dict(mq=-2), 2), (dict(out=None), 1),
+    (dict(scale=0.0), 2), (dict(scale=-1.0), 2), (dict(scale=float("nan")), 2),
     (dict(cuq=None), 1), (dict(bt=None), 1), (dict(q=MISALIGNED), 3),
     (dict(b=0), 0), (dict(tq=0), 0), (dict(mq=0), 0),
 ])
