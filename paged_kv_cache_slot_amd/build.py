@@ -38,6 +38,21 @@ def sources():
             if n.endswith(".hip") or n.endswith(".cpp")]
 
 
+def _check_symbols(path):
+    """Every kernel host stub must be defined in the library: a device-only
+    construct the host compilation pass cannot take silently drops a
+    kernel's host side, which only shows as an undefined symbol."""
+    res = subprocess.run(["nm", "-D", "--undefined-only", path],
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        return  # nm unavailable: nothing to check with
+    missing = [l.split()[-1] for l in res.stdout.splitlines()
+               if "_ZN2pa" in l]
+    if missing:
+        raise RuntimeError(f"{path} leaves library symbols undefined: "
+                           + ", ".join(missing[:4]))
+
+
 def build(verbose=False, jobs=None):
     """Compile every source and link ``libpa.so``; returns its path."""
     hipcc = _hipcc()
@@ -68,6 +83,7 @@ def build(verbose=False, jobs=None):
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stderr}")
+    _check_symbols(tmp)
     os.replace(tmp, out)
     if verbose:
         print(f"built {out}")

@@ -12,19 +12,23 @@
 //  * one workgroup (4 waves) per (M-tile of 128 rows, KV head, sequence);
 //    the G query heads of a KV head are packed into M (row m = position
 //    m / G, head m % G), so a K/V tile loaded once serves all of them;
-//  * per 64-key tile the workgroup gathers K (row-major) and V (transposed)
-//    through the block table into padded LDS, the next tile's global loads
-//    in flight while the current one is computed;
+//  * per 64-key tile the workgroup gathers K and V through the block table
+//    straight into LDS with DMA loads (global_load_lds_dwordx4; one
+//    wave-uniform block lookup per 1 KiB load; double buffered; 16-byte
+//    chunks XOR-swizzled by row), the next tile in flight while the current
+//    one is computed; one barrier per tile;
 //  * each wave computes S^T = K Q^T for its 32 rows with
 //    v_mfma_f32_32x32x16_bf16 (fp32 I/O: v_mfma_f32_32x32x2_f32), Q^T held
 //    in registers as the B operand.  In the accumulator layout every lane
 //    owns one query row, so the online softmax (running max, rescale, sum)
 //    is per lane plus one exchange between the two lane halves, and the
 //    probabilities already sit in the B-operand layout of O^T += V^T P^T --
-//    no shuffles or LDS round trip for P;
+//    no shuffles or LDS round trip for P; the V^T operand comes straight
+//    from the row-major V tile through LDS transpose reads
+//    (ds_read_b64_tr_b16);
 //  * masking is by select: keys past the causal limit or past Lk get weight
-//    exactly 0, and V rows past Lk are zeroed in LDS (a NaN there would
-//    survive a multiplication by zero);
+//    exactly 0, and V rows past Lk are zeroed in LDS on the one tile that
+//    crosses Lk (a NaN there would survive a multiplication by zero);
 //  * only tiles that cross the causal diagonal or Lk evaluate the mask; the
 //    running max moves lazily, so O is rescaled on few tiles.
 #include <math.h>
@@ -81,24 +85,19 @@ struct PrefillShape {
   static constexpr int kRow = D * kElem;                  // bytes per key row
   static constexpr int kChunks = kRow / 16;               // 16-byte chunks
   static constexpr bool kBf16 = sizeof(T) == 2;
-  // K tile, row-major, rows padded so 32 lanes reading one column of 32
-  // different rows spread over the banks.
-  static constexpr int kKPitch = kRow + 16;
-  // V tile: bf16 transposed [D][kBN keys] (MFMA A operand wants 8 keys of
-  // one dimension per lane); fp32 row-major (one element per lane).
-  static constexpr int kVPitch = kBf16 ? kBN * 2 + 8 : kRow + 16;
-  static constexpr int kVBytes = kBf16 ? D * kVPitch : kBN * kVPitch;
+  // K and V tiles: [kBN rows][kRow], rows unpadded; chunk p of row r holds
+  // the row's chunk p ^ (r % kChunks), so the rows one operand read touches
+  // sit in different banks.  Both are filled by LDS DMA
+  // (global_load_lds_dwordx4), each double buffered.
+  static constexpr int kTile = kBN * kRow;
+  static constexpr int kRowsPerDma = 1024 / kRow;         // rows per 1 KiB DMA
+  static constexpr int kDmaPerWave = kTile / 1024 / kWaves;
   static constexpr int kQSteps = D / Mma<T>::kK;          // MFMAs per S tile
   static constexpr int kPvSteps = kBN / Mma<T>::kK;       // MFMAs per O tile
   static constexpr int kDTiles = D / 32;                  // O^T M-tiles
-  // Tile staging: thread t moves chunk column t % kChunks of kKpt
-  // consecutive keys (kKpt = kLoadsPerThread), so a bf16 thread can write
-  // its 8 dims x kKpt keys of V^T as 8 runs of kKpt keys.
-  static constexpr int kLoadsPerThread = kBN * kChunks / kThreads;
-  static constexpr int kKpt = kLoadsPerThread;
-  static_assert(kBN * kChunks % kThreads == 0, "tile load split");
-  static_assert(kThreads % kChunks == 0, "chunk columns per thread");
-  static_assert(!kBf16 || kKpt == 2 || kKpt == 4, "bf16 V^T write width");
+  static constexpr size_t kLds = 4 * static_cast<size_t>(kTile);
+  static_assert(kTile % (1024 * kWaves) == 0, "tile DMA split");
+  static_assert(kBlock % kRowsPerDma == 0, "a DMA load stays in one block");
 };
 
 struct PrefillParams {
@@ -120,6 +119,38 @@ struct PrefillParams {
   int causal;
 };
 
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane l's bytes land at lds + 16 l; `lds` must be
+// the same for the whole wave.  Completion is counted by vmcnt.
+__device__ __forceinline__ void dma16(const void* src, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+#else
+  (void)src;
+  (void)lds;
+#endif
+}
+
+// LDS transpose read (ds_read_b64_tr_b16).  In each group of 16 lanes, if
+// lane s reads the four 16-bit values M[s][0..3] at its address, lane i
+// receives M[4k + i/4][i % 4] for k = 0..3 (checked on gfx950).  With four
+// lanes per key row covering 16 dimensions and four rows, every lane gets
+// four consecutive keys of one dimension -- an MFMA A operand of V^T.
+// (The host compilation pass has no LDS address space; it only needs the
+// declaration.)
+__device__ __forceinline__ uint2 lds_read_tr16(const char* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16_t*)(p));
+  return __builtin_bit_cast(uint2, r);
+#else
+  (void)p;
+  return make_uint2(0, 0);
+#endif
+}
+
 template <typename T>
 __device__ __forceinline__ void store4(T* p, const float* v);
 template <>
@@ -132,23 +163,25 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const float* v) {
                                              pack_bf16x2(v[2], v[3]));
 }
 
-// Two waves per SIMD: one wave's softmax and LDS traffic overlap the other's
-// MFMAs.  Every shape fits the 256-register budget without spilling.
+// Two waves per SIMD: one wave's softmax overlaps the other's MFMAs.  fp32
+// with D = 128 needs 128 KiB of LDS, so one workgroup per CU: no register
+// cap there (it would only spill).
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
+    PrefillShape<T, D>::kLds <= 80 * 1024 ? 2 : 1,
+    PrefillShape<T, D>::kLds <= 80 * 1024 ? 2 : 1))) void
+prefill_kernel(PrefillParams p) {
   using S = PrefillShape<T, D>;
   using M = Mma<T>;
   typedef typename M::op_t op_t;
   extern __shared__ __align__(16) char smem[];
-  char* s_k = smem;                          // [kBN][kKPitch]
-  char* s_v = smem + kBN * S::kKPitch;       // see PrefillShape
+  // [K buffer 0][K buffer 1][V buffer 0][V buffer 1]
 
   const int mtile = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
   const int j = lane % 32;                   // this lane's row inside the wave
   const int hh = lane / 32;                  // lane half
@@ -195,71 +228,58 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillParams p) 
         qb[s] = row_ok ? ld16(qrow + (s * M::kK + hh * M::kPer) * 2)
                        : make_uint4(0, 0, 0, 0);
       } else {
-        qb[s] = row_ok ? *reinterpret_cast<const float*>(
-                             qrow + (s * M::kK + hh) * 4)
+        qb[s] = row_ok ? *reinterpret_cast<const float*>(qrow + (s * M::kK + hh) * 4)
                        : 0.f;
       }
     }
   }
 
   const int64_t row_stride = static_cast<int64_t>(p.num_kv_heads) * S::kRow;
+  const int64_t blk_bytes = row_stride * kBlock;
   const int32_t* btab = p.block_tables +
                         static_cast<int64_t>(b) * p.max_blocks_per_seq;
+  const int nblk_ctx = (lk + kBlock - 1) / kBlock;   // blocks the context owns
 
-  // Tile staging (see PrefillShape): thread t owns chunk column c of keys
-  // kg * kKpt .. kg * kKpt + kKpt - 1 of the tile.
-  const int st_c = tid % S::kChunks;
-  const int st_k0 = (tid / S::kChunks) * S::kKpt;
-  uint4 kst[S::kKpt], vst[S::kKpt];
-  auto load_tile = [&](int kt) {
+  // DMA load q of this wave moves tile rows r0 .. r0 + kRowsPerDma - 1 (one
+  // cache block); lane l's 16 bytes land at byte 16 l of that 1 KiB and hold
+  // chunk pos ^ (r % kChunks) of row r.  The per-lane source offset inside a
+  // block is the same for every tile.
+  uint32_t dma_off[S::kDmaPerWave];
 #pragma unroll
-    for (int u = 0; u < S::kKpt; ++u) {
-      const int kpos = kt * kBN + st_k0 + u;
-      kst[u] = make_uint4(0, 0, 0, 0);
-      vst[u] = make_uint4(0, 0, 0, 0);
-      if (kpos < lk) {
-        const int blk = btab[kpos / kBlock];
+  for (int q = 0; q < S::kDmaPerWave; ++q) {
+    const int byte = (wave * S::kDmaPerWave + q) * 1024 + lane * 16;
+    const int r = byte / S::kRow;
+    const int pos = (byte % S::kRow) / 16;
+    dma_off[q] = static_cast<uint32_t>((r % kBlock) * row_stride + kvh * S::kRow +
+                                       (pos ^ (r % S::kChunks)) * 16);
+  }
+  auto dma_tile = [&](int kt, char* kbuf, char* vbuf) {
+#pragma unroll
+    for (int q = 0; q < S::kDmaPerWave; ++q) {
+      const int ii = wave * S::kDmaPerWave + q;
+      const int r0 = ii * S::kRowsPerDma;
+      const int bi = kt * (kBN / kBlock) + r0 / kBlock;    // uniform
+      if (bi < nblk_ctx) {
+        const int blk = __builtin_amdgcn_readfirstlane(btab[bi]);
         if (blk >= 0 && blk < p.num_blocks) {
-          const int64_t off = (static_cast<int64_t>(blk) * kBlock + kpos % kBlock) *
-                                  row_stride + static_cast<int64_t>(kvh) * S::kRow +
-                              st_c * 16;
-          kst[u] = ld16(p.k_cache + off);
-          vst[u] = ld16(p.v_cache + off);
+          const int64_t base = static_cast<int64_t>(blk) * blk_bytes;
+          dma16(p.k_cache + base + dma_off[q], kbuf + ii * 1024);
+          dma16(p.v_cache + base + dma_off[q], vbuf + ii * 1024);
         }
       }
     }
   };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int u = 0; u < S::kKpt; ++u)
-      *reinterpret_cast<uint4*>(s_k + (st_k0 + u) * S::kKPitch + st_c * 16) = kst[u];
-    if constexpr (S::kBf16) {
-      // transpose kKpt keys x 8 dims in registers: dim 2w (2w+1) of key u is
-      // the low (high) half of dword w of vst[u].
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t x[S::kKpt];
-#pragma unroll
-        for (int u = 0; u < S::kKpt; ++u)
-          x[u] = w == 0 ? vst[u].x : w == 1 ? vst[u].y : w == 2 ? vst[u].z : vst[u].w;
-        char* lo_row = s_v + (st_c * 8 + 2 * w) * S::kVPitch + st_k0 * 2;
-        char* hi_row = lo_row + S::kVPitch;
-        if constexpr (S::kKpt == 4) {
-          *reinterpret_cast<uint2*>(lo_row) =
-              make_uint2(pack_lo(x[0], x[1]), pack_lo(x[2], x[3]));
-          *reinterpret_cast<uint2*>(hi_row) =
-              make_uint2(pack_hi(x[0], x[1]), pack_hi(x[2], x[3]));
-        } else {
-          *reinterpret_cast<uint32_t*>(lo_row) = pack_lo(x[0], x[1]);
-          *reinterpret_cast<uint32_t*>(hi_row) = pack_hi(x[0], x[1]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < S::kKpt; ++u)
-        *reinterpret_cast<uint4*>(s_v + (st_k0 + u) * S::kVPitch + st_c * 16) = vst[u];
-    }
-  };
+
+  // LDS read offsets, fixed for the whole kernel.  K (A operand of S^T):
+  // lane (j, hh) reads row t * 32 + j, chunk (s * kK + hh * kPer) / 8 (bf16)
+  // -- for t = 1 the row is 32 further and the swizzle the same.
+  const int kswz = j % S::kChunks;
+  // V^T (A operand of O^T, bf16): transpose reads over rows
+  // 16 s + 4 hh + 8 half + i / 4 and dimensions dt * 32 + 16 * g16 +
+  // 4 * (i % 4), with g16 = (lane / 16) % 2, i = lane % 16.  The row's
+  // swizzle does not depend on s (16 s is a multiple of kChunks' period).
+  const int li = lane % 16;
+  const int g16 = (lane / 16) % 2;
 
   f32x16_v oacc[S::kDTiles];
 #pragma unroll
@@ -269,12 +289,19 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillParams p) 
   float run_max = -INFINITY;   // reference max of this row (scaled, log2)
   float run_sum = 0.f;         // this lane half's share of the row sum
 
-  if (ntiles > 0) load_tile(0);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    __syncthreads();           // previous tile fully consumed
-    store_tile();
-    __syncthreads();
-    if (kt + 1 < ntiles) load_tile(kt + 1);
+  auto compute = [&](int kt, const char* s_k, char* s_v) {
+    // V rows past Lk hold whatever the pool has there (NaN in a poisoned
+    // test pool); P is 0 there, but 0 * NaN is NaN, so zero them.
+    const int kbase = kt * kBN;
+    if (kbase + kBN > lk) {
+      for (int i = tid; i < kBN * S::kChunks; i += kThreads) {
+        const int r = i / S::kChunks;
+        if (kbase + r >= lk)
+          *reinterpret_cast<uint4*>(s_v + r * S::kRow + (i % S::kChunks) * 16) =
+              make_uint4(0, 0, 0, 0);
+      }
+      __syncthreads();
+    }
 
     // ---- S^T = K Q^T: two 32-key M-tiles ------------------------------
     f32x16_v sacc[2];
@@ -282,25 +309,32 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillParams p) 
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
-      const char* krow = s_k + (t * 32 + j) * S::kKPitch;
+      const char* krow = s_k + (t * 32 + j) * S::kRow;
+      // operands read in batches of up to 8 steps, ahead of their MFMAs
+      constexpr int kBatch = S::kQSteps < 8 ? S::kQSteps : 8;
 #pragma unroll
-      for (int s = 0; s < S::kQSteps; ++s) {
-        op_t a;
-        if constexpr (S::kBf16) {
-          a = *reinterpret_cast<const uint4*>(krow + (s * M::kK + hh * M::kPer) * 2);
-        } else {
-          a = *reinterpret_cast<const float*>(krow + (s * M::kK + hh) * 4);
+      for (int s0 = 0; s0 < S::kQSteps; s0 += kBatch) {
+        op_t a[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int s = s0 + u;
+          if constexpr (S::kBf16) {
+            const int c = (s * M::kK + hh * M::kPer) / 8;   // 16-byte chunk
+            a[u] = *reinterpret_cast<const uint4*>(krow + (c ^ kswz) * 16);
+          } else {
+            const int e = s * M::kK + hh;                   // element
+            a[u] = *reinterpret_cast<const float*>(krow + ((e / 4) ^ kswz) * 16 + (e % 4) * 4);
+          }
         }
-        sacc[t] = M::run(a, qb[s], sacc[t]);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) sacc[t] = M::run(a[u], qb[s0 + u], sacc[t]);
       }
     }
 
     // ---- online softmax for this lane's row ---------------------------
     // Logits stay raw; scale * log2(e) > 0 enters through one FMA with the
     // (scaled) running max.  Masked keys: raw -inf -> weight exactly 0.
-    const int kbase = kt * kBN;
     const bool need_mask = kbase + kBN - 1 > wave_lim || kbase + kBN > lk;
-    float tmax = -INFINITY;
     if (need_mask) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -310,6 +344,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillParams p) 
           sacc[t][r] = kpos <= lim ? sacc[t][r] : -INFINITY;
         }
     }
+    float tmax = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -362,21 +397,48 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillParams p) 
       }
 #pragma unroll
       for (int dt = 0; dt < S::kDTiles; ++dt) {
-        const int dim = dt * 32 + j;
         op_t a;
         if constexpr (S::kBf16) {
-          const char* vt = s_v + dim * S::kVPitch;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vt + (s * 16 + hh * 4) * 2);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vt + (s * 16 + 8 + hh * 4) * 2);
+          // keys 16 s + 4 hh + 0..3 (first half) and + 8 (second half) of
+          // dimension dt * 32 + j: two transpose reads.
+          const int dim0 = dt * 32 + 16 * g16 + 4 * (li % 4);
+          const int row_a = 16 * s + 4 * hh + li / 4;
+          const int row_b = row_a + 8;
+          const int ca = (dim0 / 8) ^ (row_a % S::kChunks);
+          const int cb = (dim0 / 8) ^ (row_b % S::kChunks);
+          const uint2 lo = lds_read_tr16(s_v + row_a * S::kRow + ca * 16 + (dim0 % 8) * 2);
+          const uint2 hi = lds_read_tr16(s_v + row_b * S::kRow + cb * 16 + (dim0 % 8) * 2);
           a = make_uint4(lo.x, lo.y, hi.x, hi.y);
         } else {
           const int r = s % 16;
           const int key = (s / 16) * 32 + (r / 4) * 8 + hh * 4 + r % 4;
-          a = *reinterpret_cast<const float*>(s_v + key * S::kVPitch + dim * 4);
+          const int dim = dt * 32 + j;
+          a = *reinterpret_cast<const float*>(
+              s_v + key * S::kRow + ((dim / 4) ^ (key % S::kChunks)) * 16 + (dim % 4) * 4);
         }
         oacc[dt] = M::run(a, bop, oacc[dt]);
       }
     }
+  };
+
+  char* const kbuf0 = smem;
+  char* const kbuf1 = smem + S::kTile;
+  char* const vbuf0 = smem + 2 * S::kTile;
+  char* const vbuf1 = smem + 3 * S::kTile;
+  if (ntiles > 0) dma_tile(0, kbuf0, vbuf0);
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    // Tile kt lives in buffers 0, tile kt + 1 in buffers 1.  Before the
+    // barrier this thread's DMA loads of the tile have landed; after it
+    // every wave's have, and every wave is done with the other buffers.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 1 < ntiles) dma_tile(kt + 1, kbuf1, vbuf1);
+    compute(kt, kbuf0, vbuf0);
+    if (kt + 1 >= ntiles) break;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 2 < ntiles) dma_tile(kt + 2, kbuf0, vbuf0);
+    compute(kt + 1, kbuf1, vbuf1);
   }
 
   // ---- normalise and write: lane (j, hh) holds dims (r/4)*8 + hh*4 + r%4
@@ -402,7 +464,7 @@ hipError_t launch_typed(const PrefillParams& prm, int num_seqs, int max_seqlen_q
                         int num_kv_heads, hipStream_t stream) {
   using S = PrefillShape<T, D>;
   const int mtiles = (max_seqlen_q * G + kBM - 1) / kBM;
-  const size_t lds = static_cast<size_t>(kBN) * S::kKPitch + S::kVBytes;
+  const size_t lds = S::kLds;
   if (lds > 65536) {
     static bool raised = false;   // once per kernel instantiation
     if (!raised) {
