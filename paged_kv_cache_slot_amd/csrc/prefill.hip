@@ -101,6 +101,8 @@ struct PrefillShape {
 };
 
 struct PrefillParams {
+  int mtiles;                // M-tiles per (sequence, KV head)
+  int num_seqs;
   void* out;
   const char* q;
   int64_t total_q;
@@ -177,9 +179,19 @@ prefill_kernel(PrefillParams p) {
   extern __shared__ __align__(16) char smem[];
   // [K buffer 0][K buffer 1][V buffer 0][V buffer 1]
 
-  const int mtile = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
+  // XCD-aware order.  The dispatcher deals workgroups to the 8 XCDs round
+  // robin (id % 8), each XCD with its own L2.  A (sequence, KV head) group's
+  // M-tiles all read the same K/V tiles, so they go to one XCD, heaviest
+  // M-tile (longest causal key range) first; group g runs on XCD g % 8.
+  // The grid holds 8 * ceil(groups / 8) * mtiles ids; ids past the last
+  // group exit.
+  const int lin = blockIdx.x;
+  const int slot = lin / 8;
+  const int grp = (slot / p.mtiles) * 8 + lin % 8;
+  if (grp >= p.num_seqs * p.num_kv_heads) return;     // uniform
+  const int mtile = p.mtiles - 1 - slot % p.mtiles;
+  const int kvh = grp % p.num_kv_heads;
+  const int b = grp / p.num_kv_heads;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
@@ -465,6 +477,11 @@ hipError_t launch_typed(const PrefillParams& prm, int num_seqs, int max_seqlen_q
   using S = PrefillShape<T, D>;
   const int mtiles = (max_seqlen_q * G + kBM - 1) / kBM;
   const size_t lds = S::kLds;
+  PrefillParams pr = prm;
+  pr.mtiles = mtiles;
+  pr.num_seqs = num_seqs;
+  const int64_t groups8 = (static_cast<int64_t>(num_seqs) * num_kv_heads + 7) / 8 * 8;
+  const int64_t wgs = groups8 * mtiles;
   if (lds > 65536) {
     static bool raised = false;   // once per kernel instantiation
     if (!raised) {
@@ -475,8 +492,8 @@ hipError_t launch_typed(const PrefillParams& prm, int num_seqs, int max_seqlen_q
       raised = true;
     }
   }
-  hipLaunchKernelGGL((prefill_kernel<T, D, G>), dim3(mtiles, num_kv_heads, num_seqs),
-                     dim3(kThreads), lds, stream, prm);
+  hipLaunchKernelGGL((prefill_kernel<T, D, G>), dim3(static_cast<unsigned>(wgs)),
+                     dim3(kThreads), lds, stream, pr);
   return hipGetLastError();
 }
 
