@@ -86,9 +86,11 @@ struct PrefillShape {
   static constexpr int kChunks = kRow / 16;               // 16-byte chunks
   static constexpr bool kBf16 = sizeof(T) == 2;
   // K and V tiles: [kBN rows][kRow], rows unpadded; chunk p of row r holds
-  // the row's chunk p ^ (r % kChunks), so the rows one operand read touches
-  // sit in different banks.  Both are filled by LDS DMA
-  // (global_load_lds_dwordx4), each double buffered.
+  // the row's chunk p ^ swizzle(r), so the lanes of one operand read touch
+  // different banks: r % kChunks for K (32 rows, one chunk each), and
+  // ((r % 4) << 2) for V (the transpose reads take 4 rows x 2 chunks per
+  // 16 lanes).  Both are filled by LDS DMA (global_load_lds_dwordx4), each
+  // double buffered.
   static constexpr int kTile = kBN * kRow;
   static constexpr int kRowsPerDma = 1024 / kRow;         // rows per 1 KiB DMA
   static constexpr int kDmaPerWave = kTile / 1024 / kWaves;
@@ -122,6 +124,13 @@ struct PrefillParams {
 };
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+template <int kChunks>
+__device__ __forceinline__ int k_swz(int row) { return row % kChunks; }
+template <int kChunks>
+__device__ __forceinline__ int v_swz(int row) {
+  return ((row % 4) << 2) & (kChunks - 1);
+}
 
 // 16 bytes per lane from global memory straight into LDS
 // (global_load_lds_dwordx4): lane l's bytes land at lds + 16 l; `lds` must be
@@ -256,14 +265,15 @@ prefill_kernel(PrefillParams p) {
   // cache block); lane l's 16 bytes land at byte 16 l of that 1 KiB and hold
   // chunk pos ^ (r % kChunks) of row r.  The per-lane source offset inside a
   // block is the same for every tile.
-  uint32_t dma_off[S::kDmaPerWave];
+  uint32_t dma_k_off[S::kDmaPerWave], dma_v_off[S::kDmaPerWave];
 #pragma unroll
   for (int q = 0; q < S::kDmaPerWave; ++q) {
     const int byte = (wave * S::kDmaPerWave + q) * 1024 + lane * 16;
     const int r = byte / S::kRow;
     const int pos = (byte % S::kRow) / 16;
-    dma_off[q] = static_cast<uint32_t>((r % kBlock) * row_stride + kvh * S::kRow +
-                                       (pos ^ (r % S::kChunks)) * 16);
+    const int64_t row_base = (r % kBlock) * row_stride + kvh * S::kRow;
+    dma_k_off[q] = static_cast<uint32_t>(row_base + (pos ^ k_swz<S::kChunks>(r)) * 16);
+    dma_v_off[q] = static_cast<uint32_t>(row_base + (pos ^ v_swz<S::kChunks>(r)) * 16);
   }
   auto dma_tile = [&](int kt, char* kbuf, char* vbuf) {
 #pragma unroll
@@ -275,8 +285,8 @@ prefill_kernel(PrefillParams p) {
         const int blk = __builtin_amdgcn_readfirstlane(btab[bi]);
         if (blk >= 0 && blk < p.num_blocks) {
           const int64_t base = static_cast<int64_t>(blk) * blk_bytes;
-          dma16(p.k_cache + base + dma_off[q], kbuf + ii * 1024);
-          dma16(p.v_cache + base + dma_off[q], vbuf + ii * 1024);
+          dma16(p.k_cache + base + dma_k_off[q], kbuf + ii * 1024);
+          dma16(p.v_cache + base + dma_v_off[q], vbuf + ii * 1024);
         }
       }
     }
@@ -285,7 +295,7 @@ prefill_kernel(PrefillParams p) {
   // LDS read offsets, fixed for the whole kernel.  K (A operand of S^T):
   // lane (j, hh) reads row t * 32 + j, chunk (s * kK + hh * kPer) / 8 (bf16)
   // -- for t = 1 the row is 32 further and the swizzle the same.
-  const int kswz = j % S::kChunks;
+  const int kswz = k_swz<S::kChunks>(j);   // rows t * 32 + j: same swizzle
   // V^T (A operand of O^T, bf16): transpose reads over rows
   // 16 s + 4 hh + 8 half + i / 4 and dimensions dt * 32 + 16 * g16 +
   // 4 * (i % 4), with g16 = (lane / 16) % 2, i = lane % 16.  The row's
@@ -416,8 +426,8 @@ prefill_kernel(PrefillParams p) {
           const int dim0 = dt * 32 + 16 * g16 + 4 * (li % 4);
           const int row_a = 16 * s + 4 * hh + li / 4;
           const int row_b = row_a + 8;
-          const int ca = (dim0 / 8) ^ (row_a % S::kChunks);
-          const int cb = (dim0 / 8) ^ (row_b % S::kChunks);
+          const int ca = (dim0 / 8) ^ v_swz<S::kChunks>(row_a);
+          const int cb = (dim0 / 8) ^ v_swz<S::kChunks>(row_b);
           const uint2 lo = lds_read_tr16(s_v + row_a * S::kRow + ca * 16 + (dim0 % 8) * 2);
           const uint2 hi = lds_read_tr16(s_v + row_b * S::kRow + cb * 16 + (dim0 % 8) * 2);
           a = make_uint4(lo.x, lo.y, hi.x, hi.y);
@@ -426,7 +436,7 @@ prefill_kernel(PrefillParams p) {
           const int key = (s / 16) * 32 + (r / 4) * 8 + hh * 4 + r % 4;
           const int dim = dt * 32 + j;
           a = *reinterpret_cast<const float*>(
-              s_v + key * S::kRow + ((dim / 4) ^ (key % S::kChunks)) * 16 + (dim % 4) * 4);
+              s_v + key * S::kRow + ((dim / 4) ^ v_swz<S::kChunks>(key)) * 16 + (dim % 4) * 4);
         }
         oacc[dt] = M::run(a, bop, oacc[dt]);
       }
