@@ -125,6 +125,18 @@ struct PrefillParams {
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
+// A wave-uniform int32 that stays constant for the whole kernel (a block id),
+// read through the constant address space so it arrives by a scalar load
+// counted by lgkmcnt.  Read as a vector load it would be counted by vmcnt,
+// and each wait for it would also wait for every DMA load issued before.
+__device__ __forceinline__ int load_uniform_i32(const int32_t* base, int idx) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return ((const __attribute__((address_space(4))) int32_t*)base)[idx];
+#else
+  return base[idx];
+#endif
+}
+
 template <int kChunks>
 __device__ __forceinline__ int k_swz(int row) { return row % kChunks; }
 template <int kChunks>
@@ -282,7 +294,7 @@ prefill_kernel(PrefillParams p) {
       const int r0 = ii * S::kRowsPerDma;
       const int bi = kt * (kBN / kBlock) + r0 / kBlock;    // uniform
       if (bi < nblk_ctx) {
-        const int blk = __builtin_amdgcn_readfirstlane(btab[bi]);
+        const int blk = load_uniform_i32(btab, bi);
         if (blk >= 0 && blk < p.num_blocks) {
           const int64_t base = static_cast<int64_t>(blk) * blk_bytes;
           dma16(p.k_cache + base + dma_k_off[q], kbuf + ii * 1024);
@@ -325,31 +337,40 @@ prefill_kernel(PrefillParams p) {
       __syncthreads();
     }
 
-    // ---- S^T = K Q^T: two 32-key M-tiles ------------------------------
+    // ---- S^T = K Q^T: two 32-key M-tiles, their MFMAs interleaved so
+    // consecutive MFMAs never wait on each other's accumulator.
     f32x16_v sacc[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
-      const char* krow = s_k + (t * 32 + j) * S::kRow;
+    {
+      const char* krow0 = s_k + j * S::kRow;
+      const char* krow1 = s_k + (32 + j) * S::kRow;
       // operands read in batches of up to 8 steps, ahead of their MFMAs
       constexpr int kBatch = S::kQSteps < 8 ? S::kQSteps : 8;
 #pragma unroll
       for (int s0 = 0; s0 < S::kQSteps; s0 += kBatch) {
-        op_t a[kBatch];
+        op_t a0[kBatch], a1[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           const int s = s0 + u;
           if constexpr (S::kBf16) {
-            const int c = (s * M::kK + hh * M::kPer) / 8;   // 16-byte chunk
-            a[u] = *reinterpret_cast<const uint4*>(krow + (c ^ kswz) * 16);
+            const int c = ((s * M::kK + hh * M::kPer) / 8) ^ kswz;   // chunk
+            a0[u] = *reinterpret_cast<const uint4*>(krow0 + c * 16);
+            a1[u] = *reinterpret_cast<const uint4*>(krow1 + c * 16);
           } else {
-            const int e = s * M::kK + hh;                   // element
-            a[u] = *reinterpret_cast<const float*>(krow + ((e / 4) ^ kswz) * 16 + (e % 4) * 4);
+            const int e = s * M::kK + hh;                          // element
+            const int off = ((e / 4) ^ kswz) * 16 + (e % 4) * 4;
+            a0[u] = *reinterpret_cast<const float*>(krow0 + off);
+            a1[u] = *reinterpret_cast<const float*>(krow1 + off);
           }
         }
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) sacc[t] = M::run(a[u], qb[s0 + u], sacc[t]);
+        for (int u = 0; u < kBatch; ++u) {
+          sacc[0] = M::run(a0[u], qb[s0 + u], sacc[0]);
+          sacc[1] = M::run(a1[u], qb[s0 + u], sacc[1]);
+        }
       }
     }
 
