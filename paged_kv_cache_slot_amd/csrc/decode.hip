@@ -12,29 +12,37 @@
 //  * one workgroup (4 waves) per (partition of P tokens, KV head, sequence):
 //    every K/V byte of a KV head is read once for all G query heads of its
 //    group; wave w takes blocks w, w+4, ... of the partition;
-//  * access pattern: 16 lanes cover one 256-byte (token, KV head) row, so
-//    every wave load instruction reads whole 128-byte lines of 4 rows; loads
-//    are non-temporal (each byte is used once) and address a wave-uniform
-//    block base held in SGPRs plus per-lane offsets fixed for the whole
-//    kernel; the next block is loaded while the current one is consumed;
-//  * pass 1, QK: each lane dots its 8 dimensions of 4 tokens against q held
-//    in registers (v_dot2_f32_bf16 for bf16, FMA for fp32); the 16 partial
-//    sums of a row are combined with four DPP steps (two quad swaps, half
-//    mirror, mirror) -- no LDS round trip for the reduction;
+//  * the 1-D grid runs KV head fastest, then sequence, then partition.  The
+//    dispatcher sends workgroup i to XCD i % 8, so this spreads every
+//    sequence and partition evenly over the 8 XCDs (a partition-fastest grid
+//    gave partition p of every sequence to XCD p % 8 and left the XCD with
+//    the always-full first partitions the last to finish);
+//  * access pattern: 8 (QK) or 16 (PV) lanes cover one 256-byte (token,
+//    KV head) row, so every load instruction reads whole 128-byte lines;
+//    loads are non-temporal buffer loads (each byte is used once) through a
+//    per-block buffer resource sized to the block's valid tokens: slots
+//    past the context and blocks outside the pool read as zeros without a
+//    memory access, so every load is issued unconditionally and the wait
+//    before each step is a fixed count; the next block is in flight while
+//    the current one is consumed;
+//  * a wave's block ids come with one vector load (lane s holds step s's
+//    id) and reach SGPRs by readlane;
+//  * pass 1, QK: each lane dots its dimensions of its tokens against q held
+//    in registers (v_dot2_f32_bf16 for bf16, FMA for fp32); the partial sums
+//    of a row are combined with DPP steps -- no LDS round trip;
 //  * the partition's logits sit in LDS token-major; the exact partition max
 //    is known before any exponent, so each logit takes one exp and nothing
 //    is rescaled; the first V block is already in flight during the softmax;
-//  * pass 2, PV: same lane layout; each lane accumulates its 8 dimensions
-//    over its tokens with weights read from LDS as broadcasts; rows of a wave
-//    are summed with lane shuffles and the 4 waves through LDS;
+//  * pass 2, PV: each lane accumulates its 8 dimensions over its tokens
+//    (v_dot2 over token pairs for bf16, with bf16 weight pairs from LDS);
+//    rows of a wave are summed with lane shuffles and the 4 waves through
+//    LDS;
 //  * a partition writes (max, sum, unnormalised output) to the workspace and
 //    a second small kernel merges the partitions with log-sum-exp weights;
 //    with a single partition the first kernel writes the output itself;
-//  * masking is by select only: tokens at or past L and blocks whose id is
-//    outside the pool contribute weight 0 *and* value 0 (loaded values are
-//    replaced, never multiplied by zero), so NaN or garbage in unused slots
-//    cannot reach the output.  Every slot of a valid block is in bounds, so
-//    whole blocks are loaded without per-token branches.
+//  * masking: tokens at or past L and blocks whose id is outside the pool
+//    get logit -inf (weight 0) and read V as zeros, so NaN or garbage in
+//    unused slots cannot reach the output.
 #include <math.h>
 
 #include "pa_device.h"
@@ -48,6 +56,18 @@ constexpr int kBlock = 16;           // tokens per cache block
 constexpr int kWaves = 4;            // waves per workgroup
 constexpr int kThreads = kWaves * kWave;
 constexpr float kLog2e = 1.4426950408889634f;
+// Word 3 of a raw (unswizzled, untyped) gfx9 buffer resource.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+// Cache-policy bits of a buffer load: non-temporal (streamed, used once).
+constexpr int kCacheNT = 2;
+
+__device__ __forceinline__ int load_uniform_i32(const int32_t* base, int idx) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return ((const __attribute__((address_space(4))) int32_t*)base)[idx];
+#else
+  return base[idx];
+#endif
+}
 
 // How a wave covers one 16-token block of one KV head: kLpr lanes share a
 // row (token), each lane takes kCpl 16-byte chunks of it, and one load
@@ -76,7 +96,11 @@ struct DecodeShape {
   static constexpr int kPairsPerBlock = kBlock / 2;
   // Register cap that keeps 5 waves per SIMD for the bf16 shapes that fit
   // without spilling; the others keep what the compiler needs.
-  static constexpr int kMinWaves = (sizeof(T) == 2 && G <= 4) ? 5 : 1;
+    static constexpr int kMinWaves = (sizeof(T) == 2 && G <= 4) ? 5 : 1;
+  // Blocks each wave has in flight: the next block's K (or V) is loaded
+  // while the current one is consumed.  Deeper prefetch was measured and
+  // gains nothing at 5 waves per SIMD.
+  static constexpr int kDepth = 2;
   static_assert(kRow % 128 == 0, "rows must be whole 128-byte lines");
   static_assert(P % (kBlock * kWaves) == 0, "partition shape");
 };
@@ -171,6 +195,7 @@ struct DecodeParams {
   int max_blocks_per_seq;
   const int32_t* context_lens;
   int max_context_len;
+  int num_seqs;
   int num_heads;
   int num_kv_heads;
   float scale_log2;  // scale * log2(e): logits live in the base-2 domain
@@ -188,6 +213,22 @@ __device__ __forceinline__ int clamp_len(const DecodeParams& p, int b) {
   return len > cap ? cap : len;
 }
 
+// A bounds-checked view of one cache block: a buffer resource whose size is
+// the bytes of the block's valid tokens.  Loads past that size return zeros
+// without touching memory, so a block past the context, a block id outside
+// the pool and the slots past the context of a partial block all read as
+// zero, and every load instruction can be issued unconditionally.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const char* base,
+                                                            int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes,
+                                           kBufferRsrcWord3);
+}
+__device__ __forceinline__ uint4 buf_ld16_nt(__amdgpu_buffer_rsrc_t r,
+                                             uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCacheNT);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <typename T, int D, int G, int P>
 __global__ __launch_bounds__(kThreads) __attribute__((
     amdgpu_waves_per_eu(DecodeShape<T, D, G, P>::kMinWaves, 8))) void
@@ -196,18 +237,26 @@ decode_partition_kernel(
   using S = DecodeShape<T, D, G, P>;
   using KL = typename S::K;
   using VL = typename S::V;
-  __shared__ int s_blk[S::kBlocks];
+  constexpr int kSteps = S::kBlocks / kWaves;  // blocks per wave
+  constexpr int kDepth = S::kDepth;
   __shared__ float s_w[P * G];        // logits, then fp32 weights: [t][h]
   __shared__ uint32_t s_wp[S::kPairPv ? P / 2 * G : 1];  // bf16 weight pairs
   __shared__ float s_red[kWaves][G];
   __shared__ float s_acc[kWaves][G][D];
   __shared__ float s_m[G], s_l[G];
 
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
+  // Workgroup i runs on XCD i % 8.  KV head varies fastest, then sequence,
+  // then partition: every XCD gets the same mix of heads, sequences and
+  // partitions (a partition-fastest order would hand partition p of every
+  // sequence to XCD p % 8 -- the always-full first partitions to one XCD,
+  // the mostly empty last ones to another), and the full early partitions
+  // are dispatched before the sparse late ones.
+  const int kvh = blockIdx.x % p.num_kv_heads;
+  const int rest = blockIdx.x / p.num_kv_heads;
+  const int b = rest % p.num_seqs;
+  const int part = rest / p.num_seqs;
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
   const bool single = p.num_partitions == 1;
 
@@ -231,22 +280,31 @@ decode_partition_kernel(
   const int ntok = min(P, len - t0);
   const int nblk = (ntok + kBlock - 1) / kBlock;
 
-  // Block ids of this partition (only the ones the context covers).
-  if (tid < nblk) {
-    s_blk[tid] = p.block_tables[static_cast<int64_t>(b) * p.max_blocks_per_seq +
-                                t0 / kBlock + tid];
+  // Step s of a wave covers block j = wave + s * kWaves of the partition.
+  // Its id comes by a scalar load (block 0 of the partition stands in past
+  // nblk); valid tokens of the block: 0 past nblk or for an id outside the
+  // pool.
+  const int32_t* btab = p.block_tables +
+                        static_cast<int64_t>(b) * p.max_blocks_per_seq +
+                        t0 / kBlock;
+  // One vector load brings the wave's block ids (lane s holds step s's id);
+  // each step then takes its id into SGPRs with a readlane.
+  int my_id = 0;
+  if (lane < kSteps && wave + lane * kWaves < nblk) my_id = btab[wave + lane * kWaves];
+  int blk_off[kSteps];   // block id, 0 standing in for a bad one (uniform)
+  int nval[kSteps];      // valid tokens of the block (uniform)
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const int j = wave + s * kWaves;
+    const int blk = __builtin_amdgcn_readlane(my_id, s);
+    const bool ok = j < nblk && blk >= 0 && blk < p.num_blocks;
+    nval[s] = ok ? min(kBlock, ntok - j * kBlock) : 0;
+    blk_off[s] = ok ? blk : 0;
   }
-
-  // Wave-uniform block base (SGPRs).  An id outside the pool reads block 0
-  // and the whole block is then ignored.
-  auto block_base = [&](const char* cache, int j, bool& ok) {
-    int blk = __builtin_amdgcn_readfirstlane(s_blk[j]);
-    ok = blk >= 0 && blk < p.num_blocks;
-    blk = ok ? blk : 0;
-    return cache + static_cast<int64_t>(blk) * blk_bytes;
+  auto rsrc = [&](const char* cache, int s) {
+    return block_rsrc(cache + static_cast<int64_t>(blk_off[s]) * blk_bytes,
+                      nval[s] * row_stride);
   };
-  // Tokens of block j that lie inside the context (uniform).
-  auto valid_in = [&](int j) { return min(kBlock, ntok - j * kBlock); };
 
   // ---- pass 1: logits -----------------------------------------------------
   // Lane (krs, ke): token i * KL::kRpi + krs, chunks cc * KL::kLpr + ke.
@@ -269,61 +327,60 @@ decode_partition_kernel(
       for (int h = 0; h < G; ++h)
         qreg[cc][h] = ld16(qbase + h * S::kRow + (cc * KL::kLpr + ke) * 16);
   }
-  __syncthreads();
 
-  auto load_k = [&](int j, uint4 (*r)[KL::kCpl], bool& ok) {
-    const char* base = block_base(p.k_cache, j, ok);
+  uint4 kr[kSteps][KL::kTpl][KL::kCpl];
+  auto load_k = [&](int s) {
+    const auto r = rsrc(p.k_cache, s);
 #pragma unroll
     for (int i = 0; i < KL::kTpl; ++i)
 #pragma unroll
-      for (int cc = 0; cc < KL::kCpl; ++cc) r[i][cc] = ld16_nt(base + koff[i][cc]);
+      for (int cc = 0; cc < KL::kCpl; ++cc) kr[s][i][cc] = buf_ld16_nt(r, koff[i][cc]);
   };
 
   float mloc[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) mloc[h] = -INFINITY;
 
-  auto logits = [&](int j, const uint4 (*kr)[KL::kCpl], bool ok) {
-    const int nvalid = ok ? valid_in(j) : 0;
+  auto logits = [&](int s) {
+    const int j = wave + s * kWaves;
+    const int nvalid = nval[s];
 #pragma unroll
     for (int i = 0; i < KL::kTpl; ++i) {
-      float s[G];
+      float sc[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) s[h] = 0.f;
+      for (int h = 0; h < G; ++h) sc[h] = 0.f;
 #pragma unroll
-      for (int cc = 0; cc < KL::kCpl; ++cc) ChunkDot<T, G>::run(kr[i][cc], qreg[cc], s);
+      for (int cc = 0; cc < KL::kCpl; ++cc) ChunkDot<T, G>::run(kr[s][i][cc], qreg[cc], sc);
 #pragma unroll
-      for (int h = 0; h < G; ++h) s[h] = row_sum<KL::kLpr>(s[h]) * p.scale_log2;
+      for (int h = 0; h < G; ++h) sc[h] = row_sum<KL::kLpr>(sc[h]) * p.scale_log2;
       const int tb = i * KL::kRpi + krs;       // token inside the block
       if (nvalid < kBlock) {                   // uniform: partial or bad block
 #pragma unroll
-        for (int h = 0; h < G; ++h) s[h] = tb < nvalid ? s[h] : -INFINITY;
+        for (int h = 0; h < G; ++h) sc[h] = tb < nvalid ? sc[h] : -INFINITY;
       }
 #pragma unroll
-      for (int h = 0; h < G; ++h) mloc[h] = fmaxf(mloc[h], s[h]);
+      for (int h = 0; h < G; ++h) mloc[h] = fmaxf(mloc[h], sc[h]);
       if (ke == 0) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) s_w[(j * kBlock + tb) * G + h] = s[h];
+        for (int h = 0; h < G; ++h) s_w[(j * kBlock + tb) * G + h] = sc[h];
       }
     }
   };
-  {
-    uint4 ka[KL::kTpl][KL::kCpl], kb[KL::kTpl][KL::kCpl];
-    bool oka = false, okb = false;
-    int j = wave;
-    if (j < nblk) load_k(j, ka, oka);
-    while (j < nblk) {
-      if (j + kWaves < nblk) load_k(j + kWaves, kb, okb);
-      logits(j, ka, oka);
-      j += kWaves;
-      if (j >= nblk) break;
-      if (j + kWaves < nblk) load_k(j + kWaves, ka, oka);
-      logits(j, kb, okb);
-      j += kWaves;
-    }
+  // kDepth - 1 blocks ahead: every load is issued unconditionally (past the
+  // context it reads nothing), so the wait before each step is a fixed count.
+#pragma unroll
+  for (int s = 0; s < kDepth - 1 && s < kSteps; ++s) load_k(s);
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    if (wave + s * kWaves >= nblk) break;
+    if (s + kDepth - 1 < kSteps) load_k(s + kDepth - 1);
+    // Keep the prefetch here: without a memory clobber the compiler may sink
+    // a load down to the step that uses it.
+    __asm__ volatile("" ::: "memory");
+    logits(s);
   }
 
-  // ---- first V block in flight; softmax over the partition ---------------
+  // ---- first V blocks in flight; softmax over the partition --------------
   // Lane (vrs, ve): token i * VL::kRpi + vrs, chunks cc * VL::kLpr + ve.
   const int vrs = lane / VL::kLpr;
   const int ve = lane % VL::kLpr;
@@ -334,16 +391,16 @@ decode_partition_kernel(
     for (int cc = 0; cc < VL::kCpl; ++cc)
       voff[i][cc] = (i * VL::kRpi + vrs) * row_stride + kvh * S::kRow +
                     (cc * VL::kLpr + ve) * 16;
-  auto load_v = [&](int j, uint4 (*r)[VL::kCpl], bool& ok) {
-    const char* base = block_base(p.v_cache, j, ok);
+  uint4 vr[kSteps][VL::kTpl][VL::kCpl];
+  auto load_v = [&](int s) {
+    const auto r = rsrc(p.v_cache, s);
 #pragma unroll
     for (int i = 0; i < VL::kTpl; ++i)
 #pragma unroll
-      for (int cc = 0; cc < VL::kCpl; ++cc) r[i][cc] = ld16_nt(base + voff[i][cc]);
+      for (int cc = 0; cc < VL::kCpl; ++cc) vr[s][i][cc] = buf_ld16_nt(r, voff[i][cc]);
   };
-  uint4 va[VL::kTpl][VL::kCpl], vb[VL::kTpl][VL::kCpl];
-  bool vok_a = false, vok_b = false;
-  if (wave < nblk) load_v(wave, va, vok_a);
+#pragma unroll
+  for (int s = 0; s < kDepth - 1 && s < kSteps; ++s) load_v(s);
 
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -402,6 +459,8 @@ decode_partition_kernel(
   }
 
   // ---- pass 2: weighted sum of V -----------------------------------------
+  // Slots past the context read as zeros (see block_rsrc) and have weight 0,
+  // so NaN or garbage there cannot reach the sums.
   float acc[G][VL::kCpl][S::kEpc];
 #pragma unroll
   for (int h = 0; h < G; ++h)
@@ -410,18 +469,8 @@ decode_partition_kernel(
 #pragma unroll
       for (int x = 0; x < S::kEpc; ++x) acc[h][cc][x] = 0.f;
 
-  auto accumulate = [&](int j, uint4 (*vr)[VL::kCpl], bool ok) {
-    if (!ok) return;  // uniform: a block outside the pool adds nothing
-    const int nvalid = valid_in(j);
-    if (nvalid < kBlock) {
-      // Partial last block: replace slots past the context by zeros (they
-      // may hold anything, NaN included); their weights are 0 as well.
-#pragma unroll
-      for (int i = 0; i < VL::kTpl; ++i)
-#pragma unroll
-        for (int cc = 0; cc < VL::kCpl; ++cc)
-          if (i * VL::kRpi + vrs >= nvalid) vr[i][cc] = make_uint4(0, 0, 0, 0);
-    }
+  auto accumulate = [&](int s) {
+    const int j = wave + s * kWaves;
     if constexpr (S::kPairPv) {
 #pragma unroll
       for (int pi = 0; pi < VL::kTpl / 2; ++pi) {
@@ -431,8 +480,8 @@ decode_partition_kernel(
         for (int h = 0; h < G; ++h) wp[h] = s_wp[(j * S::kPairsPerBlock + q) * G + h];
 #pragma unroll
         for (int cc = 0; cc < VL::kCpl; ++cc) {
-          const uint4 x = vr[2 * pi][cc];
-          const uint4 y = vr[2 * pi + 1][cc];
+          const uint4 x = vr[s][2 * pi][cc];
+          const uint4 y = vr[s][2 * pi + 1][cc];
           const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
           const uint32_t ys[4] = {y.x, y.y, y.z, y.w};
 #pragma unroll
@@ -457,7 +506,7 @@ decode_partition_kernel(
 #pragma unroll
         for (int cc = 0; cc < VL::kCpl; ++cc) {
           float v[S::kEpc];
-          Widen<T>::run(vr[i][cc], v);
+          Widen<T>::run(vr[s][i][cc], v);
 #pragma unroll
           for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -467,17 +516,12 @@ decode_partition_kernel(
       }
     }
   };
-  {
-    int j = wave;
-    while (j < nblk) {
-      if (j + kWaves < nblk) load_v(j + kWaves, vb, vok_b);
-      accumulate(j, va, vok_a);
-      j += kWaves;
-      if (j >= nblk) break;
-      if (j + kWaves < nblk) load_v(j + kWaves, va, vok_a);
-      accumulate(j, vb, vok_b);
-      j += kWaves;
-    }
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    if (wave + s * kWaves >= nblk) break;
+    if (s + kDepth - 1 < kSteps) load_v(s + kDepth - 1);
+    __asm__ volatile("" ::: "memory");
+    accumulate(s);
   }
 
   // Sum the row groups of the wave (same dimensions, different tokens) with
@@ -559,7 +603,9 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p,
 template <typename T, int D, int G, int P>
 hipError_t launch_typed(const DecodeParams& prm, int num_seqs, int num_kv_heads,
                         int num_heads, hipStream_t stream) {
-  dim3 grid(prm.num_partitions, num_kv_heads, num_seqs);
+  const int64_t wgs = static_cast<int64_t>(prm.num_partitions) * num_kv_heads * num_seqs;
+  if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
+  dim3 grid(static_cast<unsigned>(wgs));
   hipLaunchKernelGGL((decode_partition_kernel<T, D, G, P>), grid,
                      dim3(kThreads), 0, stream, prm);
   hipError_t e = hipGetLastError();
@@ -623,6 +669,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan,
   prm.max_blocks_per_seq = a.max_blocks_per_seq;
   prm.context_lens = a.context_lens;
   prm.max_context_len = a.max_context_len;
+  prm.num_seqs = a.num_seqs;
   prm.num_heads = a.num_heads;
   prm.num_kv_heads = a.num_kv_heads;
   prm.scale_log2 = a.scale * kLog2e;
