@@ -9,9 +9,15 @@
 // h / G.
 //
 // Design (MI355X-first; the work is an HBM stream, ~2 FLOP per byte):
-//  * one workgroup (4 waves) per (partition of P tokens, KV head, sequence):
-//    every K/V byte of a KV head is read once for all G query heads of its
-//    group; wave w takes blocks w, w+4, ... of the partition;
+//  * one workgroup (4 waves) per (partition, KV head, sequence): every K/V
+//    byte of a KV head is read once for all G query heads of its group;
+//  * a partition is walked in chunks of 512 tokens (the chunk's logits sit
+//    in LDS); wave w takes blocks w, w+4, ... of each chunk.  The running
+//    max and sum carry from chunk to chunk and the output so far is
+//    rescaled when the max grows, so a partition of several chunks writes
+//    one partial result.  Partial writes interleaved with the K/V read
+//    stream cost HBM read bandwidth far beyond their own bytes, so the plan
+//    takes the longest partitions that still leave enough workgroups;
 //  * the 1-D grid runs KV head fastest, then sequence, then partition.  The
 //    dispatcher sends workgroup i to XCD i % 8, so this spreads every
 //    sequence and partition evenly over the 8 XCDs (a partition-fastest grid
@@ -30,9 +36,8 @@
 //  * pass 1, QK: each lane dots its dimensions of its tokens against q held
 //    in registers (v_dot2_f32_bf16 for bf16, FMA for fp32); the partial sums
 //    of a row are combined with DPP steps -- no LDS round trip;
-//  * the partition's logits sit in LDS token-major; the exact partition max
-//    is known before any exponent, so each logit takes one exp and nothing
-//    is rescaled; the first V block is already in flight during the softmax;
+//  * the chunk's exact max is known before any exponent, so each logit takes
+//    one exp; the first V block is already in flight during the softmax;
 //  * pass 2, PV: each lane accumulates its 8 dimensions over its tokens
 //    (v_dot2 over token pairs for bf16, with bf16 weight pairs from LDS);
 //    rows of a wave are summed with lane shuffles and the 4 waves through
@@ -83,26 +88,30 @@ struct BlockLayout {
   static_assert(kLpr * 16 >= 128, "whole cache lines per instruction");
 };
 
-template <typename T, int D, int G, int P>
+template <typename T, int D, int G, int C>
 struct DecodeShape {
   static constexpr int kElem = ElemTraits<T>::kBytes;
   static constexpr int kRow = D * kElem;          // bytes of one (token, KV head)
   static constexpr int kEpc = 16 / kElem;         // elements per 16-byte chunk
-  static constexpr int kBlocks = P / kBlock;      // blocks per partition
+  static constexpr int kBlocks = C / kBlock;      // blocks per chunk
   using K = BlockLayout<kRow, 8>;    // QK: 8 lanes per row, short reductions
   using V = BlockLayout<kRow, 16>;   // PV: 16 lanes per row, few accumulators
   // bf16 PV runs on v_dot2 over token pairs (i, i + 1 of a lane's tokens).
   static constexpr bool kPairPv = sizeof(T) == 2 && V::kTpl % 2 == 0;
   static constexpr int kPairsPerBlock = kBlock / 2;
-  // Register cap that keeps 5 waves per SIMD for the bf16 shapes that fit
-  // without spilling; the others keep what the compiler needs.
-    static constexpr int kMinWaves = (sizeof(T) == 2 && G <= 4) ? 5 : 1;
+  // Register floor of 3 waves per SIMD (168 VGPRs) for bf16 with G <= 4:
+  // the chunk loop keeps the output accumulators live through the QK pass,
+  // and a tighter cap made the compiler spill (measured slower).
+#ifndef PA_DECODE_MINWAVES
+#define PA_DECODE_MINWAVES 3
+#endif
+  static constexpr int kMinWaves = (sizeof(T) == 2 && G <= 4) ? PA_DECODE_MINWAVES : 1;
   // Blocks each wave has in flight: the next block's K (or V) is loaded
   // while the current one is consumed.  Deeper prefetch was measured and
-  // gains nothing at 5 waves per SIMD.
+  // gains nothing.
   static constexpr int kDepth = 2;
   static_assert(kRow % 128 == 0, "rows must be whole 128-byte lines");
-  static_assert(P % (kBlock * kWaves) == 0, "partition shape");
+  static_assert(C % (kBlock * kWaves) == 0, "chunk shape");
 };
 
 // Partial dot products of one 16-byte chunk of K with the matching chunk of
@@ -203,6 +212,7 @@ struct DecodeParams {
   float* ws_sum;     // [B, Hq, NP]
   float* ws_acc;     // [B, Hq, NP, D]
   int num_partitions;
+  int partition_tokens;  // tokens per partition, a multiple of the chunk
 };
 
 __device__ __forceinline__ int clamp_len(const DecodeParams& p, int b) {
@@ -229,21 +239,23 @@ __device__ __forceinline__ uint4 buf_ld16_nt(__amdgpu_buffer_rsrc_t r,
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <typename T, int D, int G, int P>
+template <typename T, int D, int G, int C>
 __global__ __launch_bounds__(kThreads) __attribute__((
-    amdgpu_waves_per_eu(DecodeShape<T, D, G, P>::kMinWaves, 8))) void
+    amdgpu_waves_per_eu(DecodeShape<T, D, G, C>::kMinWaves, 8))) void
 decode_partition_kernel(
     DecodeParams p) {
-  using S = DecodeShape<T, D, G, P>;
+  using S = DecodeShape<T, D, G, C>;
   using KL = typename S::K;
   using VL = typename S::V;
-  constexpr int kSteps = S::kBlocks / kWaves;  // blocks per wave
+  constexpr int kSteps = S::kBlocks / kWaves;  // blocks per wave per chunk
   constexpr int kDepth = S::kDepth;
-  __shared__ float s_w[P * G];        // logits, then fp32 weights: [t][h]
-  __shared__ uint32_t s_wp[S::kPairPv ? P / 2 * G : 1];  // bf16 weight pairs
-  __shared__ float s_red[kWaves][G];
+  __shared__ float s_w[C * G];        // chunk logits, then fp32 weights: [t][h]
+  __shared__ uint32_t s_wp[S::kPairPv ? C / 2 * G : 1];  // bf16 weight pairs
+  __shared__ float s_rmax[kWaves][G];
+  __shared__ float s_rsum[kWaves][G];
   __shared__ float s_acc[kWaves][G][D];
-  __shared__ float s_m[G], s_l[G];
+  __shared__ float s_m[G];
+  __shared__ float s_mrun[G], s_lrun[G];   // running max and sum per head
 
   // Workgroup i runs on XCD i % 8.  KV head varies fastest, then sequence,
   // then partition: every XCD gets the same mix of heads, sequences and
@@ -261,7 +273,7 @@ decode_partition_kernel(
   const bool single = p.num_partitions == 1;
 
   const int len = clamp_len(p, b);
-  const int t0 = part * P;
+  const int t0 = part * p.partition_tokens;
   const int head0 = kvh * G;
   const int row_stride = p.num_kv_heads * S::kRow;   // bytes per slot
   const int64_t blk_bytes = static_cast<int64_t>(kBlock) * row_stride;
@@ -277,190 +289,16 @@ decode_partition_kernel(
     }
     return;
   }
-  const int ntok = min(P, len - t0);
-  const int nblk = (ntok + kBlock - 1) / kBlock;
+  const int part_end = min(len, t0 + p.partition_tokens);
+  const int32_t* brow = p.block_tables +
+                        static_cast<int64_t>(b) * p.max_blocks_per_seq;
 
-  // Step s of a wave covers block j = wave + s * kWaves of the partition.
-  // Its id comes by a scalar load (block 0 of the partition stands in past
-  // nblk); valid tokens of the block: 0 past nblk or for an id outside the
-  // pool.
-  const int32_t* btab = p.block_tables +
-                        static_cast<int64_t>(b) * p.max_blocks_per_seq +
-                        t0 / kBlock;
-  // One vector load brings the wave's block ids (lane s holds step s's id);
-  // each step then takes its id into SGPRs with a readlane.
-  int my_id = 0;
-  if (lane < kSteps && wave + lane * kWaves < nblk) my_id = btab[wave + lane * kWaves];
-  int blk_off[kSteps];   // block id, 0 standing in for a bad one (uniform)
-  int nval[kSteps];      // valid tokens of the block (uniform)
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    const int j = wave + s * kWaves;
-    const int blk = __builtin_amdgcn_readlane(my_id, s);
-    const bool ok = j < nblk && blk >= 0 && blk < p.num_blocks;
-    nval[s] = ok ? min(kBlock, ntok - j * kBlock) : 0;
-    blk_off[s] = ok ? blk : 0;
-  }
-  auto rsrc = [&](const char* cache, int s) {
-    return block_rsrc(cache + static_cast<int64_t>(blk_off[s]) * blk_bytes,
-                      nval[s] * row_stride);
-  };
-
-  // ---- pass 1: logits -----------------------------------------------------
-  // Lane (krs, ke): token i * KL::kRpi + krs, chunks cc * KL::kLpr + ke.
-  const int krs = lane / KL::kLpr;
-  const int ke = lane % KL::kLpr;
-  uint32_t koff[KL::kTpl][KL::kCpl];
-#pragma unroll
-  for (int i = 0; i < KL::kTpl; ++i)
-#pragma unroll
-    for (int cc = 0; cc < KL::kCpl; ++cc)
-      koff[i][cc] = (i * KL::kRpi + krs) * row_stride + kvh * S::kRow +
-                    (cc * KL::kLpr + ke) * 16;
-  uint4 qreg[KL::kCpl][G];
-  {
-    const char* qbase = reinterpret_cast<const char*>(p.q) +
-                        (static_cast<int64_t>(b) * p.num_heads + head0) * S::kRow;
-#pragma unroll
-    for (int cc = 0; cc < KL::kCpl; ++cc)
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-        qreg[cc][h] = ld16(qbase + h * S::kRow + (cc * KL::kLpr + ke) * 16);
-  }
-
-  uint4 kr[kSteps][KL::kTpl][KL::kCpl];
-  auto load_k = [&](int s) {
-    const auto r = rsrc(p.k_cache, s);
-#pragma unroll
-    for (int i = 0; i < KL::kTpl; ++i)
-#pragma unroll
-      for (int cc = 0; cc < KL::kCpl; ++cc) kr[s][i][cc] = buf_ld16_nt(r, koff[i][cc]);
-  };
-
-  float mloc[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) mloc[h] = -INFINITY;
-
-  auto logits = [&](int s) {
-    const int j = wave + s * kWaves;
-    const int nvalid = nval[s];
-#pragma unroll
-    for (int i = 0; i < KL::kTpl; ++i) {
-      float sc[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) sc[h] = 0.f;
-#pragma unroll
-      for (int cc = 0; cc < KL::kCpl; ++cc) ChunkDot<T, G>::run(kr[s][i][cc], qreg[cc], sc);
-#pragma unroll
-      for (int h = 0; h < G; ++h) sc[h] = row_sum<KL::kLpr>(sc[h]) * p.scale_log2;
-      const int tb = i * KL::kRpi + krs;       // token inside the block
-      if (nvalid < kBlock) {                   // uniform: partial or bad block
-#pragma unroll
-        for (int h = 0; h < G; ++h) sc[h] = tb < nvalid ? sc[h] : -INFINITY;
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h) mloc[h] = fmaxf(mloc[h], sc[h]);
-      if (ke == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) s_w[(j * kBlock + tb) * G + h] = sc[h];
-      }
-    }
-  };
-  // kDepth - 1 blocks ahead: every load is issued unconditionally (past the
-  // context it reads nothing), so the wait before each step is a fixed count.
-#pragma unroll
-  for (int s = 0; s < kDepth - 1 && s < kSteps; ++s) load_k(s);
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    if (wave + s * kWaves >= nblk) break;
-    if (s + kDepth - 1 < kSteps) load_k(s + kDepth - 1);
-    // Keep the prefetch here: without a memory clobber the compiler may sink
-    // a load down to the step that uses it.
-    __asm__ volatile("" ::: "memory");
-    logits(s);
-  }
-
-  // ---- first V blocks in flight; softmax over the partition --------------
-  // Lane (vrs, ve): token i * VL::kRpi + vrs, chunks cc * VL::kLpr + ve.
-  const int vrs = lane / VL::kLpr;
-  const int ve = lane % VL::kLpr;
-  uint32_t voff[VL::kTpl][VL::kCpl];
-#pragma unroll
-  for (int i = 0; i < VL::kTpl; ++i)
-#pragma unroll
-    for (int cc = 0; cc < VL::kCpl; ++cc)
-      voff[i][cc] = (i * VL::kRpi + vrs) * row_stride + kvh * S::kRow +
-                    (cc * VL::kLpr + ve) * 16;
-  uint4 vr[kSteps][VL::kTpl][VL::kCpl];
-  auto load_v = [&](int s) {
-    const auto r = rsrc(p.v_cache, s);
-#pragma unroll
-    for (int i = 0; i < VL::kTpl; ++i)
-#pragma unroll
-      for (int cc = 0; cc < VL::kCpl; ++cc) vr[s][i][cc] = buf_ld16_nt(r, voff[i][cc]);
-  };
-#pragma unroll
-  for (int s = 0; s < kDepth - 1 && s < kSteps; ++s) load_v(s);
-
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float m = wave_max(mloc[h]);
-    if (lane == 0) s_red[wave][h] = m;
-  }
-  __syncthreads();
+  // Running softmax state of the partition (max and sum per head) lives in
+  // LDS; each lane keeps its share of the unnormalised output.
   if (tid < G) {
-    float m = s_red[0][tid];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s_red[w][tid]);
-    s_m[tid] = m;
+    s_mrun[tid] = -INFINITY;
+    s_lrun[tid] = 0.f;
   }
-  __syncthreads();
-  {
-    // Weights 2^(s - m); masked slots (-inf) become 0, and a head whose
-    // every token was masked (m = -inf) gets all-zero weights.  kThreads is a
-    // multiple of G, so each thread always works on the same head.
-    const int h = tid % G;
-    const float m = s_m[h];
-    float acc_l = 0.f;
-    auto weight = [&](float x) {
-      return (m == -INFINITY || x == -INFINITY) ? 0.f : fast_exp2(x - m);
-    };
-    if constexpr (S::kPairPv) {
-      // Pair q of block j joins the lane's tokens t and t + VL::kRpi of the
-      // PV layout; the pair is stored as two bfloat16 (low = t).
-      for (int i = tid; i < nblk * S::kPairsPerBlock * G; i += kThreads) {
-        const int pr = i / G;
-        const int j = pr / S::kPairsPerBlock;
-        const int q = pr % S::kPairsPerBlock;
-        const int ta = j * kBlock + (q / VL::kRpi) * 2 * VL::kRpi + q % VL::kRpi;
-        const float wa = weight(s_w[ta * G + h]);
-        const float wb = weight(s_w[(ta + VL::kRpi) * G + h]);
-        s_wp[i] = static_cast<uint32_t>(f32_to_bf16_rne(wa)) |
-                  (static_cast<uint32_t>(f32_to_bf16_rne(wb)) << 16);
-        acc_l += wa + wb;
-      }
-    } else {
-      for (int i = tid; i < nblk * kBlock * G; i += kThreads) {
-        const float w = weight(s_w[i]);
-        s_w[i] = w;
-        acc_l += w;
-      }
-    }
-#pragma unroll
-    for (int o = kWave / 2; o >= G; o >>= 1) acc_l += __shfl_xor(acc_l, o, kWave);
-    if (lane < G) s_red[wave][lane] = acc_l;
-  }
-  __syncthreads();
-  if (tid < G) {
-    float l = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) l += s_red[w][tid];
-    s_l[tid] = l;
-  }
-
-  // ---- pass 2: weighted sum of V -----------------------------------------
-  // Slots past the context read as zeros (see block_rsrc) and have weight 0,
-  // so NaN or garbage there cannot reach the sums.
   float acc[G][VL::kCpl][S::kEpc];
 #pragma unroll
   for (int h = 0; h < G; ++h)
@@ -469,63 +307,286 @@ decode_partition_kernel(
 #pragma unroll
       for (int x = 0; x < S::kEpc; ++x) acc[h][cc][x] = 0.f;
 
-  auto accumulate = [&](int s) {
-    const int j = wave + s * kWaves;
-    if constexpr (S::kPairPv) {
+  // The partition is walked in chunks of C tokens whose logits fit in LDS.
+  // Each chunk: logits, the chunk max, weights against the running max, and
+  // the weighted sum of V; the output so far is rescaled when the max grows.
+  // A partition of several chunks writes one partial result instead of one
+  // per chunk: partial writes interleaved with the K/V stream cost HBM
+  // read bandwidth far beyond their own size.
+  for (int tc0 = t0; tc0 < part_end; tc0 += C) {
+    const int ntok = min(C, part_end - tc0);
+    const int nblk = (ntok + kBlock - 1) / kBlock;
+    // The lane-dependent offsets below are recomputed in every chunk (a few
+    // integer ops): hoisted out of the loop, the per-step addresses of the
+    // unrolled steps would all stay live in registers and spill.
+    int ln = lane;
+    __asm__ volatile("" : "+v"(ln));
+    // Lane (krs, ke) of the QK layout: token i * KL::kRpi + krs of a block,
+    // chunks cc * KL::kLpr + ke of its row.
+    const int krs = ln / KL::kLpr;
+    const int ke = ln % KL::kLpr;
+    uint32_t koff[KL::kTpl][KL::kCpl];
 #pragma unroll
-      for (int pi = 0; pi < VL::kTpl / 2; ++pi) {
-        const int q = pi * VL::kRpi + vrs;     // pair index inside the block
-        uint32_t wp[G];
+    for (int i = 0; i < KL::kTpl; ++i)
 #pragma unroll
-        for (int h = 0; h < G; ++h) wp[h] = s_wp[(j * S::kPairsPerBlock + q) * G + h];
+      for (int cc = 0; cc < KL::kCpl; ++cc)
+        koff[i][cc] = (i * KL::kRpi + krs) * row_stride + kvh * S::kRow +
+                      (cc * KL::kLpr + ke) * 16;
+    // Lane (vrs, ve) of the PV layout.
+    const int vrs = ln / VL::kLpr;
+    const int ve = ln % VL::kLpr;
+    uint32_t voff[VL::kTpl][VL::kCpl];
 #pragma unroll
-        for (int cc = 0; cc < VL::kCpl; ++cc) {
-          const uint4 x = vr[s][2 * pi][cc];
-          const uint4 y = vr[s][2 * pi + 1][cc];
-          const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
-          const uint32_t ys[4] = {y.x, y.y, y.z, y.w};
+    for (int i = 0; i < VL::kTpl; ++i)
 #pragma unroll
-          for (int dw = 0; dw < 4; ++dw) {
-            const uint32_t lo = pack_lo(xs[dw], ys[dw]);
-            const uint32_t hi = pack_hi(xs[dw], ys[dw]);
+      for (int cc = 0; cc < VL::kCpl; ++cc)
+        voff[i][cc] = (i * VL::kRpi + vrs) * row_stride + kvh * S::kRow +
+                      (cc * VL::kLpr + ve) * 16;
+
+    // q of the group's heads, in the QK lane layout.  Loaded again for every
+    // chunk (the lines stay in cache) rather than held across the chunk
+    // loop, where it would cost 32 registers during the PV pass.
+    uint4 qreg[KL::kCpl][G];
+    {
+      const char* qbase = reinterpret_cast<const char*>(p.q) +
+                          (static_cast<int64_t>(b) * p.num_heads + head0) * S::kRow;
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-              acc[h][cc][2 * dw] = dot2_bf16(lo, wp[h], acc[h][cc][2 * dw]);
-              acc[h][cc][2 * dw + 1] = dot2_bf16(hi, wp[h], acc[h][cc][2 * dw + 1]);
+      for (int cc = 0; cc < KL::kCpl; ++cc)
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          qreg[cc][h] = ld16(qbase + h * S::kRow + (cc * KL::kLpr + ke) * 16);
+    }
+
+    // Step s of a wave covers block j = wave + s * kWaves of the chunk.  One
+    // vector load brings the wave's block ids (lane s holds step s's id);
+    // each step takes its id into SGPRs with a readlane.  Valid tokens of a
+    // block: 0 past nblk or for an id outside the pool.
+    const int32_t* btab = brow + tc0 / kBlock;
+    int my_id = 0;
+    if (lane < kSteps && wave + lane * kWaves < nblk) my_id = btab[wave + lane * kWaves];
+    int blk_off[kSteps];   // block id, 0 standing in for a bad one (uniform)
+    int nval[kSteps];      // valid tokens of the block (uniform)
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const int j = wave + s * kWaves;
+      const int blk = __builtin_amdgcn_readlane(my_id, s);
+      const bool ok = j < nblk && blk >= 0 && blk < p.num_blocks;
+      nval[s] = ok ? min(kBlock, ntok - j * kBlock) : 0;
+      blk_off[s] = ok ? blk : 0;
+    }
+    auto rsrc = [&](const char* cache, int s) {
+      return block_rsrc(cache + static_cast<int64_t>(blk_off[s]) * blk_bytes,
+                        nval[s] * row_stride);
+    };
+
+    // ---- pass 1: logits ---------------------------------------------------
+    uint4 kr[kSteps][KL::kTpl][KL::kCpl];
+    auto load_k = [&](int s) {
+      const auto r = rsrc(p.k_cache, s);
+#pragma unroll
+      for (int i = 0; i < KL::kTpl; ++i)
+#pragma unroll
+        for (int cc = 0; cc < KL::kCpl; ++cc) kr[s][i][cc] = buf_ld16_nt(r, koff[i][cc]);
+    };
+    float mloc[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) mloc[h] = -INFINITY;
+    auto logits = [&](int s) {
+      const int j = wave + s * kWaves;
+      const int nvalid = nval[s];
+#pragma unroll
+      for (int i = 0; i < KL::kTpl; ++i) {
+        float sc[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) sc[h] = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < KL::kCpl; ++cc) ChunkDot<T, G>::run(kr[s][i][cc], qreg[cc], sc);
+#pragma unroll
+        for (int h = 0; h < G; ++h) sc[h] = row_sum<KL::kLpr>(sc[h]) * p.scale_log2;
+        const int tb = i * KL::kRpi + krs;     // token inside the block
+        if (nvalid < kBlock) {                 // uniform: partial or bad block
+#pragma unroll
+          for (int h = 0; h < G; ++h) sc[h] = tb < nvalid ? sc[h] : -INFINITY;
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) mloc[h] = fmaxf(mloc[h], sc[h]);
+        if (ke == 0) {
+#pragma unroll
+          for (int h = 0; h < G; ++h) s_w[(j * kBlock + tb) * G + h] = sc[h];
+        }
+      }
+    };
+    // kDepth - 1 blocks ahead: every load is issued unconditionally (past
+    // the context it reads nothing), so the wait before each step is a fixed
+    // count.
+#pragma unroll
+    for (int s = 0; s < kDepth - 1 && s < kSteps; ++s) load_k(s);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      if (wave + s * kWaves >= nblk) break;
+      if (s + kDepth - 1 < kSteps) load_k(s + kDepth - 1);
+      // Keep the prefetch here: without a memory clobber the compiler may
+      // sink a load down to the step that uses it.
+      __asm__ volatile("" ::: "memory");
+      logits(s);
+    }
+
+    // ---- first V blocks in flight; softmax over the chunk -----------------
+    uint4 vr[kSteps][VL::kTpl][VL::kCpl];
+    auto load_v = [&](int s) {
+      const auto r = rsrc(p.v_cache, s);
+#pragma unroll
+      for (int i = 0; i < VL::kTpl; ++i)
+#pragma unroll
+        for (int cc = 0; cc < VL::kCpl; ++cc) vr[s][i][cc] = buf_ld16_nt(r, voff[i][cc]);
+    };
+#pragma unroll
+    for (int s = 0; s < kDepth - 1 && s < kSteps; ++s) load_v(s);
+
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float m = wave_max(mloc[h]);
+      if (lane == 0) s_rmax[wave][h] = m;
+    }
+    __syncthreads();
+    if (tid < G) {
+      float m = s_rmax[0][tid];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s_rmax[w][tid]);
+      s_m[tid] = m;
+    }
+    __syncthreads();
+    // New running max per head and the factor that rescales what the
+    // previous chunks accumulated (1 when the max did not move, including
+    // the all-masked -inf case; 0 for the first chunk, whose acc is 0).
+    float m_new[G], alpha[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float m_old = s_mrun[h];
+      m_new[h] = fmaxf(m_old, s_m[h]);
+      alpha[h] = m_new[h] == m_old ? 1.f : fast_exp2(m_old - m_new[h]);
+    }
+    {
+      // Weights 2^(s - m); masked slots (-inf) become 0, and a head whose
+      // every token was masked (m = -inf) gets all-zero weights.  kThreads
+      // is a multiple of G, so each thread always works on the same head.
+      const int h = tid % G;
+      const float m = m_new[h];
+      float acc_l = 0.f;
+      auto weight = [&](float x) {
+        return (m == -INFINITY || x == -INFINITY) ? 0.f : fast_exp2(x - m);
+      };
+      if constexpr (S::kPairPv) {
+        // Pair q of block j joins the lane's tokens t and t + VL::kRpi of
+        // the PV layout; the pair is stored as two bfloat16 (low = t).
+        for (int i = tid; i < nblk * S::kPairsPerBlock * G; i += kThreads) {
+          const int pr = i / G;
+          const int j = pr / S::kPairsPerBlock;
+          const int q = pr % S::kPairsPerBlock;
+          const int ta = j * kBlock + (q / VL::kRpi) * 2 * VL::kRpi + q % VL::kRpi;
+          const float wa = weight(s_w[ta * G + h]);
+          const float wb = weight(s_w[(ta + VL::kRpi) * G + h]);
+          s_wp[i] = static_cast<uint32_t>(f32_to_bf16_rne(wa)) |
+                    (static_cast<uint32_t>(f32_to_bf16_rne(wb)) << 16);
+          acc_l += wa + wb;
+        }
+      } else {
+        for (int i = tid; i < nblk * kBlock * G; i += kThreads) {
+          const float w = weight(s_w[i]);
+          s_w[i] = w;
+          acc_l += w;
+        }
+      }
+#pragma unroll
+      for (int o = kWave / 2; o >= G; o >>= 1) acc_l += __shfl_xor(acc_l, o, kWave);
+      if (lane < G) s_rsum[wave][lane] = acc_l;
+    }
+    __syncthreads();
+    // Every thread has read the old running max; thread h moves head h's
+    // state on (the next readers come after the next chunk's barriers).
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (tid == h) {
+        float l = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) l += s_rsum[w][h];
+        s_lrun[h] = s_lrun[h] * alpha[h] + l;
+        s_mrun[h] = m_new[h];
+      }
+#pragma unroll
+      for (int cc = 0; cc < VL::kCpl; ++cc)
+#pragma unroll
+        for (int x = 0; x < S::kEpc; ++x) acc[h][cc][x] *= alpha[h];
+    }
+
+    // ---- pass 2: weighted sum of V ---------------------------------------
+    // Slots past the context read as zeros (see block_rsrc) and have weight
+    // 0, so NaN or garbage there cannot reach the sums.
+    auto accumulate = [&](int s) {
+      const int j = wave + s * kWaves;
+      if constexpr (S::kPairPv) {
+#pragma unroll
+        for (int pi = 0; pi < VL::kTpl / 2; ++pi) {
+          const int q = pi * VL::kRpi + vrs;   // pair index inside the block
+          uint32_t wp[G];
+#pragma unroll
+          for (int h = 0; h < G; ++h) wp[h] = s_wp[(j * S::kPairsPerBlock + q) * G + h];
+#pragma unroll
+          for (int cc = 0; cc < VL::kCpl; ++cc) {
+            const uint4 x = vr[s][2 * pi][cc];
+            const uint4 y = vr[s][2 * pi + 1][cc];
+            const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+            const uint32_t ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+            for (int dw = 0; dw < 4; ++dw) {
+              const uint32_t lo = pack_lo(xs[dw], ys[dw]);
+              const uint32_t hi = pack_hi(xs[dw], ys[dw]);
+#pragma unroll
+              for (int h = 0; h < G; ++h) {
+                acc[h][cc][2 * dw] = dot2_bf16(lo, wp[h], acc[h][cc][2 * dw]);
+                acc[h][cc][2 * dw + 1] = dot2_bf16(hi, wp[h], acc[h][cc][2 * dw + 1]);
+              }
             }
           }
         }
-      }
-    } else {
+      } else {
 #pragma unroll
-      for (int i = 0; i < VL::kTpl; ++i) {
-        const int t = j * kBlock + i * VL::kRpi + vrs;
-        float w[G];
+        for (int i = 0; i < VL::kTpl; ++i) {
+          const int t = j * kBlock + i * VL::kRpi + vrs;
+          float w[G];
 #pragma unroll
-        for (int h = 0; h < G; ++h) w[h] = s_w[t * G + h];
+          for (int h = 0; h < G; ++h) w[h] = s_w[t * G + h];
 #pragma unroll
-        for (int cc = 0; cc < VL::kCpl; ++cc) {
-          float v[S::kEpc];
-          Widen<T>::run(vr[s][i][cc], v);
+          for (int cc = 0; cc < VL::kCpl; ++cc) {
+            float v[S::kEpc];
+            Widen<T>::run(vr[s][i][cc], v);
 #pragma unroll
-          for (int h = 0; h < G; ++h)
+            for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int x = 0; x < S::kEpc; ++x)
-              acc[h][cc][x] = fmaf(w[h], v[x], acc[h][cc][x]);
+              for (int x = 0; x < S::kEpc; ++x)
+                acc[h][cc][x] = fmaf(w[h], v[x], acc[h][cc][x]);
+          }
         }
       }
-    }
-  };
+    };
 #pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    if (wave + s * kWaves >= nblk) break;
-    if (s + kDepth - 1 < kSteps) load_v(s + kDepth - 1);
-    __asm__ volatile("" ::: "memory");
-    accumulate(s);
+    for (int s = 0; s < kSteps; ++s) {
+      if (wave + s * kWaves >= nblk) break;
+      if (s + kDepth - 1 < kSteps) load_v(s + kDepth - 1);
+      __asm__ volatile("" ::: "memory");
+      accumulate(s);
+    }
+    // The fp32 path reads its weights from s_w, which the next chunk's
+    // logits overwrite.
+    if constexpr (!S::kPairPv) {
+      if (tc0 + C < part_end) __syncthreads();
+    }
   }
 
   // Sum the row groups of the wave (same dimensions, different tokens) with
   // shuffles, then the waves through LDS.
+  const int vrs = lane / VL::kLpr;
+  const int ve = lane % VL::kLpr;
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -556,15 +617,15 @@ decode_partition_kernel(
     for (int w = 0; w < kWaves; ++w) o += s_acc[w][h][d];
     const int64_t head = static_cast<int64_t>(b) * p.num_heads + head0 + h;
     if (single) {
-      const float l = s_l[h];
+      const float l = s_lrun[h];
       T* out = reinterpret_cast<T*>(p.out) + head * D + d;
       store_out<T>(out, l > 0.f ? o / l : 0.f);
     } else {
       const int64_t slot = head * p.num_partitions + part;
       p.ws_acc[slot * D + d] = o;
       if (d == 0) {
-        p.ws_max[slot] = s_m[h];
-        p.ws_sum[slot] = s_l[h];
+        p.ws_max[slot] = s_mrun[h];
+        p.ws_sum[slot] = s_lrun[h];
       }
     }
   }
@@ -573,8 +634,8 @@ decode_partition_kernel(
 // Merge the partitions of one (sequence, query head): weights 2^(m_p - m*)
 // rescale each partition's sum and output; the result is their ratio.
 template <typename T, int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p,
-                                                         int partition_tokens) {
+__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
+  const int partition_tokens = p.partition_tokens;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int d = threadIdx.x;
@@ -600,37 +661,44 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p,
   store_out<T>(out, l > 0.f ? o / l : 0.f);
 }
 
-template <typename T, int D, int G, int P>
+template <typename T, int D, int G, int C>
 hipError_t launch_typed(const DecodeParams& prm, int num_seqs, int num_kv_heads,
                         int num_heads, hipStream_t stream) {
   const int64_t wgs = static_cast<int64_t>(prm.num_partitions) * num_kv_heads * num_seqs;
   if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
   dim3 grid(static_cast<unsigned>(wgs));
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, G, P>), grid,
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, G, C>), grid,
                      dim3(kThreads), 0, stream, prm);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || prm.num_partitions == 1) return e;
   hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(num_heads, num_seqs),
-                     dim3(D), 0, stream, prm, P);
+                     dim3(D), 0, stream, prm);
   return hipGetLastError();
 }
 
-template <typename T, int D, int P>
+template <typename T, int D, int C>
 hipError_t dispatch_group(const DecodeParams& prm, int num_seqs,
                           int num_kv_heads, int num_heads, hipStream_t s) {
   switch (num_heads / num_kv_heads) {
-    case 1: return launch_typed<T, D, 1, P>(prm, num_seqs, num_kv_heads, num_heads, s);
-    case 2: return launch_typed<T, D, 2, P>(prm, num_seqs, num_kv_heads, num_heads, s);
-    case 4: return launch_typed<T, D, 4, P>(prm, num_seqs, num_kv_heads, num_heads, s);
-    case 8: return launch_typed<T, D, 8, P>(prm, num_seqs, num_kv_heads, num_heads, s);
+    case 1: return launch_typed<T, D, 1, C>(prm, num_seqs, num_kv_heads, num_heads, s);
+    case 2: return launch_typed<T, D, 2, C>(prm, num_seqs, num_kv_heads, num_heads, s);
+    case 4: return launch_typed<T, D, 4, C>(prm, num_seqs, num_kv_heads, num_heads, s);
+    case 8: return launch_typed<T, D, 8, C>(prm, num_seqs, num_kv_heads, num_heads, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-#ifndef PA_DECODE_PARTITION
-#define PA_DECODE_PARTITION 512
+// Tokens per chunk: the logits of one chunk sit in LDS.
+constexpr int kChunkTokens = 512;
+// A partition spans one or more chunks.  Fewer, longer partitions write
+// fewer partial results (which slow the K/V stream far beyond their own
+// bytes) but leave fewer workgroups to balance; the plan takes the longest
+// partitions that still give at least this many workgroups.
+#ifndef PA_DECODE_TARGET_WGS
+#define PA_DECODE_TARGET_WGS 8192
 #endif
-constexpr int kPartitionTokens = PA_DECODE_PARTITION;
+constexpr int64_t kTargetWorkgroups = PA_DECODE_TARGET_WGS;
+constexpr int kMaxChunksPerPartition = 16;
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -638,11 +706,22 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads,
                        int head_dim, int max_context_len) {
-  (void)num_kv_heads;
   DecodePlan plan{};
-  plan.partition_tokens = kPartitionTokens;
-  int np = (max_context_len + kPartitionTokens - 1) / kPartitionTokens;
-  plan.num_partitions = np < 1 ? 1 : np;
+  const int64_t groups = static_cast<int64_t>(num_seqs) * num_kv_heads;
+  auto parts = [&](int tokens) {
+    const int np = (max_context_len + tokens - 1) / tokens;
+    return np < 1 ? 1 : np;
+  };
+  int chunks = 1;
+#ifdef PA_DECODE_CHUNKS
+  chunks = PA_DECODE_CHUNKS;
+#else
+  while (chunks < kMaxChunksPerPartition &&
+         groups * parts(kChunkTokens * chunks * 2) >= kTargetWorkgroups)
+    chunks *= 2;
+#endif
+  plan.partition_tokens = kChunkTokens * chunks;
+  plan.num_partitions = parts(plan.partition_tokens);
   if (plan.num_partitions == 1) {
     plan.workspace_bytes = 0;
     return plan;
@@ -674,13 +753,14 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan,
   prm.num_kv_heads = a.num_kv_heads;
   prm.scale_log2 = a.scale * kLog2e;
   prm.num_partitions = plan.num_partitions;
+  prm.partition_tokens = plan.partition_tokens;
   if (plan.num_partitions > 1) {
     char* ws = static_cast<char*>(a.workspace);
     prm.ws_max = reinterpret_cast<float*>(ws + plan.off_max);
     prm.ws_sum = reinterpret_cast<float*>(ws + plan.off_sum);
     prm.ws_acc = reinterpret_cast<float*>(ws + plan.off_acc);
   }
-  constexpr int P = kPartitionTokens;
+  constexpr int P = kChunkTokens;
   if (a.bf16) {
     if (a.head_dim == 128)
       return dispatch_group<bf16_t, 128, P>(prm, a.num_seqs, a.num_kv_heads, a.num_heads, stream);

@@ -16,7 +16,7 @@ hipError_t launch_store_kv(const void* k, const void* v, void* k_cache,
 
 // ---- decode ------------------------------------------------------------
 struct DecodePlan {
-  int partition_tokens;  // tokens per context partition (multiple of 64)
+  int partition_tokens;  // tokens per context partition (multiple of 512)
   int num_partitions;    // ceil(max_context_len / partition_tokens), >= 1
   size_t workspace_bytes;
   size_t off_max, off_sum, off_acc;  // byte offsets inside the workspace

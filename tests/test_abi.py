@@ -88,8 +88,12 @@ def test_decode_validation(kw, code, no_device):
 def test_decode_workspace_query():
     lib = _lib.load()
     assert lib.pa_decode_workspace_bytes(4, 8, 2, 64, 100) == 0
+    # 8192-token contexts over 2,048 (sequence, KV head) groups split into
+    # several partitions: at least two partials of (max, sum, D floats) per
+    # (sequence, query head), 256-byte aligned sections.
     one = lib.pa_decode_workspace_bytes(256, 32, 8, 128, 8192)
-    assert one >= 256 * 32 * 16 * (128 + 2) * 4
+    assert one >= 256 * 32 * 2 * (128 + 2) * 4
+    assert one % 256 == 0
     assert lib.pa_decode_workspace_bytes(0, 8, 2, 64, 100) == 0
 
 

@@ -131,3 +131,35 @@ def test_block_permutation_invariance():
     oa_, ob_ = a.run_decode(), b.run_decode()
     torch.cuda.synchronize()
     assert torch.equal(oa_, ob_)
+
+
+def _plan_partitions(lib, b, hq, hkv, d, maxlen):
+    """Partitions of the decode plan, read back from the workspace size."""
+    ws = lib.pa_decode_workspace_bytes(b, hq, hkv, d, maxlen)
+
+    def size(np_):
+        a = lambda x: (x + 255) // 256 * 256
+        slots = b * hq * np_
+        return 2 * a(slots * 4) + a(slots * d * 4)
+    return [n for n in range(1, maxlen // 512 + 2) if size(n) == ws]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_multi_chunk_partitions(dtype):
+    """Partitions of several 512-token chunks: the running max and sum carry
+    across chunks and the output is rescaled when the max grows.  64
+    sequences x 8 KV heads with 16384-token contexts make the plan take
+    1024-token partitions (2 chunks); lengths cover chunk and partition
+    edges, and one long context forces many rescales."""
+    from paged_kv_cache_slot_amd import _lib
+    lib = _lib.load()
+    hq, hkv, d = 32, 8, 64
+    assert _plan_partitions(lib, 64, hq, hkv, d, 16384) == [16], \
+        "the plan no longer splits this case into 2-chunk partitions"
+    say("decode multi-chunk", dtype)
+    rng = np.random.default_rng(77)
+    lens = [16384, 16000, 1025, 1024, 1023, 513, 512, 511, 1, 17]
+    lens += rng.integers(1, 600, size=64 - len(lens), endpoint=True).tolist()
+    lay = wl.decode_layout(lens, 16, seed=78)
+    case = DecodeCase(lay, hq, hkv, d, dtype, seed=79)
+    _check(case, seqs=list(range(10)) + [20, 40, 63])
