@@ -72,6 +72,26 @@ def store_kv(k_cache, v_cache, k, v, slot_mapping):
     return k_out, v_out
 
 
+def copy_blocks(k_cache, v_cache, pairs):
+    """Copy whole blocks, bit for bit: for each (source, destination) pair
+    block ``destination`` of both caches becomes a copy of block
+    ``source``.  Warmup Guide, Chapter 4: copy-on-write copies the one
+    shared block a sequence is about to write into.  A pair with an id
+    outside the pool is skipped.  Returns new arrays; the inputs are not
+    modified.
+    """
+    k_out = np.array(k_cache, copy=True)
+    v_out = np.array(v_cache, copy=True)
+    num_blocks = k_out.shape[0]
+    for src, dst in pairs:
+        src, dst = int(src), int(dst)
+        if not (0 <= src < num_blocks and 0 <= dst < num_blocks):
+            continue
+        k_out[dst] = k_cache[src]
+        v_out[dst] = v_cache[src]
+    return k_out, v_out
+
+
 def gather_sequence_kv(k_cache, v_cache, block_table, length, dtype):
     """Gather one sequence's first ``length`` tokens of K and V through its
     block table into contiguous float64 arrays [length, Hkv, D].

@@ -13,6 +13,9 @@ Written from:
   matrix; section 4: the bytes of one KV block.
 * "10 Serving Engines", section 10.2.3 worked example: bytes of KV cache per
   token for the Llama 3 8B shape.
+* "Warmup Guide -- Inference Serving Internals", Chapter 4 (prefix sharing and
+  copy-on-write): ref-counted blocks that several block tables name, and the
+  rule that a write into a shared block first copies that one block.
 
 Everything is done one token at a time with Python integers, so that each
 line can be checked against the description by eye.
@@ -188,3 +191,65 @@ def kv_bytes_per_token(num_layers, num_kv_heads, head_dim, itemsize):
     Warmup Guide, Chapter 2 (the KV size formula, per token and per
     sequence) and "10 Serving Engines", section 10.2.3."""
     return 2 * num_layers * num_kv_heads * head_dim * itemsize
+
+
+class RefCountedPool:
+    """A pool of physical blocks with a reference count per block.
+
+    Warmup Guide, Chapter 4: a block several sequences share is one physical
+    block named by several block tables, with a reference count; a sequence
+    about to write into a block that others also hold first takes a fresh
+    block, copies the shared block into it, lowers the shared block's count
+    and writes into its private copy.  Freed blocks (count 0) return to the
+    free list.  Free blocks are handed out from the front of the list.
+    """
+
+    def __init__(self, free_blocks):
+        self.free = list(free_blocks)
+        self.ref = {}
+
+    def allocate(self):
+        if not self.free:
+            raise MemoryError("block pool exhausted")
+        block = self.free.pop(0)
+        self.ref[block] = 1
+        return block
+
+    def share(self, block_table):
+        """A new sequence points at the same physical blocks (a prefix hit,
+        or a fork): every block's count goes up by one."""
+        for block in block_table:
+            self.ref[block] += 1
+        return list(block_table)
+
+    def release(self, block_table):
+        """A sequence ends: its blocks' counts go down; blocks no one holds
+        any more return to the free list."""
+        for block in block_table:
+            self.ref[block] -= 1
+            if self.ref[block] == 0:
+                del self.ref[block]
+                self.free.append(block)
+
+    def append(self, block_table, length, block_size):
+        """Make room for the token at position ``length`` of a sequence.
+
+        A full last block (Chapter 3's rule) means a fresh block and no copy.
+        Otherwise the token goes into the last block; if another sequence
+        holds that block too, it is copied first (copy-on-write).  Returns
+        (block_table, length + 1, slot of the new token, copy) where copy is
+        (source block, destination block) or None.
+        """
+        table = list(block_table)
+        copy = None
+        if append_takes_new_block(length, block_size):
+            table.append(self.allocate())
+        else:
+            last = table[-1]
+            if self.ref[last] > 1:
+                fresh = self.allocate()
+                copy = (last, fresh)
+                self.ref[last] -= 1
+                table[-1] = fresh
+        slot = slot_of(table, length, block_size)
+        return table, length + 1, slot, copy

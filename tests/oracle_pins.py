@@ -90,6 +90,85 @@ def check_allocation_rules():
             assert 0 <= om.internal_waste(n, bs) <= bs - 1
 
 
+def check_prefix_sharing_example():
+    """Warmup Guide, Chapter 4 figure: a prompt in blocks [P0][P1] shared by
+    requests A, B, C (ref count 3); each continuation goes to a private
+    block; the prefix is stored once (5 physical blocks, no copies)."""
+    g = _golden("prefix_sharing.json")
+    bs = g["block_size"]
+    pool = om.RefCountedPool(range(32))
+    prompt, length = [], 0
+    for _ in range(g["prompt_tokens"]):
+        prompt, length, _, copy = pool.append(prompt, length, bs)
+        assert copy is None
+    tables = {"A": prompt}
+    for name in g["requests"][1:]:
+        tables[name] = pool.share(prompt)
+    copies = 0
+    for name in g["requests"]:
+        tables[name], _, slot, copy = pool.append(tables[name], length, bs)
+        copies += copy is not None
+        assert slot == tables[name][-1] * bs, (name, slot)
+    exp = g["expected"]
+    for blk in prompt:
+        assert pool.ref[blk] == exp["prefix_ref_count"], pool.ref
+    lasts = [tables[n][-1] for n in g["requests"]]
+    assert len(set(lasts)) == len(lasts)
+    for blk in lasts:
+        assert pool.ref[blk] == exp["continuation_ref_count"]
+    for name in g["requests"]:
+        assert tables[name][:exp["tables_share_first_blocks"]] == prompt
+    used = {b for t in tables.values() for b in t}
+    assert len(used) == exp["physical_blocks_used"], used
+    assert copies == exp["copies"]
+
+
+def check_copy_on_write_partial_block():
+    """Warmup Guide, Chapter 4: appending into a partially filled block that
+    another sequence also holds copies that one block first, lowers its ref
+    count and writes into the private copy; the last holder then writes in
+    place; a released sequence's unshared blocks return to the pool."""
+    bs = 4
+    pool = om.RefCountedPool(range(8))
+    a, length = [], 0
+    for _ in range(6):                    # 6 tokens: P0 full, P1 holds 2
+        a, length, _, copy = pool.append(a, length, bs)
+        assert copy is None
+    p0, p1 = a
+    b = pool.share(a)
+    assert pool.ref[p0] == 2 and pool.ref[p1] == 2
+    a, la, slot_a, copy_a = pool.append(a, length, bs)
+    assert copy_a is not None and copy_a[0] == p1 and copy_a[1] not in (p0, p1)
+    assert a == [p0, copy_a[1]] and slot_a == copy_a[1] * bs + 2
+    assert pool.ref[p1] == 1 and pool.ref[copy_a[1]] == 1
+    b, lb, slot_b, copy_b = pool.append(b, length, bs)
+    assert copy_b is None and b == [p0, p1] and slot_b == p1 * bs + 2
+    assert la == lb == 7
+    free_before = len(pool.free)
+    pool.release(a)
+    assert pool.ref[p0] == 1 and copy_a[1] in pool.free
+    assert len(pool.free) == free_before + 1
+
+
+def check_copy_blocks_against_brute():
+    """Block copy, element by element: each destination block of both caches
+    equals its source block; pairs with an id outside the pool and all other
+    blocks are left alone."""
+    rng = np.random.default_rng(11)
+    kc = rng.integers(0, 2**16, size=(9, 4, 2, 8), dtype=np.uint16)
+    vc = rng.integers(0, 2**16, size=(9, 4, 2, 8), dtype=np.uint16)
+    pairs = [(1, 5), (7, 2), (-1, 3), (4, 9), (0, 8)]
+    ko, vo = oa.copy_blocks(kc, vc, pairs)
+    dst_of = {5: 1, 2: 7, 8: 0}
+    for blk in range(9):
+        src = dst_of.get(blk, blk)
+        for s in range(4):
+            for h in range(2):
+                for d in range(8):
+                    assert ko[blk, s, h, d] == kc[src, s, h, d]
+                    assert vo[blk, s, h, d] == vc[src, s, h, d]
+
+
 def check_decode_slot_closed_form():
     """ModelRunner page, section 2 (prepare_decode): the new token's slot is
     last_block * bs + last_block_num_tokens - 1.  For tables built by the
@@ -467,6 +546,9 @@ ALL_CHECKS = [
     check_allocation_rules,
     check_decode_slot_closed_form,
     check_decode_padding,
+    check_prefix_sharing_example,
+    check_copy_on_write_partial_block,
+    check_copy_blocks_against_brute,
     check_kv_bytes,
     check_bf16_widening,
     check_store_against_brute,

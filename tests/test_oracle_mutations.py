@@ -147,6 +147,44 @@ def _blocks_floor(num_tokens, block_size):
     return num_tokens // block_size                  # planted: floor
 
 
+_ORIG_POOL_APPEND = om.RefCountedPool.append
+
+
+def _pool_append_never_copies(self, block_table, length, block_size):
+    table = list(block_table)
+    if om.append_takes_new_block(length, block_size):
+        table.append(self.allocate())
+    # planted: writes into a shared block without copying it
+    return table, length + 1, om.slot_of(table, length, block_size), None
+
+
+def _pool_append_no_decrement(self, block_table, length, block_size):
+    table = list(block_table)
+    copy = None
+    if om.append_takes_new_block(length, block_size):
+        table.append(self.allocate())
+    elif self.ref[table[-1]] > 1:
+        fresh = self.allocate()
+        copy = (table[-1], fresh)                    # planted: no decrement
+        table[-1] = fresh
+    return table, length + 1, om.slot_of(table, length, block_size), copy
+
+
+def _pool_share_no_count(self, block_table):
+    return list(block_table)                         # planted: no ref bump
+
+
+def _copy_blocks_reversed(k_cache, v_cache, pairs):
+    k_out = np.array(k_cache, copy=True)
+    v_out = np.array(v_cache, copy=True)
+    for src, dst in pairs:
+        if min(src, dst) < 0 or max(src, dst) >= k_out.shape[0]:
+            continue
+        k_out[src] = k_cache[dst]                    # planted: reversed
+        v_out[src] = v_cache[dst]
+    return k_out, v_out
+
+
 MUTATIONS = {
     "drop_scale": (oa, "attend", _attend_factory(drop_scale=True)),
     "no_normalize": (oa, "attend", _attend_factory(no_normalize=True)),
@@ -161,6 +199,10 @@ MUTATIONS = {
     "prefill_cu_k": (om, "prefill_metadata", _prefill_meta_cu_k_wrong),
     "store_no_skip": (oa, "store_kv", _store_no_skip),
     "blocks_floor": (om, "blocks_needed", _blocks_floor),
+    "cow_never_copies": (om.RefCountedPool, "append", _pool_append_never_copies),
+    "cow_no_decrement": (om.RefCountedPool, "append", _pool_append_no_decrement),
+    "share_no_count": (om.RefCountedPool, "share", _pool_share_no_count),
+    "copy_blocks_reversed": (oa, "copy_blocks", _copy_blocks_reversed),
 }
 
 
