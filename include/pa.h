@@ -1,9 +1,10 @@
 /*
  * pa.h -- C ABI of libpa, the MI355X (gfx950) paged KV-cache hot path.
  *
- * Three operations over a block-table-indexed KV cache:
+ * Operations over a block-table-indexed KV cache:
  *
  *   pa_store_kv        scatter new K/V rows into their physical slots
+ *   pa_copy_blocks     copy whole blocks (the data side of copy-on-write)
  *   pa_decode          one query row per sequence against its paged context
  *   pa_prefill_varlen  packed variable-length (chunked) prefill, causal,
  *                      history read through block tables
@@ -103,6 +104,34 @@ pa_status pa_store_kv(const void* k, const void* v, void* k_cache,
                       int64_t num_tokens, int32_t num_kv_heads,
                       int32_t head_dim, int64_t num_slots, pa_dtype dtype,
                       void* stream);
+
+/*
+ * pa_copy_blocks -- copy whole cache blocks, bit for bit.
+ *
+ * For every i in [0, num_pairs): block block_pairs[2i + 1] (destination) of
+ * k_cache and of v_cache becomes a copy of block block_pairs[2i] (source).
+ * This is the data side of copy-on-write: a sequence about to write into a
+ * block that other sequences also hold copies that one block into a fresh
+ * block, lowers the shared block's reference count and writes into its copy
+ * ("Warmup Guide -- Inference Serving Internals", Chapter 4).  The
+ * reference counts and block tables are host metadata, not this call's.
+ *
+ *   k_cache, v_cache  device, [num_blocks, block_bytes bytes] each (any
+ *                     block size, head count, head_dim or element type)
+ *   block_pairs       device int32 [num_pairs, 2]: (source, destination)
+ *   block_bytes       bytes of one block of one cache, a multiple of 16
+ *
+ * A pair with an id outside [0, num_blocks), or with source == destination,
+ * copies nothing.  Preconditions: destinations are distinct and no block is
+ * both a source and a destination in the same call (the copies run in
+ * parallel; a chain or a repeated destination leaves unspecified contents).
+ * num_pairs == 0 or block_bytes == 0 is a no-op returning PA_OK;
+ * PA_ERR_UNSUPPORTED for block_bytes above 1 GiB or unaligned pointers.
+ */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache,
+                         const int32_t* block_pairs, int64_t num_pairs,
+                         int64_t block_bytes, int64_t num_blocks,
+                         void* stream);
 
 /*
  * Bytes of workspace pa_decode needs for these sizes (0 when one context

@@ -34,6 +34,8 @@ SIGNATURES = {
     "pa_store_kv": (ctypes.c_int, [
         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
         _i64, _i32, _i32, _i64, ctypes.c_int, _c_void_p]),
+    "pa_copy_blocks": (ctypes.c_int, [
+        _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p]),
     "pa_decode_workspace_bytes": (_size, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (ctypes.c_int, [
         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32,

@@ -85,6 +85,22 @@ pa_status pa_store_kv(const void* k, const void* v, void* k_cache,
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+pa_status pa_copy_blocks(void* k_cache, void* v_cache,
+                         const int32_t* block_pairs, int64_t num_pairs,
+                         int64_t block_bytes, int64_t num_blocks,
+                         void* stream) {
+  if (num_pairs < 0 || block_bytes < 0 || num_blocks < 0) return PA_ERR_SHAPE;
+  if (num_pairs == 0 || block_bytes == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_pairs) return PA_ERR_NULL;
+  if (block_bytes % 16 != 0 || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_UNSUPPORTED;
+  hipError_t e = pa::launch_copy_blocks(k_cache, v_cache, block_pairs,
+                                        num_pairs, block_bytes, num_blocks,
+                                        static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads,
                                  int32_t num_kv_heads, int32_t head_dim,
                                  int32_t max_context_len) {

@@ -14,6 +14,12 @@ hipError_t launch_store_kv(const void* k, const void* v, void* k_cache,
                            int64_t num_tokens, int64_t row_bytes,
                            int64_t num_slots, hipStream_t stream);
 
+// ---- block copy (copy-on-write) -----------------------------------------
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache,
+                              const int32_t* block_pairs, int64_t num_pairs,
+                              int64_t block_bytes, int64_t num_blocks,
+                              hipStream_t stream);
+
 // ---- decode ------------------------------------------------------------
 struct DecodePlan {
   int partition_tokens;  // tokens per context partition (multiple of 512)

@@ -8,6 +8,8 @@ Serving Internals", Chapter 3 (slot = block id * block size + offset).
 Vectorised with numpy; nothing here runs on the GPU.
 """
 
+import collections
+
 import numpy as np
 
 
@@ -77,3 +79,73 @@ def prefill_inputs(tables, num_cached, num_scheduled, block_size, width=None):
         "block_tables": block_table_matrix(tables, width),
         "needs_block_tables": bool(cu_k[-1] > cu_q[-1]),
     }
+
+
+class BlockPool:
+    """Physical blocks with reference counts: prefix sharing, fork and
+    copy-on-write ("Warmup Guide -- Inference Serving Internals", Chapters 3
+    and 4).
+
+    A block named by several block tables is stored once; its count says how
+    many tables name it.  Appending a token that falls into a block others
+    also hold first moves the appender onto a private copy of that block:
+    the pool hands out a fresh block, records (shared, fresh) as a copy for
+    ``pa_copy_blocks`` to carry out, and lowers the shared block's count.
+    Blocks whose count drops to zero return to the free list.
+
+    Tables are Python lists of block ids; this class is host bookkeeping only.
+    """
+
+    def __init__(self, num_blocks, order=None):
+        ids = np.arange(num_blocks) if order is None else np.asarray(order)
+        self.refs = np.zeros(num_blocks, dtype=np.int64)
+        self._free = collections.deque(int(b) for b in ids)
+
+    @property
+    def num_free(self):
+        return len(self._free)
+
+    def _take(self):
+        if not self._free:
+            raise MemoryError("no free block")
+        blk = self._free.popleft()
+        self.refs[blk] = 1
+        return blk
+
+    def share(self, table):
+        """A second table naming the same blocks (a prefix hit or a fork)."""
+        if len(table):
+            np.add.at(self.refs, np.asarray(table, dtype=np.int64), 1)
+        return list(table)
+
+    def release(self, table):
+        """Drop one table's hold on its blocks."""
+        for blk in table:
+            self.refs[blk] -= 1
+            if self.refs[blk] == 0:
+                self._free.append(int(blk))
+
+    def append_slots(self, tables, lens, block_size):
+        """Room for one new token at the end of every sequence of a batch.
+
+        ``tables`` (lists, updated in place) and ``lens`` (token counts before
+        the append) describe the batch.  Returns (slot_mapping int32 [B],
+        copies int32 [C, 2]): the slot each new token is stored at, and the
+        (source, destination) block copies that must run before the store.
+        """
+        slots = np.empty(len(tables), dtype=np.int32)
+        copies = []
+        for i, (table, n) in enumerate(zip(tables, lens)):
+            n = int(n)
+            off = n % block_size
+            if off == 0:                      # last block full, or no block
+                table.append(self._take())
+            elif self.refs[table[-1]] > 1:    # shared partial block: copy it
+                shared = table[-1]
+                fresh = self._take()
+                self.refs[shared] -= 1
+                copies.append((shared, fresh))
+                table[-1] = fresh
+            slots[i] = table[-1] * block_size + off
+        pairs = np.asarray(copies, dtype=np.int32).reshape(-1, 2)
+        return slots, pairs

@@ -75,6 +75,27 @@ def store_kv(k, v, k_cache, v_cache, slot_mapping):
     _lib.check("pa_store_kv", st)
 
 
+def copy_blocks(k_cache, v_cache, block_pairs):
+    """Copy whole blocks of both caches ([NB, ...], same shape): for each row
+    (src, dst) of block_pairs (int32 [P, 2]), block dst becomes a copy of
+    block src.  Pairs naming a block outside the pool copy nothing."""
+    _need_gpu(k_cache, v_cache, block_pairs)
+    _i32(block_pairs, "block_pairs")
+    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache must match in shape and dtype")
+    if block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [P, 2]")
+    if not k_cache.is_contiguous() or not v_cache.is_contiguous():
+        raise ValueError("caches must be contiguous")
+    num_blocks = k_cache.shape[0]
+    block_bytes = k_cache.numel() // max(num_blocks, 1) * k_cache.element_size()
+    lib = _lib.load()
+    st = lib.pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_pairs),
+                            block_pairs.shape[0], block_bytes, num_blocks,
+                            _stream(k_cache))
+    _lib.check("pa_copy_blocks", st)
+
+
 def decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
                            max_context_len):
     return int(_lib.load().pa_decode_workspace_bytes(

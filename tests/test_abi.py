@@ -137,3 +137,27 @@ def _prefill(lib, **kw):
 ])
 def test_prefill_validation(kw, code, no_device):
     assert _prefill(_lib.load(), **kw) == code
+
+
+def _copy(lib, **kw):
+    a = dict(kc=FAKE, vc=FAKE, pairs=FAKE, n=3, bb=32768, nb=100, stream=None)
+    a.update(kw)
+    return lib.pa_copy_blocks(a["kc"], a["vc"], a["pairs"], a["n"], a["bb"],
+                              a["nb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=0), 0),                               # nothing to copy: no-op
+    (dict(bb=0), 0),                              # empty blocks: no-op
+    (dict(n=-1), 2),
+    (dict(bb=-16), 2),
+    (dict(nb=-1), 2),
+    (dict(kc=None), 1),
+    (dict(vc=None), 1),
+    (dict(pairs=None), 1),
+    (dict(bb=32760), 3),                          # not a multiple of 16
+    (dict(kc=MISALIGNED), 3),
+    (dict(bb=(1 << 30) + 16 * 1024), 3),          # block above 1 GiB
+])
+def test_copy_blocks_validation(kw, code, no_device):
+    assert _copy(_lib.load(), **kw) == code

@@ -63,3 +63,48 @@ def test_prefill_matches_oracle(bs):
             assert got[key].tolist() == want[key], key
         for key in ("max_seqlen_q", "max_seqlen_k", "needs_block_tables"):
             assert got[key] == want[key], key
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_block_pool_matches_oracle(seed):
+    """Random fork / append / release traffic: the product pool and the
+    oracle's ref-counted pool produce the same tables, slots, block copies
+    and counts."""
+    rng = np.random.default_rng(seed)
+    bs, nb = 4, 64
+    pool = pm.BlockPool(nb)
+    ref = om.RefCountedPool(range(nb))
+    seqs = []                 # (product table, oracle table, length)
+    for _ in range(200):
+        op = rng.integers(0, 10)
+        if op < 2 or not seqs:                       # new sequence
+            seqs.append(([], [], 0))
+        elif op < 4:                                 # fork
+            t, r, n = seqs[rng.integers(0, len(seqs))]
+            seqs.append((pool.share(t), ref.share(r), n))
+        elif op < 5 and len(seqs) > 1:               # finish
+            t, r, n = seqs.pop(rng.integers(0, len(seqs)))
+            pool.release(t)
+            ref.release(r)
+        else:                                        # one decode step
+            picks = rng.choice(len(seqs), size=min(len(seqs), 3),
+                               replace=False)
+            if pool.num_free < 2 * len(picks):
+                continue
+            tables = [seqs[i][0] for i in picks]
+            lens = [seqs[i][2] for i in picks]
+            slots, pairs = pool.append_slots(tables, lens, bs)
+            want_pairs = []
+            for k, i in enumerate(picks):
+                t, r, n = seqs[i]
+                r, n2, slot, copy = ref.append(r, n, bs)
+                assert slot == slots[k]
+                if copy is not None:
+                    want_pairs.append(list(copy))
+                seqs[i] = (t, r, n2)
+            assert pairs.tolist() == want_pairs
+        for t, r, _ in seqs:
+            assert t == r
+        for blk, count in ref.ref.items():
+            assert pool.refs[blk] == count
+        assert pool.num_free == len(ref.free)
