@@ -12,6 +12,10 @@
 //  * one workgroup (4 waves) per (M-tile of 128 rows, KV head, sequence);
 //    the G query heads of a KV head are packed into M (row m = position
 //    m / G, head m % G), so a K/V tile loaded once serves all of them;
+//  * a one-workgroup plan kernel first sorts the (sequence, M-tile) items
+//    by the key tiles they read, into the workspace, and workgroups take
+//    them heaviest first: with mixed history lengths the longest items no
+//    longer start late and set the tail;
 //  * per 64-key tile the workgroup gathers K and V through the block table
 //    straight into LDS with DMA loads (global_load_lds_dwordx4; one
 //    wave-uniform block lookup per 1 KiB load; double buffered; 16-byte
@@ -105,6 +109,7 @@ struct PrefillShape {
 struct PrefillParams {
   int mtiles;                // M-tiles per (sequence, KV head)
   int num_seqs;
+  const int32_t* order;      // work items, heaviest first (null: natural order)
   void* out;
   const char* q;
   int64_t total_q;
@@ -135,6 +140,36 @@ __device__ __forceinline__ int load_uniform_i32(const int32_t* base, int idx) {
 #else
   return base[idx];
 #endif
+}
+
+// Query rows and cached keys of sequence b, clamped so that no index leaves
+// the buffers: rows q0 .. q0 + lq - 1 of q, keys 0 .. lk - 1.
+struct SeqExtent {
+  int q0, lq, lk;
+};
+__device__ __forceinline__ SeqExtent seq_extent(const int32_t* cu_q,
+                                                const int32_t* cu_k, int b,
+                                                int max_q, int max_k,
+                                                int64_t total_q,
+                                                int max_blocks) {
+  int q0 = cu_q[b];
+  int lq = cu_q[b + 1] - q0;
+  int lk = cu_k[b + 1] - cu_k[b];
+  q0 = q0 < 0 ? 0 : q0;
+  lq = lq < 0 ? 0 : (lq > max_q ? max_q : lq);
+  if (q0 + lq > total_q) lq = static_cast<int>(total_q - q0 < 0 ? 0 : total_q - q0);
+  lk = lk < 0 ? 0 : (lk > max_k ? max_k : lk);
+  if (lk > max_blocks * kBlock) lk = max_blocks * kBlock;
+  return {q0, lq, lk};
+}
+
+// Keys an M-tile reads: the causal limit of its last row, or all lk.
+__device__ __forceinline__ int tile_key_end(const SeqExtent& e, int g, int m0,
+                                            int causal) {
+  const int i_last = min(e.lq - 1, (m0 + kBM - 1) / g);
+  int kend = e.lk;
+  if (causal) kend = min(e.lk, e.lk - e.lq + i_last + 1);
+  return kend < 0 ? 0 : kend;
 }
 
 template <int kChunks>
@@ -200,44 +235,37 @@ prefill_kernel(PrefillParams p) {
   extern __shared__ __align__(16) char smem[];
   // [K buffer 0][K buffer 1][V buffer 0][V buffer 1]
 
-  // XCD-aware order.  The dispatcher deals workgroups to the 8 XCDs round
-  // robin (id % 8), each XCD with its own L2.  A (sequence, KV head) group's
-  // M-tiles all read the same K/V tiles, so they go to one XCD, heaviest
-  // M-tile (longest causal key range) first; group g runs on XCD g % 8.
-  // The grid holds 8 * ceil(groups / 8) * mtiles ids; ids past the last
-  // group exit.
+  // Workgroup lin takes work item order[lin / Hkv] (a (sequence, M-tile)
+  // pair; the plan kernel lists them heaviest first, so the longest ones
+  // start first and short ones fill the tail) for KV head lin % Hkv.  The
+  // dispatcher deals workgroups to the 8 XCDs round robin (id % 8), each
+  // with its own L2; with Hkv a multiple of 8 every M-tile of one (sequence,
+  // KV head) group, which all read the same K/V tiles, runs on one XCD.
   const int lin = blockIdx.x;
-  const int slot = lin / 8;
-  const int grp = (slot / p.mtiles) * 8 + lin % 8;
-  if (grp >= p.num_seqs * p.num_kv_heads) return;     // uniform
-  const int mtile = p.mtiles - 1 - slot % p.mtiles;
-  const int kvh = grp % p.num_kv_heads;
-  const int b = grp / p.num_kv_heads;
+  const int kvh = lin % p.num_kv_heads;
+  const int rank = lin / p.num_kv_heads;
+  const int item = p.order ? load_uniform_i32(p.order, rank) : rank;
+  if (item < 0 || item >= p.num_seqs * p.mtiles) return;   // uniform
+  const int b = item / p.mtiles;
+  const int mtile = item % p.mtiles;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
   const int j = lane % 32;                   // this lane's row inside the wave
   const int hh = lane / 32;                  // lane half
 
-  // Sequence extent, clamped so no index leaves the buffers.
-  int q0 = p.cu_q[b];
-  int lq = p.cu_q[b + 1] - q0;
-  int lk = p.cu_k[b + 1] - p.cu_k[b];
-  q0 = q0 < 0 ? 0 : q0;
-  lq = lq < 0 ? 0 : (lq > p.max_seqlen_q ? p.max_seqlen_q : lq);
-  if (q0 + lq > p.total_q) lq = static_cast<int>(p.total_q - q0 < 0 ? 0 : p.total_q - q0);
-  lk = lk < 0 ? 0 : (lk > p.max_seqlen_k ? p.max_seqlen_k : lk);
-  if (lk > p.max_blocks_per_seq * kBlock) lk = p.max_blocks_per_seq * kBlock;
+  const SeqExtent ext = seq_extent(p.cu_q, p.cu_k, b, p.max_seqlen_q,
+                                   p.max_seqlen_k, p.total_q,
+                                   p.max_blocks_per_seq);
+  const int q0 = ext.q0;
+  const int lq = ext.lq;
+  const int lk = ext.lk;
   const int mrows = lq * G;
   const int m0 = mtile * kBM;
   if (m0 >= mrows) return;                   // uniform over the workgroup
 
   // Key range this workgroup needs.
-  const int i_last = min(lq - 1, (m0 + kBM - 1) / G);
-  int kend = lk;
-  if (p.causal) kend = min(lk, lk - lq + i_last + 1);
-  kend = kend < 0 ? 0 : kend;
-  const int ntiles = (kend + kBN - 1) / kBN;
+  const int ntiles = (tile_key_end(ext, G, m0, p.causal) + kBN - 1) / kBN;
 
   // This lane's row: M row m -> query position i, head h.
   const int m = m0 + wave * 32 + j;
@@ -502,17 +530,116 @@ prefill_kernel(PrefillParams p) {
     }
 }
 
+// Longest-first schedule.  One workgroup weighs every (sequence, M-tile)
+// item by the key tiles it reads (plus one for its fixed cost; 0 for an
+// M-tile past the sequence's rows) and writes the items to `order` by
+// descending weight: a counting sort over weight bins in LDS (weights past
+// the last bin share it).  Items of equal weight land in any order; the
+// attention results do not depend on the schedule.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBins = 4096;
+constexpr int kBinsPerThread = kPlanBins / kPlanThreads;
+
+struct PlanParams {
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int num_seqs;
+  int mtiles;
+  int group;
+  int max_seqlen_q;
+  int max_seqlen_k;
+  int64_t total_q;
+  int max_blocks_per_seq;
+  int causal;
+};
+
+__device__ __forceinline__ int plan_bin(const PlanParams& q, int item) {
+  const int b = item / q.mtiles;
+  const int m0 = (item % q.mtiles) * kBM;
+  const SeqExtent e = seq_extent(q.cu_q, q.cu_k, b, q.max_seqlen_q,
+                                 q.max_seqlen_k, q.total_q,
+                                 q.max_blocks_per_seq);
+  if (m0 >= e.lq * q.group) return 0;
+  const int w = (tile_key_end(e, q.group, m0, q.causal) + kBN - 1) / kBN + 1;
+  return w < kPlanBins ? w : kPlanBins - 1;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
+    PlanParams q, int32_t* __restrict__ order) {
+  __shared__ int bins[kPlanBins];
+  __shared__ int part[kPlanThreads];
+  const int tid = threadIdx.x;
+  const int n = q.num_seqs * q.mtiles;
+  for (int i = tid; i < kPlanBins; i += kPlanThreads) bins[i] = 0;
+  __syncthreads();
+  for (int item = tid; item < n; item += kPlanThreads)
+    atomicAdd(&bins[plan_bin(q, item)], 1);
+  __syncthreads();
+  // Exclusive prefix over the bins from the heaviest down: thread t owns
+  // bins kPlanBins - 1 - (kBinsPerThread * t + k).
+  int cnt[kBinsPerThread];
+  int mine = 0;
+#pragma unroll
+  for (int k = 0; k < kBinsPerThread; ++k) {
+    cnt[k] = bins[kPlanBins - 1 - (kBinsPerThread * tid + k)];
+    mine += cnt[k];
+  }
+  part[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off *= 2) {
+    const int add = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
+  int start = part[tid] - mine;
+#pragma unroll
+  for (int k = 0; k < kBinsPerThread; ++k) {
+    bins[kPlanBins - 1 - (kBinsPerThread * tid + k)] = start;
+    start += cnt[k];
+  }
+  __syncthreads();
+  for (int item = tid; item < n; item += kPlanThreads)
+    order[atomicAdd(&bins[plan_bin(q, item)], 1)] = item;
+}
+
+int m_tiles(int max_seqlen_q, int group) {
+  return static_cast<int>((static_cast<int64_t>(max_seqlen_q) * group + kBM - 1) / kBM);
+}
+
 template <typename T, int D, int G>
-hipError_t launch_typed(const PrefillParams& prm, int num_seqs, int max_seqlen_q,
-                        int num_kv_heads, hipStream_t stream) {
+hipError_t launch_typed(const PrefillParams& prm, const PrefillArgs& a,
+                        hipStream_t stream) {
   using S = PrefillShape<T, D>;
-  const int mtiles = (max_seqlen_q * G + kBM - 1) / kBM;
+  const int mtiles = m_tiles(a.max_seqlen_q, G);
+  const int64_t items = static_cast<int64_t>(a.num_seqs) * mtiles;
+  const int64_t wgs = items * a.num_kv_heads;
+  if (wgs > 0x7fffffff) return hipErrorNotSupported;
   const size_t lds = S::kLds;
   PrefillParams pr = prm;
   pr.mtiles = mtiles;
-  pr.num_seqs = num_seqs;
-  const int64_t groups8 = (static_cast<int64_t>(num_seqs) * num_kv_heads + 7) / 8 * 8;
-  const int64_t wgs = groups8 * mtiles;
+  pr.num_seqs = a.num_seqs;
+  pr.order = nullptr;
+  if (a.workspace != nullptr &&
+      a.workspace_bytes >= static_cast<size_t>(items) * sizeof(int32_t)) {
+    PlanParams q{};
+    q.cu_q = a.cu_seqlens_q;
+    q.cu_k = a.cu_seqlens_k;
+    q.num_seqs = a.num_seqs;
+    q.mtiles = mtiles;
+    q.group = G;
+    q.max_seqlen_q = a.max_seqlen_q;
+    q.max_seqlen_k = a.max_seqlen_k;
+    q.total_q = a.total_q;
+    q.max_blocks_per_seq = a.max_blocks_per_seq;
+    q.causal = a.causal ? 1 : 0;
+    int32_t* order = static_cast<int32_t*>(a.workspace);
+    hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0,
+                       stream, q, order);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    pr.order = order;
+  }
   if (lds > 65536) {
     static bool raised = false;   // once per kernel instantiation
     if (!raised) {
@@ -529,20 +656,28 @@ hipError_t launch_typed(const PrefillParams& prm, int num_seqs, int max_seqlen_q
 }
 
 template <typename T, int D>
-hipError_t dispatch_group(const PrefillParams& prm, int g, int num_seqs,
-                          int max_seqlen_q, int num_kv_heads, hipStream_t s) {
+hipError_t dispatch_group(const PrefillParams& prm, const PrefillArgs& a, int g,
+                          hipStream_t s) {
   switch (g) {
-    case 1: return launch_typed<T, D, 1>(prm, num_seqs, max_seqlen_q, num_kv_heads, s);
-    case 2: return launch_typed<T, D, 2>(prm, num_seqs, max_seqlen_q, num_kv_heads, s);
-    case 4: return launch_typed<T, D, 4>(prm, num_seqs, max_seqlen_q, num_kv_heads, s);
-    case 8: return launch_typed<T, D, 8>(prm, num_seqs, max_seqlen_q, num_kv_heads, s);
+    case 1: return launch_typed<T, D, 1>(prm, a, s);
+    case 2: return launch_typed<T, D, 2>(prm, a, s);
+    case 4: return launch_typed<T, D, 4>(prm, a, s);
+    case 8: return launch_typed<T, D, 8>(prm, a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-size_t prefill_workspace_bytes(int, int, int, int, int, int) { return 0; }
+// The schedule: one int32 per (sequence, M-tile) item.  The M-tile count
+// uses the G the launch dispatches on (num_heads / num_kv_heads).
+size_t prefill_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads,
+                               int, int max_seqlen_q, int) {
+  const int g = num_heads / num_kv_heads;
+  if (g < 1) return 0;
+  const int64_t items = static_cast<int64_t>(num_seqs) * m_tiles(max_seqlen_q, g);
+  return static_cast<size_t>((items * 4 + 255) / 256 * 256);
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   PrefillParams prm{};
@@ -564,13 +699,11 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   prm.causal = a.causal ? 1 : 0;
   const int g = a.num_heads / a.num_kv_heads;
   if (a.bf16) {
-    if (a.head_dim == 128)
-      return dispatch_group<bf16_t, 128>(prm, g, a.num_seqs, a.max_seqlen_q, a.num_kv_heads, stream);
-    return dispatch_group<bf16_t, 64>(prm, g, a.num_seqs, a.max_seqlen_q, a.num_kv_heads, stream);
+    if (a.head_dim == 128) return dispatch_group<bf16_t, 128>(prm, a, g, stream);
+    return dispatch_group<bf16_t, 64>(prm, a, g, stream);
   }
-  if (a.head_dim == 128)
-    return dispatch_group<float, 128>(prm, g, a.num_seqs, a.max_seqlen_q, a.num_kv_heads, stream);
-  return dispatch_group<float, 64>(prm, g, a.num_seqs, a.max_seqlen_q, a.num_kv_heads, stream);
+  if (a.head_dim == 128) return dispatch_group<float, 128>(prm, a, g, stream);
+  return dispatch_group<float, 64>(prm, a, g, stream);
 }
 
 }  // namespace pa

@@ -179,11 +179,12 @@ class PrefillCase:
         ops.store_kv(self.k_new, self.v_new, self.kc, self.vc,
                      self.slot_mapping)
 
-    def run_prefill(self, out=None):
+    def run_prefill(self, out=None, workspace=None):
         return ops.prefill_varlen(
             self.q, self.kc, self.vc, self.cu_q, self.cu_k,
             self.meta["max_seqlen_q"], self.meta["max_seqlen_k"],
-            self.block_tables, scale=self.scale, causal=self.causal, out=out)
+            self.block_tables, scale=self.scale, causal=self.causal, out=out,
+            workspace=workspace)
 
     def oracle_meta(self):
         seqs = [{"block_table": [int(x) for x in t], "num_cached": int(h),

@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import workloads as wl
+from paged_kv_cache_slot_amd import ops
 from tests.gpu_harness import (TOL, DecodeCase, PrefillCase, bits_equal, f64,
                                say)
 
@@ -152,3 +153,45 @@ def test_multi_token_verify_rows(lq):
     hist = rng.integers(100, 3000, 64)
     lay = wl.prefill_layout(hist, [lq] * 64, 16, seed=lq + 40)
     _check(PrefillCase(lay, 32, 8, 128, "bf16", seed=lq + 41))
+
+
+def _item_weights(lq, lk, g, causal, bm=128, bn=64):
+    """Key tiles each (sequence, M-tile) item reads, plus one; 0 for an
+    M-tile past the sequence's rows -- the longest-first schedule's key."""
+    mtiles = -(-max(lq) * g // bm)
+    w = []
+    for n, k in zip(lq, lk):
+        for mt in range(mtiles):
+            m0 = mt * bm
+            if m0 >= n * g:
+                w.append(0)
+                continue
+            i_last = min(n - 1, (m0 + bm - 1) // g)
+            kend = min(k, k - n + i_last + 1) if causal else k
+            w.append(-(-max(kend, 0) // bn) + 1)
+    return np.asarray(w)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_longest_first_schedule(causal):
+    """The plan kernel's schedule in the workspace lists every (sequence,
+    M-tile) item once, by non-increasing work; the attention result with a
+    workspace filled with garbage beforehand is unchanged."""
+    say("prefill schedule", causal)
+    hist, chunk = [0, 900, 37, 400, 0, 1500], [130, 64, 200, 1, 0, 90]
+    lay = wl.prefill_layout(hist, chunk, 16, seed=31)
+    case = PrefillCase(lay, 16, 4, 128, "bf16", seed=32, causal=causal)
+    m = case.meta
+    need = ops.prefill_workspace_bytes(len(hist), 16, 4, 128, m["max_seqlen_q"],
+                                       m["max_seqlen_k"])
+    ws = torch.full((need // 4,), -7, dtype=torch.int32, device="cuda")
+    got, _ = _check(case)
+    out2 = case.run_prefill(workspace=ws)
+    torch.cuda.synchronize()
+    assert bits_equal(wl.host_bits(out2), wl.host_bits(case.run_prefill()))
+    g = 4
+    mtiles = -(-m["max_seqlen_q"] * g // 128)
+    order = ws.cpu().numpy()[: len(hist) * mtiles]
+    assert sorted(order.tolist()) == list(range(len(hist) * mtiles))
+    w = _item_weights(chunk, [h + c for h, c in zip(hist, chunk)], g, causal)
+    assert np.all(np.diff(w[order]) <= 0), w[order]
