@@ -45,9 +45,7 @@ namespace pa {
 namespace {
 
 constexpr int kBlock = 16;         // tokens per cache block
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * kWave;
-constexpr int kBM = 128;           // M rows (query row x head) per workgroup
+constexpr int kMinBM = 128;        // fewest M rows per workgroup (any shape)
 constexpr int kBN = 64;            // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -96,13 +94,26 @@ struct PrefillShape {
   // 16 lanes).  Both are filled by LDS DMA (global_load_lds_dwordx4), each
   // double buffered.
   static constexpr int kTile = kBN * kRow;
+  // Where a wave fits in 256 registers (two per SIMD), 8 waves share each
+  // K/V tile: 256 M rows per workgroup halve the gather traffic per row,
+  // and with one workgroup per CU the LDS holds three K/V stages (tile
+  // kt + 2 in flight while tile kt is computed).  fp32 with D = 128 needs
+  // one wave per SIMD: 4 waves, two stages (128 KiB).
+  static constexpr int kWaves = (kBf16 || D == 64) ? 8 : 4;
+  static constexpr int kStages = kWaves == 8 ? 3 : 2;
+  static constexpr size_t kLds = 2 * kStages * static_cast<size_t>(kTile);
+  static constexpr int kOccupancy = kWaves == 8 ? 2 : 1;   // waves per SIMD
+  static constexpr int kThreads = kWaves * kWave;
+  static constexpr int kBM = kWaves * 32;                 // M rows per workgroup
   static constexpr int kRowsPerDma = 1024 / kRow;         // rows per 1 KiB DMA
   static constexpr int kDmaPerWave = kTile / 1024 / kWaves;
+  static constexpr int kLoadsPerTile = 2 * kDmaPerWave;   // per lane, K and V
   static constexpr int kQSteps = D / Mma<T>::kK;          // MFMAs per S tile
   static constexpr int kPvSteps = kBN / Mma<T>::kK;       // MFMAs per O tile
   static constexpr int kDTiles = D / 32;                  // O^T M-tiles
-  static constexpr size_t kLds = 4 * static_cast<size_t>(kTile);
   static_assert(kTile % (1024 * kWaves) == 0, "tile DMA split");
+  static_assert(kLds <= 160 * 1024, "LDS per CU");
+  static_assert(kStages * kLoadsPerTile <= 63, "vmcnt range");
   static_assert(kBlock % kRowsPerDma == 0, "a DMA load stays in one block");
 };
 
@@ -165,8 +176,8 @@ __device__ __forceinline__ SeqExtent seq_extent(const int32_t* cu_q,
 
 // Keys an M-tile reads: the causal limit of its last row, or all lk.
 __device__ __forceinline__ int tile_key_end(const SeqExtent& e, int g, int m0,
-                                            int causal) {
-  const int i_last = min(e.lq - 1, (m0 + kBM - 1) / g);
+                                            int bm, int causal) {
+  const int i_last = min(e.lq - 1, (m0 + bm - 1) / g);
   int kend = e.lk;
   if (causal) kend = min(e.lk, e.lk - e.lq + i_last + 1);
   return kend < 0 ? 0 : kend;
@@ -181,13 +192,39 @@ __device__ __forceinline__ int v_swz(int row) {
 
 // 16 bytes per lane from global memory straight into LDS
 // (global_load_lds_dwordx4): lane l's bytes land at lds + 16 l; `lds` must be
-// the same for the whole wave.  Completion is counted by vmcnt.
-__device__ __forceinline__ void dma16(const void* src, void* lds) {
+// the same for the whole wave (it goes to M0).  Completion is counted by
+// vmcnt.  Issued from inline assembly: the compiler cannot tell which LDS
+// bytes the load writes and, seeing the builtin, would wait for it before
+// the next LDS read of any buffer -- which would make the prefetch of later
+// tiles wait for the current one.  The caller orders the loads against LDS
+// reads with explicit vmcnt waits and barriers.
+__device__ __forceinline__ void dma16(const void* src, char* lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds)));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(m0) : "memory", "m0");
 #else
   (void)src;
   (void)lds;
+#endif
+}
+
+// Wait until at most N vector memory loads of this lane are in flight
+// (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+#endif
+}
+
+// Workgroup barrier after this wave's LDS reads have completed.  Unlike
+// __syncthreads it does not also wait for every vector load in flight (the
+// prefetched K/V tiles).
+__device__ __forceinline__ void lds_barrier() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #endif
 }
 
@@ -221,19 +258,18 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const float* v) {
                                              pack_bf16x2(v[2], v[3]));
 }
 
-// Two waves per SIMD: one wave's softmax overlaps the other's MFMAs.  fp32
-// with D = 128 needs 128 KiB of LDS, so one workgroup per CU: no register
-// cap there (it would only spill).
+// Two waves per SIMD (8-wave shapes): one wave's softmax overlaps the
+// other's MFMAs.  fp32 with D = 128 runs one wave per SIMD: no register cap
+// there (it would only spill).
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
-    PrefillShape<T, D>::kLds <= 80 * 1024 ? 2 : 1,
-    PrefillShape<T, D>::kLds <= 80 * 1024 ? 2 : 1))) void
+__global__ __launch_bounds__((PrefillShape<T, D>::kThreads)) __attribute__((amdgpu_waves_per_eu(
+    PrefillShape<T, D>::kOccupancy, PrefillShape<T, D>::kOccupancy))) void
 prefill_kernel(PrefillParams p) {
   using S = PrefillShape<T, D>;
   using M = Mma<T>;
   typedef typename M::op_t op_t;
   extern __shared__ __align__(16) char smem[];
-  // [K buffer 0][K buffer 1][V buffer 0][V buffer 1]
+  // [K stage 0 .. kStages - 1][V stage 0 .. kStages - 1]
 
   // Workgroup lin takes work item order[lin / Hkv] (a (sequence, M-tile)
   // pair; the plan kernel lists them heaviest first, so the longest ones
@@ -261,11 +297,11 @@ prefill_kernel(PrefillParams p) {
   const int lq = ext.lq;
   const int lk = ext.lk;
   const int mrows = lq * G;
-  const int m0 = mtile * kBM;
+  const int m0 = mtile * S::kBM;
   if (m0 >= mrows) return;                   // uniform over the workgroup
 
   // Key range this workgroup needs.
-  const int ntiles = (tile_key_end(ext, G, m0, p.causal) + kBN - 1) / kBN;
+  const int ntiles = (tile_key_end(ext, G, m0, S::kBM, p.causal) + kBN - 1) / kBN;
 
   // This lane's row: M row m -> query position i, head h.
   const int m = m0 + wave * 32 + j;
@@ -295,6 +331,16 @@ prefill_kernel(PrefillParams p) {
     }
   }
 
+  // Q must have arrived before the tile loop: a wait for it inside the loop
+  // would also wait for the K/V loads in flight there.
+#pragma unroll
+  for (int s = 0; s < S::kQSteps; ++s) {
+    if constexpr (S::kBf16)
+      asm volatile("" :: "v"(qb[s].x), "v"(qb[s].y), "v"(qb[s].z), "v"(qb[s].w));
+    else
+      asm volatile("" :: "v"(qb[s]));
+  }
+
   const int64_t row_stride = static_cast<int64_t>(p.num_kv_heads) * S::kRow;
   const int64_t blk_bytes = row_stride * kBlock;
   const int32_t* btab = p.block_tables +
@@ -315,20 +361,21 @@ prefill_kernel(PrefillParams p) {
     dma_k_off[q] = static_cast<uint32_t>(row_base + (pos ^ k_swz<S::kChunks>(r)) * 16);
     dma_v_off[q] = static_cast<uint32_t>(row_base + (pos ^ v_swz<S::kChunks>(r)) * 16);
   }
-  auto dma_tile = [&](int kt, char* kbuf, char* vbuf) {
+  // Every lane issues exactly kLoadsPerTile loads per tile, so that the
+  // waits below count tiles.  Rows of blocks past the context, or with an
+  // id outside the pool, are read from block 0 instead: they are past Lk
+  // (masked by select in S, zeroed in V) or the block table is invalid.
+  auto dma_tile = [&](int kt, char* kbuf, char* vbuf) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < S::kDmaPerWave; ++q) {
       const int ii = wave * S::kDmaPerWave + q;
       const int r0 = ii * S::kRowsPerDma;
       const int bi = kt * (kBN / kBlock) + r0 / kBlock;    // uniform
-      if (bi < nblk_ctx) {
-        const int blk = load_uniform_i32(btab, bi);
-        if (blk >= 0 && blk < p.num_blocks) {
-          const int64_t base = static_cast<int64_t>(blk) * blk_bytes;
-          dma16(p.k_cache + base + dma_k_off[q], kbuf + ii * 1024);
-          dma16(p.v_cache + base + dma_v_off[q], vbuf + ii * 1024);
-        }
-      }
+      int blk = bi < nblk_ctx ? load_uniform_i32(btab, bi) : 0;
+      blk = blk >= 0 && blk < p.num_blocks ? blk : 0;
+      const int64_t base = static_cast<int64_t>(blk) * blk_bytes;
+      dma16(p.k_cache + base + dma_k_off[q], kbuf + ii * 1024);
+      dma16(p.v_cache + base + dma_v_off[q], vbuf + ii * 1024);
     }
   };
 
@@ -356,7 +403,7 @@ prefill_kernel(PrefillParams p) {
     // test pool); P is 0 there, but 0 * NaN is NaN, so zero them.
     const int kbase = kt * kBN;
     if (kbase + kBN > lk) {
-      for (int i = tid; i < kBN * S::kChunks; i += kThreads) {
+      for (int i = tid; i < kBN * S::kChunks; i += S::kThreads) {
         const int r = i / S::kChunks;
         if (kbase + r >= lk)
           *reinterpret_cast<uint4*>(s_v + r * S::kRow + (i % S::kChunks) * 16) =
@@ -492,24 +539,28 @@ prefill_kernel(PrefillParams p) {
     }
   };
 
-  char* const kbuf0 = smem;
-  char* const kbuf1 = smem + S::kTile;
-  char* const vbuf0 = smem + 2 * S::kTile;
-  char* const vbuf1 = smem + 3 * S::kTile;
-  if (ntiles > 0) dma_tile(0, kbuf0, vbuf0);
-  for (int kt = 0; kt < ntiles; kt += 2) {
-    // Tile kt lives in buffers 0, tile kt + 1 in buffers 1.  Before the
-    // barrier this thread's DMA loads of the tile have landed; after it
-    // every wave's have, and every wave is done with the other buffers.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt + 1 < ntiles) dma_tile(kt + 1, kbuf1, vbuf1);
-    compute(kt, kbuf0, vbuf0);
-    if (kt + 1 >= ntiles) break;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt + 2 < ntiles) dma_tile(kt + 2, kbuf0, vbuf0);
-    compute(kt + 1, kbuf1, vbuf1);
+  // K/V stages: tile kt lives in stage kt % kStages.  Tiles up to
+  // kt + kStages - 2 are in flight when tile kt is waited for; after the
+  // barrier every wave's loads of tile kt have landed and every wave is
+  // done reading tile kt - 1, whose stage then takes tile kt + kStages - 1.
+  auto kbuf = [&](int st) __attribute__((always_inline)) { return smem + st * S::kTile; };
+  auto vbuf = [&](int st) __attribute__((always_inline)) {
+    return smem + (S::kStages + st) * S::kTile;
+  };
+#pragma unroll
+  for (int st = 0; st < S::kStages - 1; ++st)
+    if (st < ntiles) dma_tile(st, kbuf(st), vbuf(st));
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int ahead = min(S::kStages - 2, ntiles - 1 - kt);   // tiles after kt in flight
+    if (S::kStages >= 3 && ahead >= 1)
+      wait_vm<(S::kStages >= 3 ? S::kLoadsPerTile : 0)>();
+    else
+      wait_vm<0>();
+    lds_barrier();
+    const int nt = kt + S::kStages - 1;
+    if (nt < ntiles) dma_tile(nt, kbuf(nt % S::kStages), vbuf(nt % S::kStages));
+    const int st = kt % S::kStages;
+    compute(kt, kbuf(st), vbuf(st));
   }
 
   // ---- normalise and write: lane (j, hh) holds dims (r/4)*8 + hh*4 + r%4
@@ -545,6 +596,7 @@ struct PlanParams {
   const int32_t* cu_k;
   int num_seqs;
   int mtiles;
+  int bm;                    // M rows per workgroup
   int group;
   int max_seqlen_q;
   int max_seqlen_k;
@@ -555,12 +607,12 @@ struct PlanParams {
 
 __device__ __forceinline__ int plan_bin(const PlanParams& q, int item) {
   const int b = item / q.mtiles;
-  const int m0 = (item % q.mtiles) * kBM;
+  const int m0 = (item % q.mtiles) * q.bm;
   const SeqExtent e = seq_extent(q.cu_q, q.cu_k, b, q.max_seqlen_q,
                                  q.max_seqlen_k, q.total_q,
                                  q.max_blocks_per_seq);
   if (m0 >= e.lq * q.group) return 0;
-  const int w = (tile_key_end(e, q.group, m0, q.causal) + kBN - 1) / kBN + 1;
+  const int w = (tile_key_end(e, q.group, m0, q.bm, q.causal) + kBN - 1) / kBN + 1;
   return w < kPlanBins ? w : kPlanBins - 1;
 }
 
@@ -603,15 +655,15 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
     order[atomicAdd(&bins[plan_bin(q, item)], 1)] = item;
 }
 
-int m_tiles(int max_seqlen_q, int group) {
-  return static_cast<int>((static_cast<int64_t>(max_seqlen_q) * group + kBM - 1) / kBM);
+int m_tiles(int max_seqlen_q, int group, int bm) {
+  return static_cast<int>((static_cast<int64_t>(max_seqlen_q) * group + bm - 1) / bm);
 }
 
 template <typename T, int D, int G>
 hipError_t launch_typed(const PrefillParams& prm, const PrefillArgs& a,
                         hipStream_t stream) {
   using S = PrefillShape<T, D>;
-  const int mtiles = m_tiles(a.max_seqlen_q, G);
+  const int mtiles = m_tiles(a.max_seqlen_q, G, S::kBM);
   const int64_t items = static_cast<int64_t>(a.num_seqs) * mtiles;
   const int64_t wgs = items * a.num_kv_heads;
   if (wgs > 0x7fffffff) return hipErrorNotSupported;
@@ -627,6 +679,7 @@ hipError_t launch_typed(const PrefillParams& prm, const PrefillArgs& a,
     q.cu_k = a.cu_seqlens_k;
     q.num_seqs = a.num_seqs;
     q.mtiles = mtiles;
+    q.bm = S::kBM;
     q.group = G;
     q.max_seqlen_q = a.max_seqlen_q;
     q.max_seqlen_k = a.max_seqlen_k;
@@ -651,7 +704,7 @@ hipError_t launch_typed(const PrefillParams& prm, const PrefillArgs& a,
     }
   }
   hipLaunchKernelGGL((prefill_kernel<T, D, G>), dim3(static_cast<unsigned>(wgs)),
-                     dim3(kThreads), lds, stream, pr);
+                     dim3(S::kThreads), lds, stream, pr);
   return hipGetLastError();
 }
 
@@ -669,13 +722,14 @@ hipError_t dispatch_group(const PrefillParams& prm, const PrefillArgs& a, int g,
 
 }  // namespace
 
-// The schedule: one int32 per (sequence, M-tile) item.  The M-tile count
-// uses the G the launch dispatches on (num_heads / num_kv_heads).
+// The schedule: one int32 per (sequence, M-tile) item, counted for the
+// smallest M-tile of any shape and the G the launch dispatches on
+// (num_heads / num_kv_heads).
 size_t prefill_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads,
                                int, int max_seqlen_q, int) {
   const int g = num_heads / num_kv_heads;
   if (g < 1) return 0;
-  const int64_t items = static_cast<int64_t>(num_seqs) * m_tiles(max_seqlen_q, g);
+  const int64_t items = static_cast<int64_t>(num_seqs) * m_tiles(max_seqlen_q, g, kMinBM);
   return static_cast<size_t>((items * 4 + 255) / 256 * 256);
 }
 

@@ -189,9 +189,10 @@ def test_longest_first_schedule(causal):
     out2 = case.run_prefill(workspace=ws)
     torch.cuda.synchronize()
     assert bits_equal(wl.host_bits(out2), wl.host_bits(case.run_prefill()))
-    g = 4
-    mtiles = -(-m["max_seqlen_q"] * g // 128)
+    g, bm = 4, 256          # bf16 with D = 128: 8 waves x 32 rows per M-tile
+    mtiles = -(-m["max_seqlen_q"] * g // bm)
     order = ws.cpu().numpy()[: len(hist) * mtiles]
     assert sorted(order.tolist()) == list(range(len(hist) * mtiles))
-    w = _item_weights(chunk, [h + c for h, c in zip(hist, chunk)], g, causal)
+    w = _item_weights(chunk, [h + c for h, c in zip(hist, chunk)], g, causal,
+                      bm=bm)
     assert np.all(np.diff(w[order]) <= 0), w[order]
