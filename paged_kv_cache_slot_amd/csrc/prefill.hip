@@ -9,32 +9,38 @@
 // 0 .. Lk - Lq + i.  out = softmax(scale * q K^T) V per row and head.
 //
 // Design (MI355X-first; this is the dense contraction of the path):
-//  * one workgroup (4 waves) per (M-tile of 128 rows, KV head, sequence);
-//    the G query heads of a KV head are packed into M (row m = position
-//    m / G, head m % G), so a K/V tile loaded once serves all of them;
+//  * one workgroup per (M-tile, KV head, sequence): 8 waves and 256 rows
+//    for bf16 (and fp32 with D = 64), 4 waves and 128 rows for fp32 with
+//    D = 128; the G query heads of a KV head are packed into M (row m =
+//    position m / G, head m % G), so a K/V tile loaded once serves all of
+//    them and all waves;
 //  * a one-workgroup plan kernel first sorts the (sequence, M-tile) items
 //    by the key tiles they read, into the workspace, and workgroups take
 //    them heaviest first: with mixed history lengths the longest items no
 //    longer start late and set the tail;
 //  * per 64-key tile the workgroup gathers K and V through the block table
-//    straight into LDS with DMA loads (global_load_lds_dwordx4; one
-//    wave-uniform block lookup per 1 KiB load; double buffered; 16-byte
-//    chunks XOR-swizzled by row), the next tile in flight while the current
-//    one is computed; one barrier per tile;
+//    straight into LDS with DMA loads (global_load_lds_dwordx4, issued from
+//    inline assembly; one wave-uniform block lookup per 1 KiB load; 16-byte
+//    chunks XOR-swizzled by row) into a ring of stages: tile kt + 2 is in
+//    flight while tile kt is computed, with one barrier per tile;
 //  * each wave computes S^T = K Q^T for its 32 rows with
 //    v_mfma_f32_32x32x16_bf16 (fp32 I/O: v_mfma_f32_32x32x2_f32), Q^T held
 //    in registers as the B operand.  In the accumulator layout every lane
-//    owns one query row, so the online softmax (running max, rescale, sum)
-//    is per lane plus one exchange between the two lane halves, and the
+//    owns one query row, so the online softmax is per lane plus one
+//    exchange between the two lane halves (v_permlane32_swap), and the
 //    probabilities already sit in the B-operand layout of O^T += V^T P^T --
 //    no shuffles or LDS round trip for P; the V^T operand comes straight
 //    from the row-major V tile through LDS transpose reads
 //    (ds_read_b64_tr_b16);
+//  * the softmax is VALU work next to the MFMAs and sets the pace, so its
+//    common path is short: bf16 weights are taken against the running
+//    reference max without a max scan, and the row sum over the packed
+//    weights costs one dot2 per pair; the exact step (max scan, rescale of
+//    O) runs on a row's first tile and when the max grows by more than 2^8;
 //  * masking is by select: keys past the causal limit or past Lk get weight
 //    exactly 0, and V rows past Lk are zeroed in LDS on the one tile that
-//    crosses Lk (a NaN there would survive a multiplication by zero);
-//  * only tiles that cross the causal diagonal or Lk evaluate the mask; the
-//    running max moves lazily, so O is rescaled on few tiles.
+//    crosses Lk (a NaN there would survive a multiplication by zero); only
+//    tiles that cross the causal diagonal or Lk evaluate the mask.
 #include <math.h>
 
 #include "pa_device.h"
@@ -91,8 +97,8 @@ struct PrefillShape {
   // the row's chunk p ^ swizzle(r), so the lanes of one operand read touch
   // different banks: r % kChunks for K (32 rows, one chunk each), and
   // ((r % 4) << 2) for V (the transpose reads take 4 rows x 2 chunks per
-  // 16 lanes).  Both are filled by LDS DMA (global_load_lds_dwordx4), each
-  // double buffered.
+  // 16 lanes).  Both are filled by LDS DMA (global_load_lds_dwordx4) into
+  // a ring of kStages stages.
   static constexpr int kTile = kBN * kRow;
   // Where a wave fits in 256 registers (two per SIMD), 8 waves share each
   // K/V tile: 256 M rows per workgroup halve the gather traffic per row,
@@ -256,6 +262,44 @@ template <>
 __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const float* v) {
   *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]),
                                              pack_bf16x2(v[2], v[3]));
+}
+
+// The value lane l ^ 32 holds (v_permlane32_swap: no LDS round trip).
+__device__ __forceinline__ float swap_halves(float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false, false);
+  return __uint_as_float(__lane_id() < 32 ? r[1] : r[0]);
+#else
+  return x;
+#endif
+}
+
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+
+// Weights exp2(scale * s - max) of one lane's 32 logits (two S^T tiles),
+// rounded to bfloat16 and packed as the B operands of the four PV steps
+// (step q: registers (q % 2) * 8 .. + 7 of tile q / 2); returns their sum,
+// taken over the rounded values.
+__device__ __forceinline__ float bf16_weights(const f32x16_v (&s)[2], float scale,
+                                              float neg_max, uint4 (&pb)[4]) {
+  const bf16x2_v ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+  float sum[2] = {0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = (q % 2) * 8 + 2 * k;
+      const float e0 = fast_exp2(fmaf(s[q / 2][r], scale, neg_max));
+      const float e1 = fast_exp2(fmaf(s[q / 2][r + 1], scale, neg_max));
+      w[k] = pack_bf16x2(e0, e1);
+      sum[q / 2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, w[k]),
+                                                   ones, sum[q / 2], false);
+    }
+    pb[q] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  return sum[0] + sum[1];
 }
 
 // Two waves per SIMD (8-wave shapes): one wave's softmax overlaps the
@@ -462,38 +506,73 @@ prefill_kernel(PrefillParams p) {
           sacc[t][r] = kpos <= lim ? sacc[t][r] : -INFINITY;
         }
     }
-    float tmax = -INFINITY;
+    uint4 pb[4];   // bf16: packed weights, the B operand of each PV step
+    if constexpr (S::kBf16) {
+      // Fast path: weights against the current reference max, without a
+      // max scan.  The row sum is taken over the rounded weights (the ones
+      // the PV product uses), two per dot2.  A lane whose share of the sum
+      // stays <= 2^13 had every weight <= 2^13: nothing overflows.  If all
+      // its weights are <= 2^8 the check passes, so the exact path below
+      // runs only on a row's first tile and where its max grows by > 2^8.
+      float psum = bf16_weights(sacc, p.scale_log2,
+                                run_max == -INFINITY ? 0.f : -run_max, pb);
+      const bool exact = run_max == -INFINITY || !(psum <= 8192.f);
+      if (__any(exact)) {
+        float tmax = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[t][r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave)) * p.scale_log2;
-    // The reference max moves only when it would grow by more than 2^8:
-    // weights stay <= 256 and the rescale of O is skipped on most tiles.
-    // Any reference gives the same O / l; this one keeps every term finite.
-    const bool grow = tmax > run_max + 8.f;
-    if (__any(grow)) {
-      const float new_max = grow ? tmax : run_max;
-      const float alpha = run_max == -INFINITY ? 0.f : fast_exp2(run_max - new_max);
-      run_max = new_max;
-      run_sum *= alpha;
+          for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[t][r]);
+        tmax = fmaxf(tmax, swap_halves(tmax)) * p.scale_log2;
+        const bool grow = tmax > run_max + 8.f;
+        if (__any(grow)) {
+          const float new_max = grow ? tmax : run_max;
+          const float alpha = run_max == -INFINITY ? 0.f : fast_exp2(run_max - new_max);
+          run_max = new_max;
+          run_sum *= alpha;
 #pragma unroll
-      for (int t = 0; t < S::kDTiles; ++t)
+          for (int t = 0; t < S::kDTiles; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
-    }
-    // A row that has seen no visible key yet keeps max -inf and weights 0.
-    const float neg_max = run_max == -INFINITY ? 0.f : -run_max;
-    float psum = 0.f;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = fast_exp2(fmaf(sacc[t][r], p.scale_log2, neg_max));
-        sacc[t][r] = pr;
-        psum += pr;
+            for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
+        }
+        psum = bf16_weights(sacc, p.scale_log2,
+                            run_max == -INFINITY ? 0.f : -run_max, pb);
       }
-    run_sum += psum;
+      run_sum += psum;
+    } else {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[t][r]);
+      tmax = fmaxf(tmax, swap_halves(tmax)) * p.scale_log2;
+      // The reference max moves only when it would grow by more than 2^8:
+      // weights stay <= 256 and the rescale of O is skipped on most tiles.
+      // Any reference gives the same O / l; this one keeps every term finite.
+      const bool grow = tmax > run_max + 8.f;
+      if (__any(grow)) {
+        const float new_max = grow ? tmax : run_max;
+        const float alpha = run_max == -INFINITY ? 0.f : fast_exp2(run_max - new_max);
+        run_max = new_max;
+        run_sum *= alpha;
+#pragma unroll
+        for (int t = 0; t < S::kDTiles; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
+      }
+      // A row that has seen no visible key yet keeps max -inf and weights 0.
+      const float neg_max = run_max == -INFINITY ? 0.f : -run_max;
+      float psum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pr = fast_exp2(fmaf(sacc[t][r], p.scale_log2, neg_max));
+          sacc[t][r] = pr;
+          psum += pr;
+        }
+      run_sum += psum;
+    }
 
     // ---- O^T += V^T P^T -------------------------------------------------
 #pragma unroll
@@ -502,12 +581,7 @@ prefill_kernel(PrefillParams p) {
       if constexpr (S::kBf16) {
         // keys (2s + e/4) * 8 + hh * 4 + e % 4 of the tile: accumulator
         // registers (s % 2) * 8 .. + 7 of S^T M-tile s / 2.
-        const int t = s / 2;
-        const int r0 = (s % 2) * 8;
-        bop.x = pack_bf16x2(sacc[t][r0 + 0], sacc[t][r0 + 1]);
-        bop.y = pack_bf16x2(sacc[t][r0 + 2], sacc[t][r0 + 3]);
-        bop.z = pack_bf16x2(sacc[t][r0 + 4], sacc[t][r0 + 5]);
-        bop.w = pack_bf16x2(sacc[t][r0 + 6], sacc[t][r0 + 7]);
+        bop = pb[s];
       } else {
         // step s covers keys (r/4) * 8 + hh * 4 + r % 4 (+ 32 for M-tile 1)
         // with r = s % 16: one probability per lane.
@@ -565,7 +639,7 @@ prefill_kernel(PrefillParams p) {
 
   // ---- normalise and write: lane (j, hh) holds dims (r/4)*8 + hh*4 + r%4
   // of each 32-dim tile for its row.
-  const float total = run_sum + __shfl_xor(run_sum, 32, kWave);
+  const float total = run_sum + swap_halves(run_sum);
   if (!row_ok) return;
   const float inv = total > 0.f ? 1.f / total : 0.f;
   T* orow = reinterpret_cast<T*>(p.out) +
