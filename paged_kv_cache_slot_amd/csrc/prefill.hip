@@ -120,6 +120,8 @@ struct PrefillShape {
   static_assert(kTile % (1024 * kWaves) == 0, "tile DMA split");
   static_assert(kLds <= 160 * 1024, "LDS per CU");
   static_assert(kStages * kLoadsPerTile <= 63, "vmcnt range");
+  static_assert(kBlock % (kDmaPerWave * kRowsPerDma) == 0,
+                "a wave's DMA rows of a tile lie in one cache block");
   static_assert(kBlock % kRowsPerDma == 0, "a DMA load stays in one block");
 };
 
@@ -204,14 +206,17 @@ __device__ __forceinline__ int v_swz(int row) {
 // the next LDS read of any buffer -- which would make the prefetch of later
 // tiles wait for the current one.  The caller orders the loads against LDS
 // reads with explicit vmcnt waits and barriers.
-__device__ __forceinline__ void dma16(const void* src, char* lds) {
+// The source is base + off: base uniform (an SGPR pair), off this lane's
+// 32-bit byte offset.
+__device__ __forceinline__ void dma16(const char* base, uint32_t off, char* lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const unsigned m0 = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds)));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(m0) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(base), "s"(m0) : "memory", "m0");
 #else
-  (void)src;
+  (void)base;
+  (void)off;
   (void)lds;
 #endif
 }
@@ -406,20 +411,27 @@ prefill_kernel(PrefillParams p) {
     dma_v_off[q] = static_cast<uint32_t>(row_base + (pos ^ v_swz<S::kChunks>(r)) * 16);
   }
   // Every lane issues exactly kLoadsPerTile loads per tile, so that the
-  // waits below count tiles.  Rows of blocks past the context, or with an
-  // id outside the pool, are read from block 0 instead: they are past Lk
-  // (masked by select in S, zeroed in V) or the block table is invalid.
-  auto dma_tile = [&](int kt, char* kbuf, char* vbuf) __attribute__((always_inline)) {
+  // waits below count tiles.  A wave's rows of a tile lie in one cache
+  // block, whose id (a scalar load) is fetched one tile ahead of its use.
+  // Rows of blocks past the context, or with an id outside the pool, are
+  // read from block 0 instead: they are past Lk (masked by select in S,
+  // zeroed in V) or the block table is invalid.
+  // (Only called with ntiles >= 1, so the context owns a block; the load
+  // is unconditional, from a clamped index, so that nothing waits for it
+  // before its use one iteration later.)
+  const int wave_blk = wave * S::kDmaPerWave * S::kRowsPerDma / kBlock;
+  auto block_id = [&](int kt) __attribute__((always_inline)) {
+    return load_uniform_i32(btab, min(kt * (kBN / kBlock) + wave_blk, nblk_ctx - 1));
+  };
+  auto dma_tile = [&](int kt, int blk, char* kbuf, char* vbuf) __attribute__((always_inline)) {
+    const bool in_ctx = kt * (kBN / kBlock) + wave_blk < nblk_ctx;   // uniform
+    blk = in_ctx && blk >= 0 && blk < p.num_blocks ? blk : 0;
+    const int64_t base = static_cast<int64_t>(blk) * blk_bytes;
 #pragma unroll
     for (int q = 0; q < S::kDmaPerWave; ++q) {
       const int ii = wave * S::kDmaPerWave + q;
-      const int r0 = ii * S::kRowsPerDma;
-      const int bi = kt * (kBN / kBlock) + r0 / kBlock;    // uniform
-      int blk = bi < nblk_ctx ? load_uniform_i32(btab, bi) : 0;
-      blk = blk >= 0 && blk < p.num_blocks ? blk : 0;
-      const int64_t base = static_cast<int64_t>(blk) * blk_bytes;
-      dma16(p.k_cache + base + dma_k_off[q], kbuf + ii * 1024);
-      dma16(p.v_cache + base + dma_v_off[q], vbuf + ii * 1024);
+      dma16(p.k_cache + base, dma_k_off[q], kbuf + ii * 1024);
+      dma16(p.v_cache + base, dma_v_off[q], vbuf + ii * 1024);
     }
   };
 
@@ -623,7 +635,8 @@ prefill_kernel(PrefillParams p) {
   };
 #pragma unroll
   for (int st = 0; st < S::kStages - 1; ++st)
-    if (st < ntiles) dma_tile(st, kbuf(st), vbuf(st));
+    if (st < ntiles) dma_tile(st, block_id(st), kbuf(st), vbuf(st));
+  int next_blk = ntiles > 0 ? block_id(S::kStages - 1) : 0;
   for (int kt = 0; kt < ntiles; ++kt) {
     const int ahead = min(S::kStages - 2, ntiles - 1 - kt);   // tiles after kt in flight
     if (S::kStages >= 3 && ahead >= 1)
@@ -632,7 +645,10 @@ prefill_kernel(PrefillParams p) {
       wait_vm<0>();
     lds_barrier();
     const int nt = kt + S::kStages - 1;
-    if (nt < ntiles) dma_tile(nt, kbuf(nt % S::kStages), vbuf(nt % S::kStages));
+    if (nt < ntiles) {
+      dma_tile(nt, next_blk, kbuf(nt % S::kStages), vbuf(nt % S::kStages));
+      next_blk = block_id(nt + 1);
+    }
     const int st = kt % S::kStages;
     compute(kt, kbuf(st), vbuf(st));
   }
