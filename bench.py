@@ -35,6 +35,7 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 WORKLOAD = "decode8b"
 MIXED = "mixed"
+PREFIX = "prefix"
 
 
 def parse():
@@ -51,7 +52,40 @@ def parse():
     ap.add_argument("--mixed-steps", type=int, default=20,
                     help="timed steps of the mixed chunked-prefill + decode "
                          "workload (0 skips it)")
+    ap.add_argument("--prefix-steps", type=int, default=20,
+                    help="timed steps of the prefix-sharing decode workload "
+                         "(0 skips it)")
+    ap.add_argument("--flush-mb", type=int, default=512,
+                    help="MiB read between timed steps (outside the timed "
+                         "events) so that no step reads the previous step's "
+                         "data from L2 / MALL; 0 disables")
     return ap.parse_args()
+
+
+class Flusher:
+    """Reads a scratch buffer between timed steps (outside their events), so
+    that L2 and MALL hold none of the previous step's data.  A read leaves
+    no dirty lines whose write-back would land in the next step."""
+
+    def __init__(self, mb, dev):
+        import torch
+        self.buf = torch.ones((mb << 20) // 4, dtype=torch.float32,
+                              device=dev) if mb > 0 else None
+        self.sink = []
+
+    def __call__(self):
+        if self.buf is not None:
+            self.sink = [self.buf.sum()]
+
+
+def stats_ms(ms):
+    """median, p10, p90 and mean of per-step times (ms)."""
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4),
+            "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4),
+            "mean": round(float(a.mean()), 4)}
 
 
 # HBM traffic per launch measured with rocprofv3 --pmc (FETCH_SIZE and
@@ -107,7 +141,7 @@ def prefill_flops(lq, lk, hq, d):
     return 4 * d * hq * pairs
 
 
-def run_mixed(steps, warmup, dev):
+def run_mixed(steps, warmup, dev, flush):
     """Mixed step: one pa_store_kv of every new row (8 x 512 chunk rows + 192
     decode rows), then pa_prefill_varlen of the chunks, then pa_decode of the
     decode rows, on one stream.  Returns a dict for the JSON line."""
@@ -169,12 +203,15 @@ def run_mixed(steps, warmup, dev):
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
            for _ in range(steps)]
     for i in range(steps):
+        flush()
         step(evs[i])
     torch.cuda.synchronize()
-    st = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
-    pf = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
-    dc = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
-    total = sum(e[0].elapsed_time(e[3]) for e in evs) / steps
+    import numpy as np
+    st = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    pf_all = [e[1].elapsed_time(e[2]) for e in evs]
+    pf = float(np.median(pf_all))
+    dc = float(np.median([e[2].elapsed_time(e[3]) for e in evs]))
+    total = float(np.median([e[0].elapsed_time(e[3]) for e in evs]))
     flops = prefill_flops(pre.chunk, pre.history + pre.chunk, hq, d)
     dbytes = decode_bytes(dec.lens, hq, hkv, d, 2)
     row = 2 * hkv * d * 2
@@ -187,6 +224,7 @@ def run_mixed(steps, warmup, dev):
         "store_us": round(st * 1e3, 2),
         "store_gbs": round(sbytes / (st * 1e-3) / 1e9, 1),
         "prefill_us": round(pf * 1e3, 2),
+        "prefill_ms_stats": stats_ms(pf_all),
         "prefill_gflop": round(flops / 1e9, 2),
         "decode_us": round(dc * 1e3, 2),
         "decode_tbs": round(dbytes / (dc * 1e-3) / 1e12, 4),
@@ -198,6 +236,72 @@ def run_mixed(steps, warmup, dev):
                      "traffic": committed_traffic(
                          "prefill_mixed_hbm_counters.md", PREFILL_SOURCES),
                      "algorithmic_flops": flops},
+    }
+
+
+def run_prefix(steps, warmup, dev, flush):
+    """Prefix-sharing decode step: pa_store_kv of each sequence's new token
+    (private suffix blocks), then pa_decode; 128 sequences share their first
+    128 blocks.  Reports unique-byte (each physical block once) and
+    logical-byte (per sequence) rates."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from paged_kv_cache_slot_amd import metadata as pm
+    from paged_kv_cache_slot_amd import ops
+
+    cfg = wl.get_config(PREFIX)
+    lay = wl.config_decode_layout(cfg)
+    hq, hkv, d, bs = cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, 16
+    b = len(lay.lens)
+    kc, vc = wl.fill_pool(lay.num_blocks, bs, hkv, d, "bf16", cfg.seed, dev)
+    q = wl.make_values((b, hq, d), "bf16", cfg.seed + 1, dev)
+    k_new = wl.make_values((b, hkv, d), "bf16", cfg.seed + 2, dev)
+    v_new = wl.make_values((b, hkv, d), "bf16", cfg.seed + 3, dev)
+    meta = pm.decode_inputs(lay.tables, lay.lens, bs)
+    slot = torch.as_tensor(meta["slot_mapping"], device=dev)
+    bt = torch.as_tensor(meta["block_tables"], device=dev)
+    cl = torch.as_tensor(meta["context_lens"], device=dev)
+    scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q)
+    ws = torch.empty(max(ops.decode_workspace_bytes(
+        b, hq, hkv, d, meta["max_context_len"]), 1), dtype=torch.uint8,
+        device=dev)
+
+    def step(ev):
+        ev[0].record()
+        ops.store_kv(k_new, v_new, kc, vc, slot)
+        ev[1].record()
+        ops.decode(q, kc, vc, bt, cl, meta["max_context_len"], scale=scale,
+                   out=out, workspace=ws)
+        ev[2].record()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+           for _ in range(steps + warmup)]
+    for i in range(warmup):
+        step(evs[steps + i])
+    torch.cuda.synchronize()
+    for i in range(steps):
+        flush()
+        step(evs[i])
+    torch.cuda.synchronize()
+    dec = float(np.median([e[1].elapsed_time(e[2]) for e in evs[:steps]]))
+    row = 2 * hkv * d * 2
+    logical = decode_bytes(lay.lens, hq, hkv, d, 2)
+    pre_tok = cfg.shared_prefix_blocks * bs
+    uniq_tok = pre_tok + int(sum(int(n) - pre_tok for n in lay.lens))
+    unique = logical - (int(sum(int(n) for n in lay.lens)) - uniq_tok) * row
+    return {
+        "workload": cfg.title,
+        "steps": steps,
+        "decode_us": round(dec * 1e3, 2),
+        "unique_bytes": unique,
+        "logical_bytes": logical,
+        "unique_tbs": round(unique / (dec * 1e-3) / 1e12, 4),
+        "logical_tbs": round(logical / (dec * 1e-3) / 1e12, 4),
+        "decode_tokens_per_s": round(b / (dec * 1e-3), 1),
+        "kernel": "pa_decode (every sequence reads its whole context)",
     }
 
 
@@ -264,13 +368,15 @@ def main():
     torch.cuda.synchronize()
 
     def step(ev=None):
-        ops.store_kv(k_new, v_new, kc, vc, slot)
         if ev is not None:
             ev[0].record()
+        ops.store_kv(k_new, v_new, kc, vc, slot)
+        if ev is not None:
+            ev[1].record()
         ops.decode(q, kc, vc, bt, cl, maxlen, scale=scale, out=out,
                    workspace=ws)
         if ev is not None:
-            ev[1].record()
+            ev[2].record()
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -279,24 +385,27 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    flush = Flusher(args.flush_mb, dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True),
-               torch.cuda.Event(enable_timing=True))
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
               for _ in range(args.steps)]
+    # Timed region: exactly `steps` steps between two synchronisations; each
+    # step's own events exclude the cache flush written before it.
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    start.record()
     for i in range(args.steps):
+        flush()
         step(events[i])
-    stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = start.elapsed_time(stop) / args.steps
-    dec_ms = [e[0].elapsed_time(e[1]) for e in events]
-    dec_ms_avg = sum(dec_ms) / len(dec_ms)
+    step_all = [e[0].elapsed_time(e[2]) for e in events]
+    dec_all = [e[1].elapsed_time(e[2]) for e in events]
+    step_stats = stats_ms(step_all)
+    dec_stats = stats_ms(dec_all)
+    step_ms = step_stats["median"]
+    dec_ms_avg = dec_stats["median"]
 
     dbytes = decode_bytes(lay.lens, hq, hkv, d, elem)
     row = 2 * hkv * d * elem
@@ -308,25 +417,27 @@ def main():
     traffic = committed_traffic("decode_8b_step_hbm_counters.md",
                                 DECODE_SOURCES)
 
+    # The other workloads get their own pools: free the 8B-shaped one first
+    # (the mixed pool is ~3.5 GB), keeping host copies for the CPU baseline.
+    keep_cpu = not args.no_cpu_baseline
+    h_kc = wl.host_bits(kc) if keep_cpu else None
+    h_vc = wl.host_bits(vc) if keep_cpu else None
+    h_q = wl.host_bits(q) if keep_cpu else None
+    del kc, vc, ws
+    torch.cuda.empty_cache()
     mixed = None
     if args.mixed_steps > 0:
-        # free the 8B-shaped pool first; the mixed pool is ~3.5 GB
-        keep_cpu = not args.no_cpu_baseline
-        h_kc = wl.host_bits(kc) if keep_cpu else None
-        h_vc = wl.host_bits(vc) if keep_cpu else None
-        h_q = wl.host_bits(q) if keep_cpu else None
-        del kc, vc, ws
+        mixed = run_mixed(args.mixed_steps, max(2, args.warmup // 2), dev,
+                          flush)
         torch.cuda.empty_cache()
-        mixed = run_mixed(args.mixed_steps, max(2, args.warmup // 2), dev)
-    else:
-        h_kc = h_vc = h_q = None
+    prefix = None
+    if args.prefix_steps > 0:
+        prefix = run_prefix(args.prefix_steps, max(2, args.warmup // 2), dev,
+                            flush)
 
     cpu = None
     if not args.no_cpu_baseline:
         # bounded oracle sample over host copies of the same pool
-        if h_kc is None:
-            h_kc, h_vc, h_q = wl.host_bits(kc), wl.host_bits(vc), \
-                wl.host_bits(q)
         done, toks, dt = cpu_baseline(lay.tables, lay.lens, h_q, h_kc, h_vc,
                                       hq, scale, args.cpu_seconds)
         cpu_bytes = toks * row
@@ -358,6 +469,9 @@ def main():
         "tokens_per_s": round(b / (step_ms * 1e-3), 1),
         "frac_of_hbm_peak": round(value_tbs * 1e3 / HBM_PEAK_GBS, 4),
         "decode_ms": round(dec_ms_avg, 4),
+        "step_ms_stats": step_stats,
+        "decode_ms_stats": dec_stats,
+        "flush_mb_between_steps": args.flush_mb,
         "roofline": {"kernel": "pa_decode (decode_partition_kernel + "
                                "decode_merge_kernel)",
                      "bound": "hbm", "achieved": round(dec_gbs, 1),
@@ -367,6 +481,7 @@ def main():
                      "algorithmic_bytes": dbytes},
         "cpu_baseline": cpu,
         "mixed_step": mixed,
+        "prefix_step": prefix,
         "wall_s_timed": round(wall, 3),
     }
     print(json.dumps(line), flush=True)
