@@ -5,6 +5,8 @@
  *
  *   pa_store_kv        scatter new K/V rows into their physical slots
  *   pa_copy_blocks     copy whole blocks (the data side of copy-on-write)
+ *   pa_decode_shared_prefix  decode where groups of sequences share leading
+ *                      blocks: the shared keys are read once per group
  *   pa_decode          one query row per sequence against its paged context
  *   pa_prefill_varlen  packed variable-length (chunked) prefill, causal,
  *                      history read through block tables
@@ -227,6 +229,59 @@ pa_status pa_prefill_varlen(void* out, const void* q, int64_t total_q,
                             int32_t head_dim, float scale, int32_t causal,
                             void* workspace, size_t workspace_bytes,
                             pa_dtype dtype, void* stream);
+
+/* Bytes of workspace pa_decode_shared_prefix needs for these sizes (> 0
+ * whenever num_seqs > 0): partial results, one slot per suffix partition and
+ * per prefix chunk, for each (sequence, query head). */
+size_t pa_decode_shared_prefix_workspace_bytes(
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t max_suffix_len, int32_t max_prefix_len,
+    int32_t num_groups, int32_t max_group_size);
+
+/*
+ * pa_decode_shared_prefix -- decode attention, same result as pa_decode, for
+ * batches where groups of sequences share their leading cache blocks.
+ *
+ * Sharing: sequences that start with the same tokens hold the same physical
+ * blocks for them, stored once ("Warmup Guide -- Inference Serving
+ * Internals", Chapter 4, prefix sharing by reference counts).  pa_decode
+ * reads those blocks once per sequence; this call reads them once per group:
+ * the attention of all members' query rows over the shared keys runs as one
+ * MFMA pass (in chunks of keys, each giving a partial result: unnormalised
+ * output, reference max, sum), every sequence's own keys run as decode
+ * partitions, and a merge combines the partials of each (sequence, head).
+ * out[b] = softmax(scale * q[b] K_b^T) V_b over all context_lens[b] tokens,
+ * exactly as pa_decode defines it; only the order of summation differs.
+ *
+ *   out, q          device, [num_seqs, num_heads, head_dim]
+ *   block_tables,
+ *   context_lens    as pa_decode
+ *   prefix_lens     device int32 [num_seqs]: tokens of sequence b shared with
+ *                   the other members of its group (rounded down to a
+ *                   multiple of block_size); 0 for a sequence in no group
+ *   max_suffix_len  host bound of context_lens[b] - prefix_lens[b]
+ *   max_prefix_len  host bound of prefix_lens[b]
+ *   groups          device int32 [num_groups, 2]: first sequence and member
+ *                   count; members are consecutive sequences
+ *   max_group_size  host bound of the member counts
+ *   workspace       device, >= pa_decode_shared_prefix_workspace_bytes(...)
+ *
+ * Preconditions (device data, not checked): the members of a group have
+ * equal prefix_lens and identical block ids for their first prefix_lens /
+ * block_size blocks; prefix_lens[b] <= context_lens[b]; a sequence with
+ * prefix_lens[b] > 0 belongs to exactly one group; the bounds above hold.
+ * Errors and supported shapes: as pa_decode; the workspace is always
+ * required.  The caller owns every buffer; nothing is kept past the call.
+ */
+pa_status pa_decode_shared_prefix(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    int64_t num_blocks, int32_t block_size, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* prefix_lens, int32_t max_suffix_len,
+    int32_t max_prefix_len, const int32_t* groups, int32_t num_groups,
+    int32_t max_group_size, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, float scale, void* workspace,
+    size_t workspace_bytes, pa_dtype dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -150,6 +150,54 @@ def decode_metadata(seqs, block_size):
     }
 
 
+def shared_prefix_groups(seqs, block_size):
+    """Groups of consecutive decode sequences that share leading blocks.
+
+    Warmup Guide, Chapter 4 (prefix sharing): sequences that start with the
+    same tokens hold the same physical blocks for them (reference-counted,
+    stored once); only full blocks are shared -- a write into a shared block
+    copies it first.  This reading groups a batch for a decode that reads
+    each shared block once per group:
+
+    * a sequence's full blocks are its first length // block_size blocks;
+    * two sequences share the leading full blocks whose ids are equal
+      position by position, up to the first difference;
+    * scanning the batch in order, a sequence that shares k >= 1 blocks with
+      the next one starts a group with prefix k; the group takes every
+      following consecutive sequence that shares at least those k blocks
+      with the group's first sequence; every member's shared length is
+      k * block_size tokens.  Sequences in no group have shared length 0.
+
+    Returns (prefix_lens list [B], groups list of (first, count)).
+    """
+    def full_blocks(seq):
+        return seq["length"] // block_size
+
+    def shared(a, b):
+        n = min(full_blocks(a), full_blocks(b))
+        k = 0
+        while k < n and a["block_table"][k] == b["block_table"][k]:
+            k += 1
+        return k
+
+    prefix_lens = [0] * len(seqs)
+    groups = []
+    i = 0
+    while i < len(seqs):
+        k = shared(seqs[i], seqs[i + 1]) if i + 1 < len(seqs) else 0
+        if k == 0:
+            i += 1
+            continue
+        last = i + 1
+        while last + 1 < len(seqs) and shared(seqs[i], seqs[last + 1]) >= k:
+            last += 1
+        for b in range(i, last + 1):
+            prefix_lens[b] = k * block_size
+        groups.append((i, last - i + 1))
+        i = last + 1
+    return prefix_lens, groups
+
+
 def pad_decode_batch(meta, bucket):
     """Pad a decode batch to a captured-graph bucket size.
 

@@ -48,6 +48,13 @@ SIGNATURES = {
         _c_void_p, _c_void_p, _i32, _i32, _c_void_p, _i32, _i32, _i32,
         _i32, _i32, _f32, _i32, _c_void_p, _size, ctypes.c_int,
         _c_void_p]),
+    "pa_decode_shared_prefix_workspace_bytes": (_size, [
+        _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_shared_prefix": (ctypes.c_int, [
+        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32,
+        _c_void_p, _i32, _c_void_p, _c_void_p, _i32, _i32, _c_void_p, _i32,
+        _i32, _i32, _i32, _i32, _i32, _f32, _c_void_p, _size, ctypes.c_int,
+        _c_void_p]),
 }
 
 _lib = None

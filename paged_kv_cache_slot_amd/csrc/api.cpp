@@ -223,4 +223,95 @@ pa_status pa_prefill_varlen(void* out, const void* q, int64_t total_q,
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+size_t pa_decode_shared_prefix_workspace_bytes(
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t max_suffix_len, int32_t max_prefix_len,
+    int32_t num_groups, int32_t max_group_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_suffix_len < 0 || max_prefix_len < 0 || num_groups < 0 ||
+      max_group_size < 0 || num_heads % num_kv_heads != 0)
+    return 0;
+  return pa::plan_shared_prefix(num_seqs, num_heads, num_kv_heads, head_dim,
+                                max_suffix_len, max_prefix_len, num_groups,
+                                max_group_size)
+      .workspace_bytes;
+}
+
+pa_status pa_decode_shared_prefix(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    int64_t num_blocks, int32_t block_size, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* prefix_lens, int32_t max_suffix_len,
+    int32_t max_prefix_len, const int32_t* groups, int32_t num_groups,
+    int32_t max_group_size, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, float scale, void* workspace,
+    size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  pa_status st = check_attention(block_size, num_seqs, num_heads, num_kv_heads,
+                                 head_dim, max_blocks_per_seq, num_blocks,
+                                 dtype);
+  if (st != PA_OK) return st;
+  if (max_suffix_len < 0 || max_prefix_len < 0 || num_groups < 0 ||
+      max_group_size < 0)
+    return PA_ERR_SHAPE;
+  const int64_t max_len = static_cast<int64_t>(max_suffix_len) + max_prefix_len;
+  if (max_len > 0x7fffffff) return PA_ERR_SHAPE;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !context_lens || !prefix_lens) return PA_ERR_NULL;
+  if (max_len > 0 && (!k_cache || !v_cache || !block_tables))
+    return PA_ERR_NULL;
+  if (num_groups > 0 && !groups) return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return PA_ERR_UNSUPPORTED;
+  const pa::SharedPrefixPlan plan = pa::plan_shared_prefix(
+      num_seqs, num_heads, num_kv_heads, head_dim, max_suffix_len,
+      max_prefix_len, num_groups, max_group_size);
+  if (!workspace || workspace_bytes < plan.workspace_bytes)
+    return PA_ERR_WORKSPACE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  pa::PrefixArgs pre{};
+  pre.q = q;
+  pre.k_cache = k_cache;
+  pre.v_cache = v_cache;
+  pre.num_blocks = num_blocks;
+  pre.block_tables = block_tables;
+  pre.max_blocks_per_seq = max_blocks_per_seq;
+  pre.prefix_lens = prefix_lens;
+  pre.groups = groups;
+  pre.num_groups = num_groups;
+  pre.max_group_size = max_group_size;
+  pre.max_prefix_len = max_prefix_len;
+  pre.num_seqs = num_seqs;
+  pre.num_heads = num_heads;
+  pre.num_kv_heads = num_kv_heads;
+  pre.head_dim = head_dim;
+  pre.scale = scale;
+  pre.workspace = workspace;
+  pre.bf16 = dtype == PA_BF16;
+  hipError_t e = pa::launch_prefix_partials(pre, plan, s);
+  if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
+  if (e != hipSuccess) return PA_ERR_LAUNCH;
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_blocks = num_blocks;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.max_context_len = static_cast<int>(max_len);
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.scale = scale;
+  a.workspace = workspace;
+  a.bf16 = dtype == PA_BF16;
+  a.prefix_lens = prefix_lens;
+  e = pa::launch_decode_suffix(a, plan, s);
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -208,12 +208,30 @@ struct DecodeParams {
   int num_heads;
   int num_kv_heads;
   float scale_log2;  // scale * log2(e): logits live in the base-2 domain
-  float* ws_max;     // [B, Hq, NP]   (multi-partition only)
-  float* ws_sum;     // [B, Hq, NP]
-  float* ws_acc;     // [B, Hq, NP, D]
+  float* ws_max;     // [B, Hq, ws_stride]   (multi-partition only)
+  float* ws_sum;     // [B, Hq, ws_stride]
+  float* ws_acc;     // [B, Hq, ws_stride, D]
   int num_partitions;
   int partition_tokens;  // tokens per partition, a multiple of the chunk
+  int ws_stride;         // partial slots per (sequence, head) >= num_partitions
+  // Shared-prefix (cascade) decode: the partitions cover tokens
+  // [start_b, L_b) with start_b = prefix_lens[b] rounded down to a block;
+  // slots num_partitions .. + ceil(start_b / prefix_chunk_tokens) - 1 hold
+  // the prefix partials, which the merge adds.  Null for plain decode.
+  const int32_t* prefix_lens;
+  int prefix_chunk_tokens;
+  int prefix_chunks;     // prefix slots per (sequence, head)
+  int force_partials;    // write partials even with one partition
 };
+
+// First token of the partitions: 0, or the block-aligned shared prefix.
+__device__ __forceinline__ int suffix_start(const DecodeParams& p, int b,
+                                            int len) {
+  if (p.prefix_lens == nullptr) return 0;
+  int st = p.prefix_lens[b];
+  st = st < 0 ? 0 : (st > len ? len : st);
+  return st - st % kBlock;
+}
 
 __device__ __forceinline__ int clamp_len(const DecodeParams& p, int b) {
   int len = p.context_lens[b];
@@ -270,10 +288,10 @@ decode_partition_kernel(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
-  const bool single = p.num_partitions == 1;
+  const bool single = p.num_partitions == 1 && !p.force_partials;
 
   const int len = clamp_len(p, b);
-  const int t0 = part * p.partition_tokens;
+  const int t0 = suffix_start(p, b, len) + part * p.partition_tokens;
   const int head0 = kvh * G;
   const int row_stride = p.num_kv_heads * S::kRow;   // bytes per slot
   const int64_t blk_bytes = static_cast<int64_t>(kBlock) * row_stride;
@@ -621,7 +639,7 @@ decode_partition_kernel(
       T* out = reinterpret_cast<T*>(p.out) + head * D + d;
       store_out<T>(out, l > 0.f ? o / l : 0.f);
     } else {
-      const int64_t slot = head * p.num_partitions + part;
+      const int64_t slot = head * p.ws_stride + part;
       p.ws_acc[slot * D + d] = o;
       if (d == 0) {
         p.ws_max[slot] = s_mrun[h];
@@ -640,23 +658,35 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
   const int b = blockIdx.y;
   const int d = threadIdx.x;
   const int len = clamp_len(p, b);
-  const int np = (len + partition_tokens - 1) / partition_tokens;
+  const int start = suffix_start(p, b, len);
+  int np = (len - start + partition_tokens - 1) / partition_tokens;
+  np = np > p.num_partitions ? p.num_partitions : np;   // bound violated
+  int npre = 0;                      // prefix partials of this sequence
+  if (start > 0 && p.prefix_chunks > 0) {
+    npre = (start + p.prefix_chunk_tokens - 1) / p.prefix_chunk_tokens;
+    npre = npre > p.prefix_chunks ? p.prefix_chunks : npre;
+  }
   const int64_t head = static_cast<int64_t>(b) * p.num_heads + h;
   T* out = reinterpret_cast<T*>(p.out) + head * D + d;
-  const float* mx = p.ws_max + head * p.num_partitions;
-  const float* sm = p.ws_sum + head * p.num_partitions;
-  const float* ac = p.ws_acc + head * p.num_partitions * D + d;
+  const float* mx = p.ws_max + head * p.ws_stride;
+  const float* sm = p.ws_sum + head * p.ws_stride;
+  const float* ac = p.ws_acc + head * p.ws_stride * D + d;
+  // Slots 0 .. np - 1 (this call's partitions), then num_partitions ..
+  // num_partitions + npre - 1 (the prefix partials).
+  auto slot = [&](int i) { return i < np ? i : p.num_partitions + (i - np); };
+  const int n = np + npre;
   float m = -INFINITY;
-  for (int i = 0; i < np; ++i) m = fmaxf(m, mx[i]);
-  if (np == 0 || m == -INFINITY) {
+  for (int i = 0; i < n; ++i) m = fmaxf(m, mx[slot(i)]);
+  if (n == 0 || m == -INFINITY) {
     store_out<T>(out, 0.f);
     return;
   }
   float l = 0.f, o = 0.f;
-  for (int i = 0; i < np; ++i) {
-    const float w = fast_exp2(mx[i] - m);
-    l = fmaf(w, sm[i], l);
-    o = fmaf(w, ac[static_cast<int64_t>(i) * D], o);
+  for (int i = 0; i < n; ++i) {
+    const int k = slot(i);
+    const float w = fast_exp2(mx[k] - m);
+    l = fmaf(w, sm[k], l);
+    o = fmaf(w, ac[static_cast<int64_t>(k) * D], o);
   }
   store_out<T>(out, l > 0.f ? o / l : 0.f);
 }
@@ -670,7 +700,7 @@ hipError_t launch_typed(const DecodeParams& prm, int num_seqs, int num_kv_heads,
   hipLaunchKernelGGL((decode_partition_kernel<T, D, G, C>), grid,
                      dim3(kThreads), 0, stream, prm);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || prm.num_partitions == 1) return e;
+  if (e != hipSuccess || (prm.num_partitions == 1 && !prm.force_partials)) return e;
   hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(num_heads, num_seqs),
                      dim3(D), 0, stream, prm);
   return hipGetLastError();
@@ -699,8 +729,22 @@ constexpr int kChunkTokens = 512;
 #endif
 constexpr int64_t kTargetWorkgroups = PA_DECODE_TARGET_WGS;
 constexpr int kMaxChunksPerPartition = 16;
+constexpr int64_t kPrefixTargetWorkgroups = 128;
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+hipError_t dispatch_decode(const DecodeParams& prm, const DecodeArgs& a,
+                           hipStream_t stream) {
+  constexpr int P = kChunkTokens;
+  if (a.bf16) {
+    if (a.head_dim == 128)
+      return dispatch_group<bf16_t, 128, P>(prm, a.num_seqs, a.num_kv_heads, a.num_heads, stream);
+    return dispatch_group<bf16_t, 64, P>(prm, a.num_seqs, a.num_kv_heads, a.num_heads, stream);
+  }
+  if (a.head_dim == 128)
+    return dispatch_group<float, 128, P>(prm, a.num_seqs, a.num_kv_heads, a.num_heads, stream);
+  return dispatch_group<float, 64, P>(prm, a.num_seqs, a.num_kv_heads, a.num_heads, stream);
+}
 
 }  // namespace
 
@@ -736,6 +780,39 @@ DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads,
   return plan;
 }
 
+// Shared-prefix plan: the suffix partitions as for plain decode (over the
+// longest suffix), plus prefix partials of prefix_chunk_tokens keys each.
+// The chunk length aims at ~128 prefix workgroups in all (an M-tile of the
+// prefix pass holds 256 rows), and is at least two 64-key tiles.
+SharedPrefixPlan plan_shared_prefix(int num_seqs, int num_heads,
+                                    int num_kv_heads, int head_dim,
+                                    int max_suffix_len, int max_prefix_len,
+                                    int num_groups, int max_group_size) {
+  SharedPrefixPlan plan{};
+  plan.suffix = plan_decode(num_seqs, num_heads, num_kv_heads, head_dim,
+                            max_suffix_len);
+  const int g = num_heads / num_kv_heads;
+  const int64_t mtiles = (static_cast<int64_t>(max_group_size) * g + 255) / 256;
+  const int64_t per_chunk = static_cast<int64_t>(num_groups) * mtiles * num_kv_heads;
+  int64_t want = per_chunk > 0 ? (kPrefixTargetWorkgroups + per_chunk - 1) / per_chunk : 1;
+  want = want < 1 ? 1 : want;
+  int64_t ct = (max_prefix_len + want - 1) / want;
+  ct = (ct + 63) / 64 * 64;
+  ct = ct < 128 ? 128 : ct;
+  plan.prefix_chunk_tokens = static_cast<int>(ct);
+  plan.prefix_chunks = max_prefix_len > 0
+                           ? static_cast<int>((max_prefix_len + ct - 1) / ct)
+                           : 0;
+  plan.total_slots = plan.suffix.num_partitions + plan.prefix_chunks;
+  const size_t slots = static_cast<size_t>(num_seqs) * num_heads * plan.total_slots;
+  plan.off_max = 0;
+  plan.off_sum = align256(slots * sizeof(float));
+  plan.off_acc = plan.off_sum + align256(slots * sizeof(float));
+  plan.workspace_bytes =
+      plan.off_acc + align256(slots * static_cast<size_t>(head_dim) * sizeof(float));
+  return plan;
+}
+
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan,
                          hipStream_t stream) {
   DecodeParams prm{};
@@ -754,21 +831,44 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan,
   prm.scale_log2 = a.scale * kLog2e;
   prm.num_partitions = plan.num_partitions;
   prm.partition_tokens = plan.partition_tokens;
+  prm.ws_stride = plan.num_partitions;
   if (plan.num_partitions > 1) {
     char* ws = static_cast<char*>(a.workspace);
     prm.ws_max = reinterpret_cast<float*>(ws + plan.off_max);
     prm.ws_sum = reinterpret_cast<float*>(ws + plan.off_sum);
     prm.ws_acc = reinterpret_cast<float*>(ws + plan.off_acc);
   }
-  constexpr int P = kChunkTokens;
-  if (a.bf16) {
-    if (a.head_dim == 128)
-      return dispatch_group<bf16_t, 128, P>(prm, a.num_seqs, a.num_kv_heads, a.num_heads, stream);
-    return dispatch_group<bf16_t, 64, P>(prm, a.num_seqs, a.num_kv_heads, a.num_heads, stream);
-  }
-  if (a.head_dim == 128)
-    return dispatch_group<float, 128, P>(prm, a.num_seqs, a.num_kv_heads, a.num_heads, stream);
-  return dispatch_group<float, 64, P>(prm, a.num_seqs, a.num_kv_heads, a.num_heads, stream);
+  return dispatch_decode(prm, a, stream);
+}
+
+hipError_t launch_decode_suffix(const DecodeArgs& a, const SharedPrefixPlan& plan,
+                                hipStream_t stream) {
+  DecodeParams prm{};
+  prm.out = a.out;
+  prm.q = a.q;
+  prm.k_cache = static_cast<const char*>(a.k_cache);
+  prm.v_cache = static_cast<const char*>(a.v_cache);
+  prm.num_blocks = a.num_blocks;
+  prm.block_tables = a.block_tables;
+  prm.max_blocks_per_seq = a.max_blocks_per_seq;
+  prm.context_lens = a.context_lens;
+  prm.max_context_len = a.max_context_len;
+  prm.num_seqs = a.num_seqs;
+  prm.num_heads = a.num_heads;
+  prm.num_kv_heads = a.num_kv_heads;
+  prm.scale_log2 = a.scale * kLog2e;
+  prm.num_partitions = plan.suffix.num_partitions;
+  prm.partition_tokens = plan.suffix.partition_tokens;
+  prm.ws_stride = plan.total_slots;
+  prm.prefix_lens = a.prefix_lens;
+  prm.prefix_chunk_tokens = plan.prefix_chunk_tokens;
+  prm.prefix_chunks = plan.prefix_chunks;
+  prm.force_partials = 1;
+  char* ws = static_cast<char*>(a.workspace);
+  prm.ws_max = reinterpret_cast<float*>(ws + plan.off_max);
+  prm.ws_sum = reinterpret_cast<float*>(ws + plan.off_sum);
+  prm.ws_acc = reinterpret_cast<float*>(ws + plan.off_acc);
+  return dispatch_decode(prm, a, stream);
 }
 
 }  // namespace pa

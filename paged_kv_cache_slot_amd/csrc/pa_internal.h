@@ -48,10 +48,61 @@ struct DecodeArgs {
   float scale;
   void* workspace;
   bool bf16;
+  const int32_t* prefix_lens = nullptr;   // shared-prefix decode only
 };
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan,
                          hipStream_t stream);
+
+// ---- shared-prefix (cascade) decode ------------------------------------
+struct SharedPrefixPlan {
+  DecodePlan suffix;         // partitions over [prefix, L_b) (workspace unused)
+  int prefix_chunk_tokens;   // keys per prefix partial, multiple of 64
+  int prefix_chunks;         // prefix partial slots per (sequence, head)
+  int total_slots;           // suffix.num_partitions + prefix_chunks
+  size_t workspace_bytes;
+  size_t off_max, off_sum, off_acc;  // [B, Hq, total_slots] (acc: x D)
+};
+
+SharedPrefixPlan plan_shared_prefix(int num_seqs, int num_heads,
+                                    int num_kv_heads, int head_dim,
+                                    int max_suffix_len, int max_prefix_len,
+                                    int num_groups, int max_group_size);
+
+// Suffix pass + merge of a shared-prefix decode: a.prefix_lens set,
+// a.max_context_len the bound of L_b.  Writes the suffix partials and then
+// merges them with the prefix partials already in the workspace.
+hipError_t launch_decode_suffix(const DecodeArgs& a,
+                                const SharedPrefixPlan& plan,
+                                hipStream_t stream);
+
+// Prefix pass: for each group, the attention of every member's query rows
+// over the group's shared prefix keys, in chunks, as partials (unnormalised
+// output, reference max, sum) in slots suffix.num_partitions + chunk.
+struct PrefixArgs {
+  const void* q;             // [num_seqs, Hq, D]
+  const void* k_cache;
+  const void* v_cache;
+  int64_t num_blocks;
+  const int32_t* block_tables;
+  int max_blocks_per_seq;
+  const int32_t* prefix_lens;   // [num_seqs]
+  const int32_t* groups;        // [num_groups, 2]: first sequence, count
+  int num_groups;
+  int max_group_size;
+  int max_prefix_len;
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int head_dim;
+  float scale;
+  void* workspace;
+  bool bf16;
+};
+
+hipError_t launch_prefix_partials(const PrefixArgs& a,
+                                  const SharedPrefixPlan& plan,
+                                  hipStream_t stream);
 
 // ---- prefill -----------------------------------------------------------
 struct PrefillArgs {

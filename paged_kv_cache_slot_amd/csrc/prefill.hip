@@ -145,6 +145,22 @@ struct PrefillParams {
   int num_kv_heads;
   float scale_log2;
   int causal;
+  // Shared-prefix partials (group mode): item b = group * chunks + chunk;
+  // the group's members are query rows groups[2g] .. + groups[2g + 1] - 1,
+  // its keys the first prefix_lens[groups[2g]] tokens (rounded down to a
+  // block) of that first member's table, non-causal, tiles chunk *
+  // chunk_tiles .. + chunk_tiles - 1.  Output: partials in the decode
+  // workspace layout, slot slot0 + chunk of each (row, head).
+  int group_mode;
+  const int32_t* groups;
+  const int32_t* prefix_lens;
+  int chunk_tiles;
+  int chunks;
+  float* ws_max;
+  float* ws_sum;
+  float* ws_acc;
+  int ws_stride;
+  int slot0;
 };
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -339,9 +355,30 @@ prefill_kernel(PrefillParams p) {
   const int j = lane % 32;                   // this lane's row inside the wave
   const int hh = lane / 32;                  // lane half
 
-  const SeqExtent ext = seq_extent(p.cu_q, p.cu_k, b, p.max_seqlen_q,
-                                   p.max_seqlen_k, p.total_q,
-                                   p.max_blocks_per_seq);
+  SeqExtent ext;
+  int kt0 = 0;              // first key tile of this workgroup
+  int chunk = 0;            // group mode: which prefix partial
+  int table_row = b;        // block-table row of the keys
+  if (p.group_mode) {
+    const int g = b / p.chunks;
+    chunk = b % p.chunks;
+    int first = p.groups[2 * g];
+    int cnt = p.groups[2 * g + 1];
+    first = first < 0 ? 0 : first;
+    cnt = cnt < 0 ? 0 : (cnt > p.max_seqlen_q ? p.max_seqlen_q : cnt);
+    if (first >= p.total_q) cnt = 0;
+    else if (first + cnt > p.total_q) cnt = static_cast<int>(p.total_q - first);
+    int pl = cnt > 0 ? p.prefix_lens[first] : 0;
+    pl = pl < 0 ? 0 : (pl > p.max_seqlen_k ? p.max_seqlen_k : pl);
+    if (pl > p.max_blocks_per_seq * kBlock) pl = p.max_blocks_per_seq * kBlock;
+    pl -= pl % kBlock;
+    ext = {first, cnt, pl};
+    kt0 = chunk * p.chunk_tiles;
+    table_row = first;
+  } else {
+    ext = seq_extent(p.cu_q, p.cu_k, b, p.max_seqlen_q, p.max_seqlen_k,
+                     p.total_q, p.max_blocks_per_seq);
+  }
   const int q0 = ext.q0;
   const int lq = ext.lq;
   const int lk = ext.lk;
@@ -349,8 +386,12 @@ prefill_kernel(PrefillParams p) {
   const int m0 = mtile * S::kBM;
   if (m0 >= mrows) return;                   // uniform over the workgroup
 
-  // Key range this workgroup needs.
-  const int ntiles = (tile_key_end(ext, G, m0, S::kBM, p.causal) + kBN - 1) / kBN;
+  // Key tiles this workgroup reads: kt0 .. kt0 + ntiles - 1.
+  int ntiles = (tile_key_end(ext, G, m0, S::kBM, p.causal) + kBN - 1) / kBN;
+  if (p.group_mode) {
+    ntiles = min(ntiles - kt0, p.chunk_tiles);
+    if (ntiles <= 0) return;   // past this group's prefix: never merged
+  }
 
   // This lane's row: M row m -> query position i, head h.
   const int m = m0 + wave * 32 + j;
@@ -393,7 +434,7 @@ prefill_kernel(PrefillParams p) {
   const int64_t row_stride = static_cast<int64_t>(p.num_kv_heads) * S::kRow;
   const int64_t blk_bytes = row_stride * kBlock;
   const int32_t* btab = p.block_tables +
-                        static_cast<int64_t>(b) * p.max_blocks_per_seq;
+                        static_cast<int64_t>(table_row) * p.max_blocks_per_seq;
   const int nblk_ctx = (lk + kBlock - 1) / kBlock;   // blocks the context owns
 
   // DMA load q of this wave moves tile rows r0 .. r0 + kRowsPerDma - 1 (one
@@ -633,30 +674,50 @@ prefill_kernel(PrefillParams p) {
   auto vbuf = [&](int st) __attribute__((always_inline)) {
     return smem + (S::kStages + st) * S::kTile;
   };
+  // Local tile i is key tile kt0 + i and lives in stage i % kStages.
 #pragma unroll
   for (int st = 0; st < S::kStages - 1; ++st)
-    if (st < ntiles) dma_tile(st, block_id(st), kbuf(st), vbuf(st));
-  int next_blk = ntiles > 0 ? block_id(S::kStages - 1) : 0;
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int ahead = min(S::kStages - 2, ntiles - 1 - kt);   // tiles after kt in flight
+    if (st < ntiles) dma_tile(kt0 + st, block_id(kt0 + st), kbuf(st), vbuf(st));
+  int next_blk = ntiles > 0 ? block_id(kt0 + S::kStages - 1) : 0;
+  for (int it = 0; it < ntiles; ++it) {
+    const int ahead = min(S::kStages - 2, ntiles - 1 - it);   // tiles after it in flight
     if (S::kStages >= 3 && ahead >= 1)
       wait_vm<(S::kStages >= 3 ? S::kLoadsPerTile : 0)>();
     else
       wait_vm<0>();
     lds_barrier();
-    const int nt = kt + S::kStages - 1;
+    const int nt = it + S::kStages - 1;
     if (nt < ntiles) {
-      dma_tile(nt, next_blk, kbuf(nt % S::kStages), vbuf(nt % S::kStages));
-      next_blk = block_id(nt + 1);
+      dma_tile(kt0 + nt, next_blk, kbuf(nt % S::kStages), vbuf(nt % S::kStages));
+      next_blk = block_id(kt0 + nt + 1);
     }
-    const int st = kt % S::kStages;
-    compute(kt, kbuf(st), vbuf(st));
+    const int st = it % S::kStages;
+    compute(kt0 + it, kbuf(st), vbuf(st));
   }
 
   // ---- normalise and write: lane (j, hh) holds dims (r/4)*8 + hh*4 + r%4
   // of each 32-dim tile for its row.
   const float total = run_sum + swap_halves(run_sum);
   if (!row_ok) return;
+  if (p.group_mode) {
+    // A partial: the unnormalised output, its reference max and its sum.
+    const int64_t slot =
+        ((static_cast<int64_t>(q0) + i_pos) * p.num_heads + kvh * G + h) *
+            p.ws_stride + p.slot0 + chunk;
+    float* acc = p.ws_acc + slot * D;
+#pragma unroll
+    for (int dt = 0; dt < S::kDTiles; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<float4*>(acc + dt * 32 + g4 * 8 + hh * 4) =
+            make_float4(oacc[dt][g4 * 4], oacc[dt][g4 * 4 + 1],
+                        oacc[dt][g4 * 4 + 2], oacc[dt][g4 * 4 + 3]);
+    if (hh == 0) {
+      p.ws_max[slot] = run_max;
+      p.ws_sum[slot] = total;
+    }
+    return;
+  }
   const float inv = total > 0.f ? 1.f / total : 0.f;
   T* orow = reinterpret_cast<T*>(p.out) +
             ((static_cast<int64_t>(q0) + i_pos) * p.num_heads + kvh * G + h) * D;
@@ -750,6 +811,25 @@ int m_tiles(int max_seqlen_q, int group, int bm) {
 }
 
 template <typename T, int D, int G>
+hipError_t launch_kernel(const PrefillParams& pr, int64_t wgs, hipStream_t stream) {
+  using S = PrefillShape<T, D>;
+  const size_t lds = S::kLds;
+  if (lds > 65536) {
+    static bool raised = false;   // once per kernel instantiation
+    if (!raised) {
+      hipError_t e = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(&prefill_kernel<T, D, G>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      if (e != hipSuccess) return e;
+      raised = true;
+    }
+  }
+  hipLaunchKernelGGL((prefill_kernel<T, D, G>), dim3(static_cast<unsigned>(wgs)),
+                     dim3(S::kThreads), lds, stream, pr);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int G>
 hipError_t launch_typed(const PrefillParams& prm, const PrefillArgs& a,
                         hipStream_t stream) {
   using S = PrefillShape<T, D>;
@@ -783,19 +863,28 @@ hipError_t launch_typed(const PrefillParams& prm, const PrefillArgs& a,
     if (e != hipSuccess) return e;
     pr.order = order;
   }
-  if (lds > 65536) {
-    static bool raised = false;   // once per kernel instantiation
-    if (!raised) {
-      hipError_t e = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&prefill_kernel<T, D, G>),
-          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-      if (e != hipSuccess) return e;
-      raised = true;
-    }
-  }
-  hipLaunchKernelGGL((prefill_kernel<T, D, G>), dim3(static_cast<unsigned>(wgs)),
-                     dim3(S::kThreads), lds, stream, pr);
-  return hipGetLastError();
+  (void)lds;
+  return launch_kernel<T, D, G>(pr, wgs, stream);
+}
+
+// Shared-prefix partials: group mode of the same kernel, natural order.
+template <typename T, int D, int G>
+hipError_t launch_prefix_typed(const PrefillParams& prm, const PrefixArgs& a,
+                               const SharedPrefixPlan& plan, hipStream_t stream) {
+  using S = PrefillShape<T, D>;
+  if (a.num_groups <= 0 || plan.prefix_chunks <= 0 || a.max_group_size <= 0)
+    return hipSuccess;
+  PrefillParams pr = prm;
+  pr.mtiles = m_tiles(a.max_group_size, G, S::kBM);
+  const int64_t items = static_cast<int64_t>(a.num_groups) * plan.prefix_chunks;
+  const int64_t wgs = items * pr.mtiles * a.num_kv_heads;
+  if (items > 0x7fffffff || wgs > 0x7fffffff) return hipErrorNotSupported;
+  pr.num_seqs = static_cast<int>(items);
+  pr.order = nullptr;
+  pr.group_mode = 1;
+  pr.chunk_tiles = plan.prefix_chunk_tokens / kBN;
+  pr.chunks = plan.prefix_chunks;
+  return launch_kernel<T, D, G>(pr, wgs, stream);
 }
 
 template <typename T, int D>
@@ -806,6 +895,18 @@ hipError_t dispatch_group(const PrefillParams& prm, const PrefillArgs& a, int g,
     case 2: return launch_typed<T, D, 2>(prm, a, s);
     case 4: return launch_typed<T, D, 4>(prm, a, s);
     case 8: return launch_typed<T, D, 8>(prm, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T, int D>
+hipError_t dispatch_prefix(const PrefillParams& prm, const PrefixArgs& a,
+                           const SharedPrefixPlan& plan, hipStream_t s) {
+  switch (a.num_heads / a.num_kv_heads) {
+    case 1: return launch_prefix_typed<T, D, 1>(prm, a, plan, s);
+    case 2: return launch_prefix_typed<T, D, 2>(prm, a, plan, s);
+    case 4: return launch_prefix_typed<T, D, 4>(prm, a, plan, s);
+    case 8: return launch_prefix_typed<T, D, 8>(prm, a, plan, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -848,6 +949,39 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   }
   if (a.head_dim == 128) return dispatch_group<float, 128>(prm, a, g, stream);
   return dispatch_group<float, 64>(prm, a, g, stream);
+}
+
+hipError_t launch_prefix_partials(const PrefixArgs& a,
+                                  const SharedPrefixPlan& plan,
+                                  hipStream_t stream) {
+  PrefillParams prm{};
+  prm.q = static_cast<const char*>(a.q);
+  prm.total_q = a.num_seqs;
+  prm.k_cache = static_cast<const char*>(a.k_cache);
+  prm.v_cache = static_cast<const char*>(a.v_cache);
+  prm.num_blocks = a.num_blocks;
+  prm.max_seqlen_q = a.max_group_size;
+  prm.max_seqlen_k = a.max_prefix_len;
+  prm.block_tables = a.block_tables;
+  prm.max_blocks_per_seq = a.max_blocks_per_seq;
+  prm.num_heads = a.num_heads;
+  prm.num_kv_heads = a.num_kv_heads;
+  prm.scale_log2 = a.scale * kLog2e;
+  prm.causal = 0;
+  prm.groups = a.groups;
+  prm.prefix_lens = a.prefix_lens;
+  char* ws = static_cast<char*>(a.workspace);
+  prm.ws_max = reinterpret_cast<float*>(ws + plan.off_max);
+  prm.ws_sum = reinterpret_cast<float*>(ws + plan.off_sum);
+  prm.ws_acc = reinterpret_cast<float*>(ws + plan.off_acc);
+  prm.ws_stride = plan.total_slots;
+  prm.slot0 = plan.suffix.num_partitions;
+  if (a.bf16) {
+    if (a.head_dim == 128) return dispatch_prefix<bf16_t, 128>(prm, a, plan, stream);
+    return dispatch_prefix<bf16_t, 64>(prm, a, plan, stream);
+  }
+  if (a.head_dim == 128) return dispatch_prefix<float, 128>(prm, a, plan, stream);
+  return dispatch_prefix<float, 64>(prm, a, plan, stream);
 }
 
 }  // namespace pa

@@ -54,6 +54,50 @@ def decode_inputs(tables, lens, block_size, width=None):
     }
 
 
+def shared_prefix_inputs(tables, lens, block_size):
+    """Sharing groups of a decode batch, for decode_shared_prefix: runs of
+    consecutive sequences whose leading full blocks are the same physical
+    blocks.  A sequence that shares k >= 1 full blocks with the next one
+    opens a group with a k-block prefix; following sequences join while
+    they share at least those k blocks with the group's first sequence.
+
+    Returns dict(prefix_lens int32 [B] (k * block_size for members, 0
+    otherwise), groups int32 [G, 2] (first, count), max_prefix_len,
+    max_suffix_len, max_group_size).
+    """
+    lens = np.asarray(lens, dtype=np.int64)
+    rows = [np.asarray(t, dtype=np.int64) for t in tables]
+    full = lens // block_size
+
+    def common(a, b):
+        n = int(min(full[a], full[b]))
+        diff = np.nonzero(rows[a][:n] != rows[b][:n])[0]
+        return int(diff[0]) if len(diff) else n
+
+    prefix = np.zeros(len(rows), dtype=np.int64)
+    groups = []
+    i = 0
+    while i < len(rows):
+        k = common(i, i + 1) if i + 1 < len(rows) else 0
+        if k == 0:
+            i += 1
+            continue
+        j = i + 1
+        while j + 1 < len(rows) and common(i, j + 1) >= k:
+            j += 1
+        prefix[i:j + 1] = k * block_size
+        groups.append((i, j - i + 1))
+        i = j + 1
+    g = np.asarray(groups, dtype=np.int32).reshape(-1, 2)
+    return {
+        "prefix_lens": prefix.astype(np.int32),
+        "groups": g,
+        "max_prefix_len": int(prefix.max()) if len(prefix) else 0,
+        "max_suffix_len": int((lens - prefix).max()) if len(lens) else 0,
+        "max_group_size": int(g[:, 1].max()) if len(g) else 0,
+    }
+
+
 def prefill_inputs(tables, num_cached, num_scheduled, block_size, width=None):
     """Chunked-prefill batch: sequence b computes tokens
     [num_cached[b], num_cached[b] + num_scheduled[b]) this round.

@@ -139,6 +139,61 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
     return out
 
 
+def shared_prefix_workspace_bytes(num_seqs, num_heads, num_kv_heads,
+                                  head_dim, max_suffix_len, max_prefix_len,
+                                  num_groups, max_group_size):
+    return int(_lib.load().pa_decode_shared_prefix_workspace_bytes(
+        num_seqs, num_heads, num_kv_heads, head_dim, max_suffix_len,
+        max_prefix_len, num_groups, max_group_size))
+
+
+def decode_shared_prefix(q, k_cache, v_cache, block_tables, context_lens,
+                         prefix_lens, groups, max_suffix_len, max_prefix_len,
+                         max_group_size, scale=None, out=None,
+                         workspace=None):
+    """Decode attention where groups of consecutive sequences share their
+    leading blocks (same result as decode()).  prefix_lens int32 [B]
+    (shared tokens, 0 outside any group); groups int32 [G, 2] (first
+    sequence, count); max_suffix_len / max_prefix_len / max_group_size are
+    host-side bounds.  Returns out [B, Hq, D]."""
+    _need_gpu(q, k_cache, v_cache, block_tables, context_lens, prefix_lens,
+              groups, out, workspace)
+    for t, n in ((block_tables, "block_tables"), (context_lens, "context_lens"),
+                 (prefix_lens, "prefix_lens"), (groups, "groups")):
+        _i32(t, n)
+    b, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if d2 != d or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shape does not match q")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b:
+        raise ValueError("block_tables must be [B, W]")
+    if context_lens.numel() != b or prefix_lens.numel() != b:
+        raise ValueError("context_lens and prefix_lens must be [B]")
+    if groups.dim() != 2 or groups.shape[1] != 2:
+        raise ValueError("groups must be [G, 2]")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and caches must share a dtype")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    ng = groups.shape[0]
+    need = shared_prefix_workspace_bytes(b, hq, hkv, d, max_suffix_len,
+                                         max_prefix_len, ng, max_group_size)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() \
+        if workspace is not None else 0
+    lib = _lib.load()
+    st = lib.pa_decode_shared_prefix(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), nb, bs,
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        _ptr(prefix_lens), int(max_suffix_len), int(max_prefix_len),
+        _ptr(groups), ng, int(max_group_size), b, hq, hkv, d, scale,
+        _ptr(workspace), ws_bytes, _dtype_code(q), _stream(q))
+    _lib.check("pa_decode_shared_prefix", st)
+    return out
+
+
 def prefill_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
                             max_seqlen_q, max_seqlen_k):
     return int(_lib.load().pa_prefill_workspace_bytes(

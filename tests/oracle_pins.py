@@ -123,6 +123,40 @@ def check_prefix_sharing_example():
     assert copies == exp["copies"]
 
 
+def check_shared_prefix_groups():
+    """Sharing groups for the read-once decode (Warmup Guide, Chapter 4):
+    the figure's three requests form one group whose shared length is the
+    two prompt blocks; by hand from the rule: only full blocks count, a
+    group keeps the first pair's shared length, a shorter share starts a
+    new group, and a sequence sharing nothing stays alone."""
+    g = _golden("prefix_sharing.json")
+    bs = g["block_size"]
+    nshared = g["expected"]["tables_share_first_blocks"]
+    prompt = list(range(nshared))
+    seqs = [{"block_table": prompt + [10 + i], "length": g["prompt_tokens"] + 1 + i}
+            for i in range(len(g["requests"]))]
+    lens, groups = om.shared_prefix_groups(seqs, bs)
+    assert groups == [(0, len(g["requests"]))], groups
+    assert lens == [nshared * bs] * len(g["requests"]), lens
+
+    def run(tables, lengths, b=4):
+        return om.shared_prefix_groups(
+            [{"block_table": t, "length": n} for t, n in zip(tables, lengths)], b)
+
+    # equal ids past the shorter sequence's full blocks do not count
+    assert run([[1, 2, 3], [1, 2, 4], [5, 6]], [12, 10, 8]) == \
+        ([8, 8, 0], [(0, 2)])
+    # a partially filled last block is never shared, even with equal ids
+    assert run([[1, 2], [1, 2]], [6, 7]) == ([4, 4], [(0, 2)])
+    # the group keeps the first pair's 3 blocks; a 2-block share starts anew
+    assert run([[1, 2, 3], [1, 2, 3], [1, 2, 9], [1, 7, 8]], [12, 12, 12, 12]) == \
+        ([12, 12, 4, 4], [(0, 2), (2, 2)])
+    # nothing shared
+    assert run([[1], [2], [3]], [4, 4, 4]) == ([0, 0, 0], [])
+    # a single sequence never forms a group
+    assert run([[1, 2]], [8]) == ([0], [])
+
+
 def check_copy_on_write_partial_block():
     """Warmup Guide, Chapter 4: appending into a partially filled block that
     another sequence also holds copies that one block first, lowers its ref
@@ -547,6 +581,7 @@ ALL_CHECKS = [
     check_decode_slot_closed_form,
     check_decode_padding,
     check_prefix_sharing_example,
+    check_shared_prefix_groups,
     check_copy_on_write_partial_block,
     check_copy_blocks_against_brute,
     check_kv_bytes,

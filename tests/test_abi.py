@@ -161,3 +161,45 @@ def _copy(lib, **kw):
 ])
 def test_copy_blocks_validation(kw, code, no_device):
     assert _copy(_lib.load(), **kw) == code
+
+
+def _shared(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, nb=64, bs=16, bt=FAKE, w=8,
+             cl=FAKE, pl=FAKE, maxsuf=60, maxpre=64, groups=FAKE, ng=1,
+             maxg=4, b=4, hq=8, hkv=2, d=64, scale=0.125, ws=None, wsb=0,
+             dtype=_lib.PA_F32, stream=None)
+    a.update(kw)
+    return lib.pa_decode_shared_prefix(
+        a["out"], a["q"], a["k"], a["v"], a["nb"], a["bs"], a["bt"], a["w"],
+        a["cl"], a["pl"], a["maxsuf"], a["maxpre"], a["groups"], a["ng"],
+        a["maxg"], a["b"], a["hq"], a["hkv"], a["d"], a["scale"], a["ws"],
+        a["wsb"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), 3), (dict(bs=8), 3), (dict(hq=6, hkv=2), 3),
+    (dict(dtype=4), 3), (dict(b=-1), 2), (dict(maxsuf=-1), 2),
+    (dict(maxpre=-16), 2), (dict(ng=-1), 2), (dict(maxg=-2), 2),
+    (dict(maxsuf=0x7fffffff, maxpre=16), 2), (dict(scale=0.0), 2),
+    (dict(out=None), 1), (dict(q=None), 1), (dict(cl=None), 1),
+    (dict(pl=None), 1), (dict(bt=None), 1), (dict(groups=None), 1),
+    (dict(v=MISALIGNED), 3),
+    (dict(), 4),                                   # workspace is required
+    (dict(ws=FAKE, wsb=64), 4),                    # and must be large enough
+    (dict(b=0), 0),                                # empty batch: no-op
+])
+def test_shared_prefix_validation(kw, code, no_device):
+    assert _shared(_lib.load(), **kw) == code
+
+
+def test_shared_prefix_workspace_query():
+    lib = _lib.load()
+    q = lib.pa_decode_shared_prefix_workspace_bytes
+    # 128 sequences sharing 2,048 tokens, suffixes up to 512: one suffix
+    # partition plus the prefix chunks, (max, sum, D floats) each
+    n = q(128, 32, 8, 128, 512, 2048, 1, 128)
+    assert n >= 128 * 32 * 2 * (128 + 2) * 4 and n % 256 == 0
+    # no prefix: still one partial slot per (sequence, head) for the merge
+    assert q(4, 8, 2, 64, 100, 0, 0, 0) >= 4 * 8 * (64 + 2) * 4
+    assert q(0, 8, 2, 64, 100, 0, 0, 0) == 0
+    assert q(4, 8, 2, 64, -1, 0, 0, 0) == 0

@@ -108,3 +108,35 @@ def test_block_pool_matches_oracle(seed):
         for blk, count in ref.ref.items():
             assert pool.refs[blk] == count
         assert pool.num_free == len(ref.free)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_shared_prefix_inputs_match_oracle(seed):
+    """Random batches with planted runs of sharers (prefixes of various
+    lengths, partial last blocks, equal ids past a sequence's full blocks):
+    the product's sharing groups equal the oracle's exactly."""
+    rng = np.random.default_rng(seed)
+    bs = 16
+    tables, lens = [], []
+    nxt = 1000
+    while len(tables) < 40:
+        run = int(rng.integers(1, 6))
+        k = int(rng.integers(0, 6))
+        prefix = list(range(nxt, nxt + k))
+        nxt += k
+        for _ in range(run):
+            extra = int(rng.integers(0, 4))
+            t = prefix[:int(rng.integers(max(k - 1, 0), k + 1))] + \
+                list(range(nxt, nxt + extra + 1))
+            nxt += extra + 1
+            n = (len(t) - 1) * bs + int(rng.integers(1, bs + 1))
+            tables.append(t)
+            lens.append(n)
+    got = pm.shared_prefix_inputs(tables, lens, bs)
+    want_lens, want_groups = om.shared_prefix_groups(
+        [{"block_table": t, "length": n} for t, n in zip(tables, lens)], bs)
+    assert got["prefix_lens"].tolist() == want_lens
+    assert [tuple(g) for g in got["groups"].tolist()] == want_groups
+    assert got["max_group_size"] == max((c for _, c in want_groups), default=0)
+    assert got["max_prefix_len"] == max(want_lens)
+    assert got["max_suffix_len"] == max(n - p for n, p in zip(lens, want_lens))

@@ -185,6 +185,29 @@ def _copy_blocks_reversed(k_cache, v_cache, pairs):
     return k_out, v_out
 
 
+_orig_shared_groups = om.shared_prefix_groups
+
+
+def _shared_groups_counts_partial(seqs, block_size):
+    """Counts the partially filled last block as shareable."""
+    rounded = [{"block_table": s["block_table"],
+                "length": -(-s["length"] // block_size) * block_size} for s in seqs]
+    return _orig_shared_groups(rounded, block_size)
+
+
+def _shared_groups_greedy_shrink(seqs, block_size):
+    """Lets the group's shared length shrink as members join."""
+    lens, groups = _orig_shared_groups(seqs, block_size)
+    if len(groups) > 1 and groups[0][0] + groups[0][1] == groups[1][0]:
+        first, count = groups[0]
+        merged = (first, count + groups[1][1])
+        k = min(lens[first], lens[groups[1][0]])
+        for b in range(first, first + merged[1]):
+            lens[b] = k
+        groups = [merged] + groups[2:]
+    return lens, groups
+
+
 MUTATIONS = {
     "drop_scale": (oa, "attend", _attend_factory(drop_scale=True)),
     "no_normalize": (oa, "attend", _attend_factory(no_normalize=True)),
@@ -203,6 +226,10 @@ MUTATIONS = {
     "cow_no_decrement": (om.RefCountedPool, "append", _pool_append_no_decrement),
     "share_no_count": (om.RefCountedPool, "share", _pool_share_no_count),
     "copy_blocks_reversed": (oa, "copy_blocks", _copy_blocks_reversed),
+    "shared_counts_partial": (om, "shared_prefix_groups",
+                              _shared_groups_counts_partial),
+    "shared_group_shrinks": (om, "shared_prefix_groups",
+                             _shared_groups_greedy_shrink),
 }
 
 
