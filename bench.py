@@ -269,24 +269,46 @@ def run_prefix(steps, warmup, dev, flush):
         b, hq, hkv, d, meta["max_context_len"]), 1), dtype=torch.uint8,
         device=dev)
 
-    def step(ev):
-        ev[0].record()
-        ops.store_kv(k_new, v_new, kc, vc, slot)
-        ev[1].record()
+    sp = pm.shared_prefix_inputs(lay.tables, lay.lens, bs)
+    pl = torch.as_tensor(sp["prefix_lens"], device=dev)
+    groups = torch.as_tensor(sp["groups"], device=dev)
+    ng = int(sp["groups"].shape[0])
+    wsp = torch.empty(max(ops.shared_prefix_workspace_bytes(
+        b, hq, hkv, d, sp["max_suffix_len"], sp["max_prefix_len"], ng,
+        sp["max_group_size"]), 1), dtype=torch.uint8, device=dev)
+    out2 = torch.empty_like(q)
+
+    def attend_plain():
         ops.decode(q, kc, vc, bt, cl, meta["max_context_len"], scale=scale,
                    out=out, workspace=ws)
-        ev[2].record()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-           for _ in range(steps + warmup)]
-    for i in range(warmup):
-        step(evs[steps + i])
-    torch.cuda.synchronize()
-    for i in range(steps):
-        flush()
-        step(evs[i])
-    torch.cuda.synchronize()
-    dec = float(np.median([e[1].elapsed_time(e[2]) for e in evs[:steps]]))
+    def attend_shared():
+        ops.decode_shared_prefix(q, kc, vc, bt, cl, pl, groups,
+                                 sp["max_suffix_len"], sp["max_prefix_len"],
+                                 sp["max_group_size"], scale=scale, out=out2,
+                                 workspace=wsp)
+
+    def timed(attend):
+        def step(ev):
+            ev[0].record()
+            ops.store_kv(k_new, v_new, kc, vc, slot)
+            ev[1].record()
+            attend()
+            ev[2].record()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+               for _ in range(steps + warmup)]
+        for i in range(warmup):
+            step(evs[steps + i])
+        torch.cuda.synchronize()
+        for i in range(steps):
+            flush()
+            step(evs[i])
+        torch.cuda.synchronize()
+        return float(np.median([e[1].elapsed_time(e[2]) for e in evs[:steps]]))
+
+    dec = timed(attend_plain)
+    shared = timed(attend_shared)
+    diff = float((out.float() - out2.float()).abs().max())
     row = 2 * hkv * d * 2
     logical = decode_bytes(lay.lens, hq, hkv, d, 2)
     pre_tok = cfg.shared_prefix_blocks * bs
@@ -302,6 +324,18 @@ def run_prefix(steps, warmup, dev, flush):
         "logical_tbs": round(logical / (dec * 1e-3) / 1e12, 4),
         "decode_tokens_per_s": round(b / (dec * 1e-3), 1),
         "kernel": "pa_decode (every sequence reads its whole context)",
+        "shared_prefix": {
+            "kernel": "pa_decode_shared_prefix (shared blocks read once per "
+                      "group: prefix partials on MFMA + suffix partitions + "
+                      "merge)",
+            "groups": ng,
+            "decode_us": round(shared * 1e3, 2),
+            "unique_tbs": round(unique / (shared * 1e-3) / 1e12, 4),
+            "logical_tbs": round(logical / (shared * 1e-3) / 1e12, 4),
+            "decode_tokens_per_s": round(b / (shared * 1e-3), 1),
+            "speedup_vs_pa_decode": round(dec / shared, 3),
+            "max_abs_diff_vs_pa_decode": round(diff, 6),
+        },
     }
 
 

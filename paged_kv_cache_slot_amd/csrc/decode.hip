@@ -719,7 +719,10 @@ hipError_t dispatch_group(const DecodeParams& prm, int num_seqs,
 }
 
 // Tokens per chunk: the logits of one chunk sit in LDS.
-constexpr int kChunkTokens = 512;
+#ifndef PA_DECODE_CHUNK_TOKENS
+#define PA_DECODE_CHUNK_TOKENS 512
+#endif
+constexpr int kChunkTokens = PA_DECODE_CHUNK_TOKENS;
 // A partition spans one or more chunks.  Fewer, longer partitions write
 // fewer partial results (which slow the K/V stream far beyond their own
 // bytes) but leave fewer workgroups to balance; the plan takes the longest
@@ -729,7 +732,10 @@ constexpr int kChunkTokens = 512;
 #endif
 constexpr int64_t kTargetWorkgroups = PA_DECODE_TARGET_WGS;
 constexpr int kMaxChunksPerPartition = 16;
-constexpr int64_t kPrefixTargetWorkgroups = 128;
+#ifndef PA_PREFIX_TARGET_WGS
+#define PA_PREFIX_TARGET_WGS 128
+#endif
+constexpr int64_t kPrefixTargetWorkgroups = PA_PREFIX_TARGET_WGS;
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
