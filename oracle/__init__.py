@@ -18,6 +18,12 @@ hot path computes:
   (prepare_prefill / prepare_decode) and section 5 (padding), and the
   "Warmup Guide -- Inference Serving Internals", Chapter 3 (blocks, block
   table, the append off-by-one).
+* ``fp8`` -- an 8-bit (OCP E4M3) KV cache: the code of a scaled value
+  (round to nearest even, saturating), code values, the quantising store and
+  decode over dequantised K/V.  The pages only name a cache-precision flag
+  ("10 Serving Engines"); format, rounding and scale are readings, pinned
+  against an independent E4M3 implementation (parity partly unpinned by
+  the pages).
 * ``attention`` -- the slot scatter of new K/V rows, the gather of one
   sequence's K/V through its block table into contiguous arrays, and
   softmax(scale * q K^T) V for decode rows and varlen (chunked) prefill rows

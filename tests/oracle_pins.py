@@ -14,6 +14,7 @@ import os
 import numpy as np
 
 import oracle.attention as oa
+import oracle.fp8 as of8
 import oracle.metadata as om
 from tests import brute_force as bf
 
@@ -155,6 +156,77 @@ def check_shared_prefix_groups():
     assert run([[1], [2], [3]], [4, 4, 4]) == ([0, 0, 0], [])
     # a single sequence never forms a group
     assert run([[1, 2]], [8]) == ([0], [])
+
+
+def check_e4m3_codes_against_library():
+    """E4M3 values of all 256 codes equal torch's float8_e4m3fn decoding
+    (an independent implementation of the OCP format)."""
+    import torch
+    lib = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn) \
+        .to(torch.float64).numpy()
+    mine = np.array([of8.e4m3_value(c) for c in range(256)])
+    assert np.array_equal(np.isnan(lib), np.isnan(mine))
+    ok = ~np.isnan(lib)
+    assert np.array_equal(lib[ok], mine[ok])
+
+
+def check_e4m3_encode_against_library():
+    """Encoding equals torch's round-to-nearest-even float32 -> e4m3fn cast
+    of the value saturated to +-448, over normals, subnormals, exact ties
+    (midpoints between neighbouring codes) and out-of-range values."""
+    import torch
+    rng = np.random.default_rng(21)
+    vals = np.array([of8.e4m3_value(c) for c in range(256)])
+    vals = vals[np.isfinite(vals)]
+    srt = np.unique(vals)
+    mids = (srt[1:] + srt[:-1]) / 2
+    x = np.concatenate([
+        rng.normal(size=4000) * rng.choice([1e-3, 0.05, 1, 30, 400], 4000),
+        mids, vals, [600.0, -1e30, 449.0, 464.0, 500.0, -0.0, 0.0]]).astype(np.float32)
+    mine = of8.quantize(x, 1.0)
+    lib = torch.from_numpy(np.clip(x, -448, 448)).to(torch.float8_e4m3fn) \
+        .view(torch.uint8).numpy()
+    assert np.array_equal(mine, lib), np.nonzero(mine != lib)[0][:10]
+
+
+def check_e4m3_hand_values():
+    """Values worked out by hand from the format: 1 = 0x38, 448 = 0x7E (the
+    largest finite), larger values saturate to it, -0 keeps its sign,
+    2^-9 is the smallest subnormal; halfway cases go to the even mantissa
+    (2^-10 -> 0, 3 * 2^-10 -> 2 steps, 1 + 1/16 -> 1, 1 + 3/16 -> 1.25);
+    1.125 * 2^-4 = 0x19; the scale divides before rounding."""
+    enc = of8.e4m3_encode
+    assert enc(1.0) == 0x38 and enc(448.0) == 0x7E and enc(1e6) == 0x7E
+    assert enc(-1e6) == 0xFE and enc(-0.0) == 0x80 and enc(0.0) == 0x00
+    assert enc(2.0 ** -9) == 0x01 and enc(2.0 ** -10) == 0x00
+    assert enc(3 * 2.0 ** -10) == 0x02
+    assert enc(1 + 1 / 16) == 0x38 and enc(1 + 3 / 16) == 0x3A
+    assert enc(1.125 * 2.0 ** -4) == 0x19
+    assert of8.quantize(np.float32([3.0]), 0.5)[0] == enc(1.5)
+    assert of8.e4m3_value(0x7E) == 448.0 and math.isnan(of8.e4m3_value(0xFF))
+
+
+def check_fp8_decode_equals_dequantized():
+    """Decode over an E4M3 cache equals plain decode over float32 caches
+    holding code * scale (exact in float32), for random codes and scales."""
+    rng = np.random.default_rng(23)
+    nb, bs, hkv, d, hq = 6, 4, 2, 8, 4
+    kc = rng.integers(0, 256, size=(nb, bs, hkv, d)).astype(np.uint8)
+    vc = rng.integers(0, 256, size=(nb, bs, hkv, d)).astype(np.uint8)
+    kc[(kc & 0x7F) == 0x7F] = 0x10            # no NaN codes
+    vc[(vc & 0x7F) == 0x7F] = 0x21
+    q = rng.normal(size=(3, hq, d)).astype(np.float32)
+    tables = [[0, 3], [5, 1, 2], [4]]
+    lens = [7, 10, 3]
+    bt = np.full((3, 3), -1)
+    for i, t in enumerate(tables):
+        bt[i, :len(t)] = t
+    ks, vs = 0.0625, 0.015625
+    got = of8.decode_attention(q, kc, vc, bt, lens, 0.3, ks, vs, "f32")
+    kf = of8.dequantize(kc, ks).astype(np.float32)
+    vf = of8.dequantize(vc, vs).astype(np.float32)
+    want = oa.decode_attention(q, kf, vf, bt, lens, 0.3, "f32")
+    assert np.max(np.abs(got - want)) < 1e-12
 
 
 def check_copy_on_write_partial_block():
@@ -583,6 +655,10 @@ ALL_CHECKS = [
     check_prefix_sharing_example,
     check_shared_prefix_groups,
     check_copy_on_write_partial_block,
+    check_e4m3_codes_against_library,
+    check_e4m3_encode_against_library,
+    check_e4m3_hand_values,
+    check_fp8_decode_equals_dequantized,
     check_copy_blocks_against_brute,
     check_kv_bytes,
     check_bf16_widening,

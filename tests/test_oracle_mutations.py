@@ -208,6 +208,40 @@ def _shared_groups_greedy_shrink(seqs, block_size):
     return lens, groups
 
 
+import oracle.fp8 as of8  # noqa: E402
+
+_orig_e4m3_encode = of8.e4m3_encode
+_orig_e4m3_value = of8.e4m3_value
+
+
+def _e4m3_round_half_up(v):
+    """Rounds halfway cases away from zero instead of to even."""
+    code = _orig_e4m3_encode(v)
+    a = abs(float(v))
+    if a != a or a >= 448.0:
+        return code
+    nxt = _orig_e4m3_value((code & 0x7F) + 1) if (code & 0x7F) < 0x7E else None
+    here = abs(_orig_e4m3_value(code))
+    if nxt is not None and a - here == nxt - a:
+        return (code & 0x80) | ((code & 0x7F) + 1)
+    return code
+
+
+def _e4m3_no_saturation(v):
+    """Lets values past 448 become the NaN code."""
+    if abs(float(v)) > 464.0:
+        return (0x80 if v < 0 else 0) | 0x7F
+    return _orig_e4m3_encode(v)
+
+
+def _e4m3_subnormal_exponent(code):
+    """Gives subnormals the exponent of the smallest normal binade."""
+    if (code >> 3) & 0xF == 0 and code & 7:
+        s = -1.0 if code & 0x80 else 1.0
+        return s * (1 + (code & 7) / 8.0) * 2.0 ** -7
+    return _orig_e4m3_value(code)
+
+
 MUTATIONS = {
     "drop_scale": (oa, "attend", _attend_factory(drop_scale=True)),
     "no_normalize": (oa, "attend", _attend_factory(no_normalize=True)),
@@ -230,6 +264,9 @@ MUTATIONS = {
                               _shared_groups_counts_partial),
     "shared_group_shrinks": (om, "shared_prefix_groups",
                              _shared_groups_greedy_shrink),
+    "e4m3_round_half_up": (of8, "e4m3_encode", _e4m3_round_half_up),
+    "e4m3_no_saturation": (of8, "e4m3_encode", _e4m3_no_saturation),
+    "e4m3_subnormal_exponent": (of8, "e4m3_value", _e4m3_subnormal_exponent),
 }
 
 
