@@ -7,6 +7,7 @@
  *   pa_copy_blocks     copy whole blocks (the data side of copy-on-write)
  *   pa_decode_shared_prefix  decode where groups of sequences share leading
  *                      blocks: the shared keys are read once per group
+ *   pa_store_kv_fp8, pa_decode_fp8  the same over an 8-bit (E4M3) cache
  *   pa_decode          one query row per sequence against its paged context
  *   pa_prefill_varlen  packed variable-length (chunked) prefill, causal,
  *                      history read through block tables
@@ -282,6 +283,54 @@ pa_status pa_decode_shared_prefix(
     int32_t max_group_size, int32_t num_seqs, int32_t num_heads,
     int32_t num_kv_heads, int32_t head_dim, float scale, void* workspace,
     size_t workspace_bytes, pa_dtype dtype, void* stream);
+
+/*
+ * 8-bit KV cache.  The pages name a cache-precision option ("10 Serving
+ * Engines": the --kv-cache-dtype flag, effective where the engine and its
+ * kernels support it) and fix nothing else; the format here is OCP E4M3
+ * (sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities,
+ * largest finite 448), one byte per element, with one float scale per cache
+ * chosen by the caller: an element x is stored as the code nearest to
+ * x / scale (the product x * (1 / scale) in float32, ties to an even
+ * mantissa, saturated to +-448); attention reads code * scale.  Layout,
+ * slots and block tables are those of the 16/32-bit caches:
+ * [num_blocks, block_size, num_kv_heads, head_dim] bytes per cache.
+ */
+
+/*
+ * pa_store_kv_fp8 -- as pa_store_kv, quantising each row into E4M3 caches.
+ *
+ *   k, v          device, [num_tokens, num_kv_heads, head_dim] of src_dtype
+ *                 (PA_F32 or PA_BF16), 16-byte aligned
+ *   k_cache,
+ *   v_cache       device uint8, [num_slots, num_kv_heads, head_dim]
+ *   k_scale,
+ *   v_scale       > 0, finite: the caches' scales
+ *
+ * Requires num_kv_heads * head_dim to be a multiple of 8.
+ */
+pa_status pa_store_kv_fp8(const void* k, const void* v, void* k_cache,
+                          void* v_cache, const int32_t* slot_mapping,
+                          int64_t num_tokens, int32_t num_kv_heads,
+                          int32_t head_dim, int64_t num_slots,
+                          pa_dtype src_dtype, float k_scale, float v_scale,
+                          void* stream);
+
+/*
+ * pa_decode_fp8 -- as pa_decode over E4M3 caches, with q and out bfloat16:
+ * out[b,h] = softmax(scale * q . K) V with K = code * k_scale and
+ * V = code * v_scale.  head_dim 128 only.  Workspace as
+ * pa_decode_workspace_bytes(...) for the same sizes.
+ */
+pa_status pa_decode_fp8(void* out, const void* q, const void* k_cache,
+                        const void* v_cache, int64_t num_blocks,
+                        int32_t block_size, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const int32_t* context_lens,
+                        int32_t max_context_len, int32_t num_seqs,
+                        int32_t num_heads, int32_t num_kv_heads,
+                        int32_t head_dim, float scale, float k_scale,
+                        float v_scale, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 #ifdef __cplusplus
 }

@@ -55,6 +55,13 @@ SIGNATURES = {
         _c_void_p, _i32, _c_void_p, _c_void_p, _i32, _i32, _c_void_p, _i32,
         _i32, _i32, _i32, _i32, _i32, _f32, _c_void_p, _size, ctypes.c_int,
         _c_void_p]),
+    "pa_store_kv_fp8": (ctypes.c_int, [
+        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+        _i64, _i32, _i32, _i64, ctypes.c_int, _f32, _f32, _c_void_p]),
+    "pa_decode_fp8": (ctypes.c_int, [
+        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32,
+        _c_void_p, _i32, _c_void_p, _i32, _i32, _i32, _i32, _i32, _f32,
+        _f32, _f32, _c_void_p, _size, _c_void_p]),
 }
 
 _lib = None

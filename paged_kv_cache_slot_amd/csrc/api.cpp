@@ -314,4 +314,84 @@ pa_status pa_decode_shared_prefix(
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+pa_status pa_store_kv_fp8(const void* k, const void* v, void* k_cache,
+                          void* v_cache, const int32_t* slot_mapping,
+                          int64_t num_tokens, int32_t num_kv_heads,
+                          int32_t head_dim, int64_t num_slots,
+                          pa_dtype src_dtype, float k_scale, float v_scale,
+                          void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_slots < 0)
+    return PA_ERR_SHAPE;
+  if (!(k_scale > 0.f) || !std::isfinite(k_scale) || !(v_scale > 0.f) ||
+      !std::isfinite(v_scale))
+    return PA_ERR_SHAPE;
+  if (!dtype_ok(src_dtype)) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
+  const int64_t row_elems = static_cast<int64_t>(num_kv_heads) * head_dim;
+  if (row_elems % 8 != 0) return PA_ERR_UNSUPPORTED;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return PA_ERR_UNSUPPORTED;
+  hipError_t e = pa::launch_store_kv_fp8(
+      k, v, k_cache, v_cache, slot_mapping, num_tokens, row_elems, num_slots,
+      src_dtype == PA_BF16, 1.0f / k_scale, 1.0f / v_scale,
+      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status pa_decode_fp8(void* out, const void* q, const void* k_cache,
+                        const void* v_cache, int64_t num_blocks,
+                        int32_t block_size, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const int32_t* context_lens,
+                        int32_t max_context_len, int32_t num_seqs,
+                        int32_t num_heads, int32_t num_kv_heads,
+                        int32_t head_dim, float scale, float k_scale,
+                        float v_scale, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  pa_status st = check_attention(block_size, num_seqs, num_heads, num_kv_heads,
+                                 head_dim, max_blocks_per_seq, num_blocks,
+                                 PA_BF16);
+  if (st != PA_OK) return st;
+  if (head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (max_context_len < 0) return PA_ERR_SHAPE;
+  if (!(scale > 0.f) || !std::isfinite(scale) || !(k_scale > 0.f) ||
+      !std::isfinite(k_scale) || !(v_scale > 0.f) || !std::isfinite(v_scale))
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !context_lens) return PA_ERR_NULL;
+  if (max_context_len > 0 && (!k_cache || !v_cache || !block_tables))
+    return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return PA_ERR_UNSUPPORTED;
+  pa::DecodePlan plan = pa::plan_decode(num_seqs, num_heads, num_kv_heads,
+                                        head_dim, max_context_len);
+  if (plan.workspace_bytes > 0 &&
+      (!workspace || workspace_bytes < plan.workspace_bytes))
+    return PA_ERR_WORKSPACE;
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_blocks = num_blocks;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.max_context_len = max_context_len;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.scale = scale;
+  a.workspace = workspace;
+  a.bf16 = true;
+  a.fp8_cache = true;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  hipError_t e = pa::launch_decode(a, plan, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -88,10 +88,15 @@ struct BlockLayout {
   static_assert(kLpr * 16 >= 128, "whole cache lines per instruction");
 };
 
-template <typename T, int D, int G, int C>
+// F8: the cache holds E4M3 codes (one byte per element) and q / out are
+// bfloat16.  The kernel then runs the bfloat16 layout on a virtual bf16 row
+// (kRow): each lane loads the codes of its virtual chunks (8 codes per
+// 16-byte virtual chunk) and widens them to bfloat16 right before use.
+template <typename T, int D, int G, int C, bool F8 = false>
 struct DecodeShape {
   static constexpr int kElem = ElemTraits<T>::kBytes;
-  static constexpr int kRow = D * kElem;          // bytes of one (token, KV head)
+  static constexpr int kRow = D * kElem;          // bytes of one (token, KV head) as T
+  static constexpr int kCacheRow = F8 ? D : kRow; // bytes of it in the cache
   static constexpr int kEpc = 16 / kElem;         // elements per 16-byte chunk
   static constexpr int kBlocks = C / kBlock;      // blocks per chunk
   using K = BlockLayout<kRow, 8>;    // QK: 8 lanes per row, short reductions
@@ -110,7 +115,8 @@ struct DecodeShape {
   // while the current one is consumed.  Deeper prefetch was measured and
   // gains nothing.
   static constexpr int kDepth = 2;
-  static_assert(kRow % 128 == 0, "rows must be whole 128-byte lines");
+  static_assert(kCacheRow % 128 == 0, "rows must be whole 128-byte lines");
+  static_assert(!F8 || sizeof(T) == 2, "E4M3 cache with bfloat16 q / out");
   static_assert(C % (kBlock * kWaves) == 0, "chunk shape");
 };
 
@@ -222,6 +228,7 @@ struct DecodeParams {
   int prefix_chunk_tokens;
   int prefix_chunks;     // prefix slots per (sequence, head)
   int force_partials;    // write partials even with one partition
+  float v_scale;         // output factor (E4M3 cache: V = code * v_scale)
 };
 
 // First token of the partitions: 0, or the block-aligned shared prefix.
@@ -257,12 +264,30 @@ __device__ __forceinline__ uint4 buf_ld16_nt(__amdgpu_buffer_rsrc_t r,
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <typename T, int D, int G, int C>
+__device__ __forceinline__ uint2 buf_ld8_nt(__amdgpu_buffer_rsrc_t r,
+                                            uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCacheNT);
+  return make_uint2(v[0], v[1]);
+}
+
+// Eight E4M3 codes (bytes of lo, then hi) -> eight bfloat16 (exact; E4M3
+// values are a subset of bfloat16's).
+template <bool kHigh>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHigh));
+}
+__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  return make_uint4(e4m3x2_to_bf16<false>(lo), e4m3x2_to_bf16<true>(lo),
+                    e4m3x2_to_bf16<false>(hi), e4m3x2_to_bf16<true>(hi));
+}
+
+template <typename T, int D, int G, int C, bool F8>
 __global__ __launch_bounds__(kThreads) __attribute__((
-    amdgpu_waves_per_eu(DecodeShape<T, D, G, C>::kMinWaves, 8))) void
+    amdgpu_waves_per_eu(DecodeShape<T, D, G, C, F8>::kMinWaves, 8))) void
 decode_partition_kernel(
     DecodeParams p) {
-  using S = DecodeShape<T, D, G, C>;
+  using S = DecodeShape<T, D, G, C, F8>;
   using KL = typename S::K;
   using VL = typename S::V;
   constexpr int kSteps = S::kBlocks / kWaves;  // blocks per wave per chunk
@@ -293,7 +318,7 @@ decode_partition_kernel(
   const int len = clamp_len(p, b);
   const int t0 = suffix_start(p, b, len) + part * p.partition_tokens;
   const int head0 = kvh * G;
-  const int row_stride = p.num_kv_heads * S::kRow;   // bytes per slot
+  const int row_stride = p.num_kv_heads * S::kCacheRow;   // bytes per slot
   const int64_t blk_bytes = static_cast<int64_t>(kBlock) * row_stride;
 
   if (t0 >= len) {
@@ -343,13 +368,17 @@ decode_partition_kernel(
     // chunks cc * KL::kLpr + ke of its row.
     const int krs = ln / KL::kLpr;
     const int ke = ln % KL::kLpr;
+    // (F8: lane ke's virtual chunks are ke * kCpl + cc, whose codes are
+    // one contiguous 8 * kCpl-byte piece of the row.)
     uint32_t koff[KL::kTpl][KL::kCpl];
 #pragma unroll
     for (int i = 0; i < KL::kTpl; ++i)
 #pragma unroll
       for (int cc = 0; cc < KL::kCpl; ++cc)
-        koff[i][cc] = (i * KL::kRpi + krs) * row_stride + kvh * S::kRow +
-                      (cc * KL::kLpr + ke) * 16;
+        koff[i][cc] = F8 ? (i * KL::kRpi + krs) * row_stride + kvh * S::kCacheRow +
+                               ke * (8 * KL::kCpl)
+                         : (i * KL::kRpi + krs) * row_stride + kvh * S::kRow +
+                               (cc * KL::kLpr + ke) * 16;
     // Lane (vrs, ve) of the PV layout.
     const int vrs = ln / VL::kLpr;
     const int ve = ln % VL::kLpr;
@@ -358,8 +387,10 @@ decode_partition_kernel(
     for (int i = 0; i < VL::kTpl; ++i)
 #pragma unroll
       for (int cc = 0; cc < VL::kCpl; ++cc)
-        voff[i][cc] = (i * VL::kRpi + vrs) * row_stride + kvh * S::kRow +
-                      (cc * VL::kLpr + ve) * 16;
+        voff[i][cc] = F8 ? (i * VL::kRpi + vrs) * row_stride + kvh * S::kCacheRow +
+                               (cc * VL::kLpr + ve) * 8
+                         : (i * VL::kRpi + vrs) * row_stride + kvh * S::kRow +
+                               (cc * VL::kLpr + ve) * 16;
 
     // q of the group's heads, in the QK lane layout.  Loaded again for every
     // chunk (the lines stay in cache) rather than held across the chunk
@@ -372,7 +403,8 @@ decode_partition_kernel(
       for (int cc = 0; cc < KL::kCpl; ++cc)
 #pragma unroll
         for (int h = 0; h < G; ++h)
-          qreg[cc][h] = ld16(qbase + h * S::kRow + (cc * KL::kLpr + ke) * 16);
+          qreg[cc][h] = ld16(qbase + h * S::kRow +
+                             (F8 ? ke * KL::kCpl + cc : cc * KL::kLpr + ke) * 16);
     }
 
     // Step s of a wave covers block j = wave + s * kWaves of the chunk.  One
@@ -399,12 +431,27 @@ decode_partition_kernel(
 
     // ---- pass 1: logits ---------------------------------------------------
     uint4 kr[kSteps][KL::kTpl][KL::kCpl];
+    uint4 kr8[kSteps][KL::kTpl];          // F8: the codes of both chunks
+    static_assert(!F8 || KL::kCpl == 2, "E4M3 K: two virtual chunks per lane");
     auto load_k = [&](int s) {
       const auto r = rsrc(p.k_cache, s);
 #pragma unroll
-      for (int i = 0; i < KL::kTpl; ++i)
+      for (int i = 0; i < KL::kTpl; ++i) {
+        if constexpr (F8) {
+          kr8[s][i] = buf_ld16_nt(r, koff[i][0]);
+        } else {
 #pragma unroll
-        for (int cc = 0; cc < KL::kCpl; ++cc) kr[s][i][cc] = buf_ld16_nt(r, koff[i][cc]);
+          for (int cc = 0; cc < KL::kCpl; ++cc) kr[s][i][cc] = buf_ld16_nt(r, koff[i][cc]);
+        }
+      }
+    };
+    auto k_chunk = [&](int s, int i, int cc) __attribute__((always_inline)) {
+      if constexpr (F8) {
+        return cc == 0 ? e4m3x8_to_bf16(kr8[s][i].x, kr8[s][i].y)
+                       : e4m3x8_to_bf16(kr8[s][i].z, kr8[s][i].w);
+      } else {
+        return kr[s][i][cc];
+      }
     };
     float mloc[G];
 #pragma unroll
@@ -418,7 +465,7 @@ decode_partition_kernel(
 #pragma unroll
         for (int h = 0; h < G; ++h) sc[h] = 0.f;
 #pragma unroll
-        for (int cc = 0; cc < KL::kCpl; ++cc) ChunkDot<T, G>::run(kr[s][i][cc], qreg[cc], sc);
+        for (int cc = 0; cc < KL::kCpl; ++cc) ChunkDot<T, G>::run(k_chunk(s, i, cc), qreg[cc], sc);
 #pragma unroll
         for (int h = 0; h < G; ++h) sc[h] = row_sum<KL::kLpr>(sc[h]) * p.scale_log2;
         const int tb = i * KL::kRpi + krs;     // token inside the block
@@ -451,12 +498,27 @@ decode_partition_kernel(
 
     // ---- first V blocks in flight; softmax over the chunk -----------------
     uint4 vr[kSteps][VL::kTpl][VL::kCpl];
+    uint2 vr8[kSteps][VL::kTpl];          // F8: the codes of the chunk
+    static_assert(!F8 || VL::kCpl == 1, "E4M3 V: one virtual chunk per lane");
     auto load_v = [&](int s) {
       const auto r = rsrc(p.v_cache, s);
 #pragma unroll
-      for (int i = 0; i < VL::kTpl; ++i)
+      for (int i = 0; i < VL::kTpl; ++i) {
+        if constexpr (F8) {
+          vr8[s][i] = buf_ld8_nt(r, voff[i][0]);
+        } else {
 #pragma unroll
-        for (int cc = 0; cc < VL::kCpl; ++cc) vr[s][i][cc] = buf_ld16_nt(r, voff[i][cc]);
+          for (int cc = 0; cc < VL::kCpl; ++cc) vr[s][i][cc] = buf_ld16_nt(r, voff[i][cc]);
+        }
+      }
+    };
+    auto v_chunk = [&](int s, int i, int cc) __attribute__((always_inline)) {
+      if constexpr (F8) {
+        (void)cc;
+        return e4m3x8_to_bf16(vr8[s][i].x, vr8[s][i].y);
+      } else {
+        return vr[s][i][cc];
+      }
     };
 #pragma unroll
     for (int s = 0; s < kDepth - 1 && s < kSteps; ++s) load_v(s);
@@ -551,8 +613,8 @@ decode_partition_kernel(
           for (int h = 0; h < G; ++h) wp[h] = s_wp[(j * S::kPairsPerBlock + q) * G + h];
 #pragma unroll
           for (int cc = 0; cc < VL::kCpl; ++cc) {
-            const uint4 x = vr[s][2 * pi][cc];
-            const uint4 y = vr[s][2 * pi + 1][cc];
+            const uint4 x = v_chunk(s, 2 * pi, cc);
+            const uint4 y = v_chunk(s, 2 * pi + 1, cc);
             const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
             const uint32_t ys[4] = {y.x, y.y, y.z, y.w};
 #pragma unroll
@@ -577,7 +639,7 @@ decode_partition_kernel(
 #pragma unroll
           for (int cc = 0; cc < VL::kCpl; ++cc) {
             float v[S::kEpc];
-            Widen<T>::run(vr[s][i][cc], v);
+            Widen<T>::run(v_chunk(s, i, cc), v);
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -637,7 +699,7 @@ decode_partition_kernel(
     if (single) {
       const float l = s_lrun[h];
       T* out = reinterpret_cast<T*>(p.out) + head * D + d;
-      store_out<T>(out, l > 0.f ? o / l : 0.f);
+      store_out<T>(out, l > 0.f ? o / l * p.v_scale : 0.f);
     } else {
       const int64_t slot = head * p.ws_stride + part;
       p.ws_acc[slot * D + d] = o;
@@ -688,16 +750,16 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
     l = fmaf(w, sm[k], l);
     o = fmaf(w, ac[static_cast<int64_t>(k) * D], o);
   }
-  store_out<T>(out, l > 0.f ? o / l : 0.f);
+  store_out<T>(out, l > 0.f ? o / l * p.v_scale : 0.f);
 }
 
-template <typename T, int D, int G, int C>
+template <typename T, int D, int G, int C, bool F8>
 hipError_t launch_typed(const DecodeParams& prm, int num_seqs, int num_kv_heads,
                         int num_heads, hipStream_t stream) {
   const int64_t wgs = static_cast<int64_t>(prm.num_partitions) * num_kv_heads * num_seqs;
   if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
   dim3 grid(static_cast<unsigned>(wgs));
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, G, C>), grid,
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, G, C, F8>), grid,
                      dim3(kThreads), 0, stream, prm);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || (prm.num_partitions == 1 && !prm.force_partials)) return e;
@@ -706,14 +768,14 @@ hipError_t launch_typed(const DecodeParams& prm, int num_seqs, int num_kv_heads,
   return hipGetLastError();
 }
 
-template <typename T, int D, int C>
+template <typename T, int D, int C, bool F8 = false>
 hipError_t dispatch_group(const DecodeParams& prm, int num_seqs,
                           int num_kv_heads, int num_heads, hipStream_t s) {
   switch (num_heads / num_kv_heads) {
-    case 1: return launch_typed<T, D, 1, C>(prm, num_seqs, num_kv_heads, num_heads, s);
-    case 2: return launch_typed<T, D, 2, C>(prm, num_seqs, num_kv_heads, num_heads, s);
-    case 4: return launch_typed<T, D, 4, C>(prm, num_seqs, num_kv_heads, num_heads, s);
-    case 8: return launch_typed<T, D, 8, C>(prm, num_seqs, num_kv_heads, num_heads, s);
+    case 1: return launch_typed<T, D, 1, C, F8>(prm, num_seqs, num_kv_heads, num_heads, s);
+    case 2: return launch_typed<T, D, 2, C, F8>(prm, num_seqs, num_kv_heads, num_heads, s);
+    case 4: return launch_typed<T, D, 4, C, F8>(prm, num_seqs, num_kv_heads, num_heads, s);
+    case 8: return launch_typed<T, D, 8, C, F8>(prm, num_seqs, num_kv_heads, num_heads, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -742,6 +804,10 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 hipError_t dispatch_decode(const DecodeParams& prm, const DecodeArgs& a,
                            hipStream_t stream) {
   constexpr int P = kChunkTokens;
+  if (a.fp8_cache) {   // E4M3 cache, bf16 q / out, head_dim 128 (checked by the caller)
+    return dispatch_group<bf16_t, 128, P, true>(prm, a.num_seqs, a.num_kv_heads,
+                                                a.num_heads, stream);
+  }
   if (a.bf16) {
     if (a.head_dim == 128)
       return dispatch_group<bf16_t, 128, P>(prm, a.num_seqs, a.num_kv_heads, a.num_heads, stream);
@@ -834,7 +900,8 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan,
   prm.num_seqs = a.num_seqs;
   prm.num_heads = a.num_heads;
   prm.num_kv_heads = a.num_kv_heads;
-  prm.scale_log2 = a.scale * kLog2e;
+  prm.scale_log2 = a.scale * a.k_scale * kLog2e;
+  prm.v_scale = a.v_scale;
   prm.num_partitions = plan.num_partitions;
   prm.partition_tokens = plan.partition_tokens;
   prm.ws_stride = plan.num_partitions;
@@ -862,7 +929,8 @@ hipError_t launch_decode_suffix(const DecodeArgs& a, const SharedPrefixPlan& pla
   prm.num_seqs = a.num_seqs;
   prm.num_heads = a.num_heads;
   prm.num_kv_heads = a.num_kv_heads;
-  prm.scale_log2 = a.scale * kLog2e;
+  prm.scale_log2 = a.scale * a.k_scale * kLog2e;
+  prm.v_scale = a.v_scale;
   prm.num_partitions = plan.suffix.num_partitions;
   prm.partition_tokens = plan.suffix.partition_tokens;
   prm.ws_stride = plan.total_slots;

@@ -14,6 +14,16 @@ hipError_t launch_store_kv(const void* k, const void* v, void* k_cache,
                            int64_t num_tokens, int64_t row_bytes,
                            int64_t num_slots, hipStream_t stream);
 
+// Quantising store into E4M3 caches: row t (num_kv_heads * head_dim
+// elements of bf16 or fp32) goes to flat slot slot_mapping[t] as the codes
+// of x * inv_scale (per cache), saturated to +-448.
+hipError_t launch_store_kv_fp8(const void* k, const void* v, void* k_cache,
+                               void* v_cache, const int32_t* slot_mapping,
+                               int64_t num_tokens, int64_t row_elems,
+                               int64_t num_slots, bool bf16_src,
+                               float k_inv_scale, float v_inv_scale,
+                               hipStream_t stream);
+
 // ---- block copy (copy-on-write) -----------------------------------------
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache,
                               const int32_t* block_pairs, int64_t num_pairs,
@@ -49,6 +59,10 @@ struct DecodeArgs {
   void* workspace;
   bool bf16;
   const int32_t* prefix_lens = nullptr;   // shared-prefix decode only
+  // E4M3 cache (q / out bf16): K = code * k_scale, V = code * v_scale.
+  bool fp8_cache = false;
+  float k_scale = 1.f;
+  float v_scale = 1.f;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan,

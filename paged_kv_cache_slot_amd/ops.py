@@ -194,6 +194,65 @@ def decode_shared_prefix(q, k_cache, v_cache, block_tables, context_lens,
     return out
 
 
+def store_kv_fp8(k, v, k_cache, v_cache, slot_mapping, k_scale, v_scale):
+    """Quantise rows of k / v ([T, Hkv, D], bf16 or fp32) into 8-bit E4M3
+    caches (uint8 [NB, bs, Hkv, D]) at flat slots; negative slots skipped.
+    Each element is stored as the code of x / scale (per cache)."""
+    _need_gpu(k, v, k_cache, v_cache, slot_mapping)
+    _i32(slot_mapping, "slot_mapping")
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise TypeError("8-bit caches must be uint8 tensors of E4M3 codes")
+    t, hkv, d = k.shape
+    nb, bs, hkv2, d2 = k_cache.shape
+    if (hkv2, d2) != (hkv, d) or v_cache.shape != k_cache.shape or \
+            v.shape != k.shape or slot_mapping.numel() != t:
+        raise ValueError("shapes of rows, caches and slot_mapping disagree")
+    lib = _lib.load()
+    st = lib.pa_store_kv_fp8(_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache),
+                             _ptr(slot_mapping), t, hkv, d, nb * bs,
+                             _dtype_code(k), float(k_scale), float(v_scale),
+                             _stream(k))
+    _lib.check("pa_store_kv_fp8", st)
+
+
+def decode_fp8(q, k_cache, v_cache, block_tables, context_lens,
+               max_context_len, k_scale, v_scale, scale=None, out=None,
+               workspace=None):
+    """Paged decode over 8-bit E4M3 caches (uint8 [NB, 16, Hkv, 128]):
+    K = code * k_scale, V = code * v_scale; q and out bf16 [B, Hq, 128]."""
+    _need_gpu(q, k_cache, v_cache, block_tables, context_lens, out, workspace)
+    _i32(block_tables, "block_tables")
+    _i32(context_lens, "context_lens")
+    if q.dtype != torch.bfloat16:
+        raise TypeError("decode over an 8-bit cache takes bf16 q")
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise TypeError("8-bit caches must be uint8 tensors of E4M3 codes")
+    b, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if d2 != d or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shape does not match q")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b:
+        raise ValueError("block_tables must be [B, W]")
+    if context_lens.numel() != b:
+        raise ValueError("context_lens must be [B]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    need = decode_workspace_bytes(b, hq, hkv, d, max_context_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() \
+        if workspace is not None else 0
+    lib = _lib.load()
+    st = lib.pa_decode_fp8(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                           nb, bs, _ptr(block_tables), block_tables.shape[1],
+                           _ptr(context_lens), int(max_context_len), b, hq,
+                           hkv, d, scale, float(k_scale), float(v_scale),
+                           _ptr(workspace), ws_bytes, _stream(q))
+    _lib.check("pa_decode_fp8", st)
+    return out
+
+
 def prefill_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
                             max_seqlen_q, max_seqlen_k):
     return int(_lib.load().pa_prefill_workspace_bytes(

@@ -38,7 +38,7 @@ def no_device():
 def declared_symbols():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_symbols_exported():
@@ -203,3 +203,44 @@ def test_shared_prefix_workspace_query():
     assert q(4, 8, 2, 64, 100, 0, 0, 0) >= 4 * 8 * (64 + 2) * 4
     assert q(0, 8, 2, 64, 100, 0, 0, 0) == 0
     assert q(4, 8, 2, 64, -1, 0, 0, 0) == 0
+
+
+def _store8(lib, **kw):
+    a = dict(k=FAKE, v=FAKE, kc=FAKE, vc=FAKE, sm=FAKE, t=4, hkv=2, d=64,
+             s=1024, dtype=_lib.PA_BF16, ks=0.5, vs=0.25, stream=None)
+    a.update(kw)
+    return lib.pa_store_kv_fp8(a["k"], a["v"], a["kc"], a["vc"], a["sm"],
+                               a["t"], a["hkv"], a["d"], a["s"], a["dtype"],
+                               a["ks"], a["vs"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(t=-1), 2), (dict(hkv=0), 2), (dict(s=-1), 2), (dict(ks=0.0), 2),
+    (dict(vs=-1.0), 2), (dict(ks=float("inf")), 2), (dict(vs=float("nan")), 2),
+    (dict(dtype=2), 3), (dict(k=None), 1), (dict(sm=None), 1),
+    (dict(vc=MISALIGNED), 3), (dict(hkv=1, d=4), 3), (dict(t=0), 0),
+])
+def test_store_fp8_validation(kw, code, no_device):
+    assert _store8(_lib.load(), **kw) == code
+
+
+def _decode8(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, nb=64, bs=16, bt=FAKE, w=8,
+             cl=FAKE, maxlen=100, b=4, hq=8, hkv=2, d=128, scale=0.125,
+             ks=0.5, vs=0.25, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.pa_decode_fp8(a["out"], a["q"], a["k"], a["v"], a["nb"],
+                             a["bs"], a["bt"], a["w"], a["cl"], a["maxlen"],
+                             a["b"], a["hq"], a["hkv"], a["d"], a["scale"],
+                             a["ks"], a["vs"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=64), 3), (dict(d=96), 3), (dict(bs=32), 3), (dict(hq=6, hkv=2), 3),
+    (dict(b=-1), 2), (dict(maxlen=-1), 2), (dict(scale=0.0), 2),
+    (dict(ks=0.0), 2), (dict(vs=float("inf")), 2), (dict(out=None), 1),
+    (dict(cl=None), 1), (dict(bt=None), 1), (dict(k=MISALIGNED), 3),
+    (dict(maxlen=4096), 4), (dict(b=0), 0),
+])
+def test_decode_fp8_validation(kw, code, no_device):
+    assert _decode8(_lib.load(), **kw) == code

@@ -23,4 +23,5 @@ from .layout import (  # noqa: F401
 )
 from .values import (  # noqa: F401
     make_values, fill_pool, poison_unused, host_bits, torch_dtype,
+    make_codes, fill_pool_codes,
 )
