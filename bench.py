@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--prefix-steps", type=int, default=20,
                     help="timed steps of the prefix-sharing decode workload "
                          "(0 skips it)")
+    ap.add_argument("--fp8-steps", type=int, default=20,
+                    help="timed steps of the 8B-shaped decode step over an "
+                         "8-bit (E4M3) cache (0 skips it)")
     ap.add_argument("--flush-mb", type=int, default=512,
                     help="MiB read between timed steps (outside the timed "
                          "events) so that no step reads the previous step's "
@@ -339,6 +342,72 @@ def run_prefix(steps, warmup, dev, flush):
     }
 
 
+def run_fp8(steps, warmup, dev, flush):
+    """The 8B-shaped decode step over an 8-bit (E4M3) cache: pa_store_kv_fp8
+    of the 256 new rows, then pa_decode_fp8.  Bytes count one byte per
+    cached element."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from paged_kv_cache_slot_amd import metadata as pm
+    from paged_kv_cache_slot_amd import ops
+
+    cfg = wl.get_config(WORKLOAD)
+    lay = wl.config_decode_layout(cfg)
+    hq, hkv, d, bs = cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, 16
+    b = len(lay.lens)
+    kc, vc = wl.fill_pool_codes(lay.num_blocks, bs, hkv, d, cfg.seed, dev)
+    q = wl.make_values((b, hq, d), "bf16", cfg.seed + 1, dev)
+    k_new = wl.make_values((b, hkv, d), "bf16", cfg.seed + 2, dev)
+    v_new = wl.make_values((b, hkv, d), "bf16", cfg.seed + 3, dev)
+    meta = pm.decode_inputs(lay.tables, lay.lens, bs)
+    slot = torch.as_tensor(meta["slot_mapping"], device=dev)
+    bt = torch.as_tensor(meta["block_tables"], device=dev)
+    cl = torch.as_tensor(meta["context_lens"], device=dev)
+    maxlen = meta["max_context_len"]
+    out = torch.empty_like(q)
+    ws = torch.empty(max(ops.decode_workspace_bytes(b, hq, hkv, d, maxlen), 1),
+                     dtype=torch.uint8, device=dev)
+    ks, vs = 1 / 16, 1 / 16
+
+    def step(ev):
+        ev[0].record()
+        ops.store_kv_fp8(k_new, v_new, kc, vc, slot, ks, vs)
+        ev[1].record()
+        ops.decode_fp8(q, kc, vc, bt, cl, maxlen, ks, vs, out=out,
+                       workspace=ws)
+        ev[2].record()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+           for _ in range(steps + warmup)]
+    for i in range(warmup):
+        step(evs[steps + i])
+    torch.cuda.synchronize()
+    for i in range(steps):
+        flush()
+        step(evs[i])
+    torch.cuda.synchronize()
+    dec_all = [e[1].elapsed_time(e[2]) for e in evs[:steps]]
+    step_all = [e[0].elapsed_time(e[2]) for e in evs[:steps]]
+    dec = float(np.median(dec_all))
+    stp = float(np.median(step_all))
+    dbytes = decode_bytes(lay.lens, hq, hkv, d, 1) + \
+        len(lay.lens) * hq * d * (2 - 1) * 2      # q and out stay bf16
+    return {
+        "workload": cfg.title + "; 8-bit E4M3 cache",
+        "steps": steps,
+        "decode_us": round(dec * 1e3, 2),
+        "step_us": round(stp * 1e3, 2),
+        "decode_ms_stats": stats_ms(dec_all),
+        "algorithmic_bytes": dbytes,
+        "decode_tbs": round(dbytes / (dec * 1e-3) / 1e12, 4),
+        "frac_of_hbm_peak": round(dbytes / (dec * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(b / (stp * 1e-3), 1),
+        "kernel": "pa_decode_fp8 (decode_partition_kernel<..., E4M3> + merge)",
+    }
+
+
 def cpu_baseline(case_tables, lens, h_q, h_kc, h_vc, hq, scale, budget_s):
     """Time the oracle on whole sequences until ~budget_s seconds pass."""
     import numpy as np
@@ -468,6 +537,11 @@ def main():
     if args.prefix_steps > 0:
         prefix = run_prefix(args.prefix_steps, max(2, args.warmup // 2), dev,
                             flush)
+        torch.cuda.empty_cache()
+    fp8 = None
+    if args.fp8_steps > 0:
+        fp8 = run_fp8(args.fp8_steps, max(2, args.warmup // 2), dev, flush)
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -516,6 +590,7 @@ def main():
         "cpu_baseline": cpu,
         "mixed_step": mixed,
         "prefix_step": prefix,
+        "fp8_step": fp8,
         "wall_s_timed": round(wall, 3),
     }
     print(json.dumps(line), flush=True)
