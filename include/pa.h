@@ -138,7 +138,11 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache,
 
 /*
  * Bytes of workspace pa_decode needs for these sizes (0 when one context
- * partition covers max_context_len and no merge pass is needed).
+ * partition covers max_context_len and no merge pass is needed).  The
+ * workspace holds the partitions' partial results and, for large grids, a
+ * longest-first work order that a one-workgroup plan kernel writes at the
+ * start of each call (every call rewrites it, so calls that share a
+ * workspace on one stream are safe).
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads,
                                  int32_t num_kv_heads, int32_t head_dim,

@@ -229,6 +229,9 @@ struct DecodeParams {
   int prefix_chunks;     // prefix slots per (sequence, head)
   int force_partials;    // write partials even with one partition
   float v_scale;         // output factor (E4M3 cache: V = code * v_scale)
+  // Longest-first schedule (null: natural order): entry r is the (part *
+  // num_seqs + b) item workgroups r * Hkv .. r * Hkv + Hkv - 1 take.
+  const int32_t* order;
 };
 
 // First token of the partitions: 0, or the block-aligned shared prefix.
@@ -307,7 +310,11 @@ decode_partition_kernel(
   // the mostly empty last ones to another), and the full early partitions
   // are dispatched before the sparse late ones.
   const int kvh = blockIdx.x % p.num_kv_heads;
-  const int rest = blockIdx.x / p.num_kv_heads;
+  int rest = blockIdx.x / p.num_kv_heads;
+  if (p.order != nullptr) {
+    rest = load_uniform_i32(p.order, rest);
+    if (rest < 0 || rest >= p.num_seqs * p.num_partitions) return;   // uniform
+  }
   const int b = rest % p.num_seqs;
   const int part = rest / p.num_seqs;
   const int tid = threadIdx.x;
@@ -753,12 +760,76 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
   store_out<T>(out, l > 0.f ? o / l * p.v_scale : 0.f);
 }
 
+// Longest-first schedule of the (sequence, partition) items: one workgroup
+// counts the items per token count (in 16-token bins, the last bin shared
+// by everything longer), then writes them longest first.  With contexts of
+// mixed lengths the partial and empty partitions otherwise start last and
+// leave the tail of the grid to a few long ones.  Items of equal weight
+// land in any order; the results do not depend on the schedule.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBins = 1024;
+constexpr int kBinsPerThread = kPlanBins / kPlanThreads;
+
+__device__ __forceinline__ int plan_bin(const DecodeParams& p, int item) {
+  const int b = item % p.num_seqs;
+  const int part = item / p.num_seqs;
+  const int len = clamp_len(p, b);
+  int n = len - suffix_start(p, b, len) - part * p.partition_tokens;
+  n = n < 0 ? 0 : (n > p.partition_tokens ? p.partition_tokens : n);
+  const int bin = (n + kBlock - 1) / kBlock;
+  return bin < kPlanBins ? bin : kPlanBins - 1;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(
+    DecodeParams p, int32_t* __restrict__ order) {
+  __shared__ int bins[kPlanBins];
+  __shared__ int part_sum[kPlanThreads];
+  const int tid = threadIdx.x;
+  const int n = p.num_seqs * p.num_partitions;
+  for (int i = tid; i < kPlanBins; i += kPlanThreads) bins[i] = 0;
+  __syncthreads();
+  for (int item = tid; item < n; item += kPlanThreads)
+    atomicAdd(&bins[plan_bin(p, item)], 1);
+  __syncthreads();
+  // Exclusive prefix from the heaviest bin down.
+  int cnt[kBinsPerThread];
+  int mine = 0;
+#pragma unroll
+  for (int k = 0; k < kBinsPerThread; ++k) {
+    cnt[k] = bins[kPlanBins - 1 - (kBinsPerThread * tid + k)];
+    mine += cnt[k];
+  }
+  part_sum[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off *= 2) {
+    const int add = tid >= off ? part_sum[tid - off] : 0;
+    __syncthreads();
+    part_sum[tid] += add;
+    __syncthreads();
+  }
+  int start = part_sum[tid] - mine;
+#pragma unroll
+  for (int k = 0; k < kBinsPerThread; ++k) {
+    bins[kPlanBins - 1 - (kBinsPerThread * tid + k)] = start;
+    start += cnt[k];
+  }
+  __syncthreads();
+  for (int item = tid; item < n; item += kPlanThreads)
+    order[atomicAdd(&bins[plan_bin(p, item)], 1)] = item;
+}
+
 template <typename T, int D, int G, int C, bool F8>
 hipError_t launch_typed(const DecodeParams& prm, int num_seqs, int num_kv_heads,
                         int num_heads, hipStream_t stream) {
   const int64_t wgs = static_cast<int64_t>(prm.num_partitions) * num_kv_heads * num_seqs;
   if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
   dim3 grid(static_cast<unsigned>(wgs));
+  if (prm.order != nullptr) {
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream,
+                       prm, const_cast<int32_t*>(prm.order));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((decode_partition_kernel<T, D, G, C, F8>), grid,
                      dim3(kThreads), 0, stream, prm);
   hipError_t e = hipGetLastError();
@@ -800,6 +871,22 @@ constexpr int kMaxChunksPerPartition = 16;
 constexpr int64_t kPrefixTargetWorkgroups = PA_PREFIX_TARGET_WGS;
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// The longest-first schedule pays for its plan kernel (a few microseconds)
+// only on grids of several partitions and well over one wave of
+// workgroups.  Appends the order array to a multi-partition plan's
+// workspace; returns whether the plan uses one.
+constexpr int64_t kOrderMinWorkgroups = 4096;
+bool plan_order(DecodePlan& plan, int num_seqs, int num_kv_heads) {
+  const int64_t wgs = static_cast<int64_t>(num_seqs) * num_kv_heads * plan.num_partitions;
+  plan.use_order = plan.num_partitions > 1 && wgs >= kOrderMinWorkgroups;
+  if (plan.use_order && plan.workspace_bytes > 0) {
+    plan.off_order = plan.workspace_bytes;
+    plan.workspace_bytes += align256(static_cast<size_t>(num_seqs) *
+                                     plan.num_partitions * sizeof(int32_t));
+  }
+  return plan.use_order;
+}
 
 hipError_t dispatch_decode(const DecodeParams& prm, const DecodeArgs& a,
                            hipStream_t stream) {
@@ -849,6 +936,7 @@ DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads,
   plan.off_acc = plan.off_sum + align256(slots * sizeof(float));
   plan.workspace_bytes =
       plan.off_acc + align256(slots * static_cast<size_t>(head_dim) * sizeof(float));
+  plan_order(plan, num_seqs, num_kv_heads);
   return plan;
 }
 
@@ -882,6 +970,13 @@ SharedPrefixPlan plan_shared_prefix(int num_seqs, int num_heads,
   plan.off_acc = plan.off_sum + align256(slots * sizeof(float));
   plan.workspace_bytes =
       plan.off_acc + align256(slots * static_cast<size_t>(head_dim) * sizeof(float));
+  plan.suffix.off_order = 0;
+  plan.suffix.use_order = false;
+  if (plan_order(plan.suffix, num_seqs, num_kv_heads)) {
+    plan.suffix.off_order = plan.workspace_bytes;
+    plan.workspace_bytes += align256(static_cast<size_t>(num_seqs) *
+                                     plan.suffix.num_partitions * sizeof(int32_t));
+  }
   return plan;
 }
 
@@ -910,6 +1005,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan,
     prm.ws_max = reinterpret_cast<float*>(ws + plan.off_max);
     prm.ws_sum = reinterpret_cast<float*>(ws + plan.off_sum);
     prm.ws_acc = reinterpret_cast<float*>(ws + plan.off_acc);
+    if (plan.use_order) prm.order = reinterpret_cast<int32_t*>(ws + plan.off_order);
   }
   return dispatch_decode(prm, a, stream);
 }
@@ -942,6 +1038,8 @@ hipError_t launch_decode_suffix(const DecodeArgs& a, const SharedPrefixPlan& pla
   prm.ws_max = reinterpret_cast<float*>(ws + plan.off_max);
   prm.ws_sum = reinterpret_cast<float*>(ws + plan.off_sum);
   prm.ws_acc = reinterpret_cast<float*>(ws + plan.off_acc);
+  if (plan.suffix.use_order)
+    prm.order = reinterpret_cast<int32_t*>(ws + plan.suffix.off_order);
   return dispatch_decode(prm, a, stream);
 }
 

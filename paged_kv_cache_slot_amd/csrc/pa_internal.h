@@ -36,6 +36,8 @@ struct DecodePlan {
   int num_partitions;    // ceil(max_context_len / partition_tokens), >= 1
   size_t workspace_bytes;
   size_t off_max, off_sum, off_acc;  // byte offsets inside the workspace
+  bool use_order;        // longest-first schedule of (sequence, partition)
+  size_t off_order;      // its int32 [num_seqs * num_partitions] array
 };
 
 DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads,

@@ -140,7 +140,10 @@ def _plan_partitions(lib, b, hq, hkv, d, maxlen):
     def size(np_):
         a = lambda x: (x + 255) // 256 * 256
         slots = b * hq * np_
-        return 2 * a(slots * 4) + a(slots * d * 4)
+        n = 2 * a(slots * 4) + a(slots * d * 4)
+        if np_ > 1 and b * hkv * np_ >= 4096:   # longest-first schedule
+            n += a(b * np_ * 4)
+        return n
     return [n for n in range(1, maxlen // 512 + 2) if size(n) == ws]
 
 
