@@ -193,9 +193,11 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache,
 
 /* Bytes of workspace pa_prefill_varlen needs for these sizes: the work
  * schedule, one int32 per (sequence, 128-row M-tile) item (0 when
- * max_seqlen_k is 0).  Written and read by each call; its contents between
- * calls mean nothing.  Calls that share a workspace on one stream are safe;
- * calls on different streams need their own. */
+ * max_seqlen_k is 0).  Written and read by each call when there are more
+ * work items than one attention workgroup has threads; with fewer, every
+ * workgroup ranks the items itself and the workspace is not touched.  Its
+ * contents between calls mean nothing.  Calls that share a workspace on
+ * one stream are safe; calls on different streams need their own. */
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads,
                                   int32_t num_kv_heads, int32_t head_dim,
                                   int32_t max_seqlen_q, int32_t max_seqlen_k);

@@ -128,7 +128,9 @@ struct PrefillShape {
 struct PrefillParams {
   int mtiles;                // M-tiles per (sequence, KV head)
   int num_seqs;
-  const int32_t* order;      // work items, heaviest first (null: natural order)
+  const int32_t* order;      // work items, heaviest first (null: see rank_inline)
+  int rank_inline;           // no order: 1 = each workgroup ranks the items
+                             // itself (at most one per thread), 0 = natural
   void* out;
   const char* q;
   int64_t total_q;
@@ -205,6 +207,19 @@ __device__ __forceinline__ int tile_key_end(const SeqExtent& e, int g, int m0,
   int kend = e.lk;
   if (causal) kend = min(e.lk, e.lk - e.lq + i_last + 1);
   return kend < 0 ? 0 : kend;
+}
+
+// Work of a (sequence, M-tile) item, the key of the longest-first order:
+// the key tiles it reads plus one for its fixed cost; 0 for an M-tile past
+// the sequence's rows.  Capped at kPlanBins - 1 (the plan kernel's bins).
+constexpr int kPlanBins = 4096;
+__device__ __forceinline__ int item_weight(const SeqExtent& e, int item,
+                                           int mtiles, int bm, int group,
+                                           int causal) {
+  const int m0 = (item % mtiles) * bm;
+  if (m0 >= e.lq * group) return 0;
+  const int w = (tile_key_end(e, group, m0, bm, causal) + kBN - 1) / kBN + 1;
+  return w < kPlanBins ? w : kPlanBins - 1;
 }
 
 template <int kChunks>
@@ -345,11 +360,47 @@ prefill_kernel(PrefillParams p) {
   const int lin = blockIdx.x;
   const int kvh = lin % p.num_kv_heads;
   const int rank = lin / p.num_kv_heads;
-  const int item = p.order ? load_uniform_i32(p.order, rank) : rank;
+  const int tid = threadIdx.x;
+  int item = rank;
+  if (p.order != nullptr) {
+    item = load_uniform_i32(p.order, rank);
+  } else if (p.rank_inline) {
+    // Few items (at most one per thread): the workgroup finds the item of
+    // rank `rank` itself, in the same order the plan kernel would give
+    // (heaviest first, equal weights by index), without that kernel's
+    // launch.  Scratch: the last V stage, which no DMA writes before the
+    // tile loop's first barrier.
+    int* s_w = reinterpret_cast<int*>(
+        smem + (2 * S::kStages - 1) * static_cast<size_t>(S::kTile));
+    int* s_item = s_w + S::kThreads;
+    const int n = p.num_seqs * p.mtiles;
+    const int n4 = (n + 3) & ~3;
+    int w = -1;
+    if (tid < n) {
+      const SeqExtent e = seq_extent(p.cu_q, p.cu_k, tid / p.mtiles, p.max_seqlen_q,
+                                     p.max_seqlen_k, p.total_q, p.max_blocks_per_seq);
+      w = item_weight(e, tid, p.mtiles, S::kBM, G, p.causal);
+    }
+    if (tid < n4) s_w[tid] = w;               // padding -1: lighter than any item
+    if (tid == 0) *s_item = -1;
+    __syncthreads();
+    if (tid < n) {
+      int r = 0;
+      for (int j = 0; j < n4; j += 4) {
+        const int4 x = *reinterpret_cast<const int4*>(s_w + j);
+        r += (x.x > w || (x.x == w && j < tid)) ? 1 : 0;
+        r += (x.y > w || (x.y == w && j + 1 < tid)) ? 1 : 0;
+        r += (x.z > w || (x.z == w && j + 2 < tid)) ? 1 : 0;
+        r += (x.w > w || (x.w == w && j + 3 < tid)) ? 1 : 0;
+      }
+      if (r == rank) *s_item = tid;
+    }
+    __syncthreads();
+    item = __builtin_amdgcn_readfirstlane(*s_item);
+  }
   if (item < 0 || item >= p.num_seqs * p.mtiles) return;   // uniform
   const int b = item / p.mtiles;
   const int mtile = item % p.mtiles;
-  const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
   const int j = lane % 32;                   // this lane's row inside the wave
@@ -739,7 +790,6 @@ prefill_kernel(PrefillParams p) {
 // the last bin share it).  Items of equal weight land in any order; the
 // attention results do not depend on the schedule.
 constexpr int kPlanThreads = 1024;
-constexpr int kPlanBins = 4096;
 constexpr int kBinsPerThread = kPlanBins / kPlanThreads;
 
 struct PlanParams {
@@ -757,14 +807,9 @@ struct PlanParams {
 };
 
 __device__ __forceinline__ int plan_bin(const PlanParams& q, int item) {
-  const int b = item / q.mtiles;
-  const int m0 = (item % q.mtiles) * q.bm;
-  const SeqExtent e = seq_extent(q.cu_q, q.cu_k, b, q.max_seqlen_q,
-                                 q.max_seqlen_k, q.total_q,
-                                 q.max_blocks_per_seq);
-  if (m0 >= e.lq * q.group) return 0;
-  const int w = (tile_key_end(e, q.group, m0, q.bm, q.causal) + kBN - 1) / kBN + 1;
-  return w < kPlanBins ? w : kPlanBins - 1;
+  const SeqExtent e = seq_extent(q.cu_q, q.cu_k, item / q.mtiles, q.max_seqlen_q,
+                                 q.max_seqlen_k, q.total_q, q.max_blocks_per_seq);
+  return item_weight(e, item, q.mtiles, q.bm, q.group, q.causal);
 }
 
 __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
@@ -842,8 +887,11 @@ hipError_t launch_typed(const PrefillParams& prm, const PrefillArgs& a,
   pr.mtiles = mtiles;
   pr.num_seqs = a.num_seqs;
   pr.order = nullptr;
-  if (a.workspace != nullptr &&
-      a.workspace_bytes >= static_cast<size_t>(items) * sizeof(int32_t)) {
+  pr.rank_inline = 0;
+  if (items <= S::kThreads) {
+    pr.rank_inline = 1;   // ranked inside the attention kernel
+  } else if (a.workspace != nullptr &&
+             a.workspace_bytes >= static_cast<size_t>(items) * sizeof(int32_t)) {
     PlanParams q{};
     q.cu_q = a.cu_seqlens_q;
     q.cu_k = a.cu_seqlens_k;
@@ -881,6 +929,7 @@ hipError_t launch_prefix_typed(const PrefillParams& prm, const PrefixArgs& a,
   if (items > 0x7fffffff || wgs > 0x7fffffff) return hipErrorNotSupported;
   pr.num_seqs = static_cast<int>(items);
   pr.order = nullptr;
+  pr.rank_inline = 0;
   pr.group_mode = 1;
   pr.chunk_tiles = plan.prefix_chunk_tokens / kBN;
   pr.chunks = plan.prefix_chunks;

@@ -174,10 +174,47 @@ def _item_weights(lq, lk, g, causal, bm=128, bn=64):
 
 @pytest.mark.parametrize("causal", [True, False])
 def test_longest_first_schedule(causal):
-    """The plan kernel's schedule in the workspace lists every (sequence,
-    M-tile) item once, by non-increasing work; the attention result with a
-    workspace filled with garbage beforehand is unchanged."""
-    say("prefill schedule", causal)
+    """More work items than one workgroup has threads (40 sequences x 16
+    M-tiles): the plan kernel writes the schedule into the workspace; it
+    lists every (sequence, M-tile) item once, by non-increasing work, and
+    the result with a workspace filled with garbage beforehand matches the
+    oracle."""
+    say("prefill schedule (plan kernel)", causal)
+    rng = np.random.default_rng(33)
+    hist = rng.integers(0, 300, 40).tolist()
+    chunk = rng.integers(1, 100, 40).tolist()
+    chunk[7], chunk[20] = 1024, 0
+    lay = wl.prefill_layout(hist, chunk, 16, seed=31)
+    case = PrefillCase(lay, 16, 4, 128, "bf16", seed=32, causal=causal)
+    m = case.meta
+    g, bm = 4, 256          # bf16 with D = 128: 8 waves x 32 rows per M-tile
+    mtiles = -(-m["max_seqlen_q"] * g // bm)
+    assert len(hist) * mtiles > 512
+    need = ops.prefill_workspace_bytes(len(hist), 16, 4, 128, m["max_seqlen_q"],
+                                       m["max_seqlen_k"])
+    ws = torch.full((need // 4,), -7, dtype=torch.int32, device="cuda")
+    case.run_store()
+    out = case.run_prefill(workspace=ws)
+    torch.cuda.synchronize()
+    ek, ev = case.oracle_store()
+    got, want = f64(out), case.oracle_prefill(ek, ev)
+    assert np.all(np.isfinite(got))
+    assert np.max(np.abs(got - want)) <= TOL["bf16"]
+    order = ws.cpu().numpy()[: len(hist) * mtiles]
+    assert sorted(order.tolist()) == list(range(len(hist) * mtiles))
+    w = _item_weights(chunk, [h + c for h, c in zip(hist, chunk)], g, causal,
+                      bm=bm)
+    assert np.all(np.diff(w[order]) <= 0), w[order]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_inline_ranked_schedule(causal):
+    """At most one work item per thread (6 sequences x 4 M-tiles): each
+    workgroup ranks the items itself and no plan kernel runs, so the
+    workspace is left as it was.  Every item must still be computed exactly
+    once: the output (NaN beforehand) matches the oracle, and equals the
+    output of a call without a workspace bit for bit."""
+    say("prefill schedule (in-kernel rank)", causal)
     hist, chunk = [0, 900, 37, 400, 0, 1500], [130, 64, 200, 1, 0, 90]
     lay = wl.prefill_layout(hist, chunk, 16, seed=31)
     case = PrefillCase(lay, 16, 4, 128, "bf16", seed=32, causal=causal)
@@ -185,14 +222,13 @@ def test_longest_first_schedule(causal):
     need = ops.prefill_workspace_bytes(len(hist), 16, 4, 128, m["max_seqlen_q"],
                                        m["max_seqlen_k"])
     ws = torch.full((need // 4,), -7, dtype=torch.int32, device="cuda")
-    got, _ = _check(case)
-    out2 = case.run_prefill(workspace=ws)
+    case.run_store()
+    out = torch.full_like(case.q, float("nan"))
+    case.run_prefill(out=out, workspace=ws)
     torch.cuda.synchronize()
-    assert bits_equal(wl.host_bits(out2), wl.host_bits(case.run_prefill()))
-    g, bm = 4, 256          # bf16 with D = 128: 8 waves x 32 rows per M-tile
-    mtiles = -(-m["max_seqlen_q"] * g // bm)
-    order = ws.cpu().numpy()[: len(hist) * mtiles]
-    assert sorted(order.tolist()) == list(range(len(hist) * mtiles))
-    w = _item_weights(chunk, [h + c for h, c in zip(hist, chunk)], g, causal,
-                      bm=bm)
-    assert np.all(np.diff(w[order]) <= 0), w[order]
+    ek, ev = case.oracle_store()
+    got, want = f64(out), case.oracle_prefill(ek, ev)
+    assert np.all(np.isfinite(got))
+    assert np.max(np.abs(got - want)) <= TOL["bf16"]
+    assert bits_equal(wl.host_bits(out), wl.host_bits(case.run_prefill()))
+    assert bool((ws == -7).all())
