@@ -744,18 +744,44 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
   // num_partitions + npre - 1 (the prefix partials).
   auto slot = [&](int i) { return i < np ? i : p.num_partitions + (i - np); };
   const int n = np + npre;
-  float m = -INFINITY;
-  for (int i = 0; i < n; ++i) m = fmaxf(m, mx[slot(i)]);
+  // Groups of up to kGroup partials: all their loads are issued together
+  // (one memory round trip per group), then the group's max becomes the
+  // reference, rescaling what earlier groups summed.  With n <= kGroup this
+  // is the plain two-pass merge: max over all, then weighted sums in order.
+  constexpr int kGroup = 8;
+  float m = -INFINITY, l = 0.f, o = 0.f;
+  for (int i0 = 0; i0 < n; i0 += kGroup) {
+    float mv[kGroup], sv[kGroup], av[kGroup];
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {
+      const bool in = i0 + u < n;
+      const int k = slot(in ? i0 + u : i0);
+      mv[u] = in ? mx[k] : -INFINITY;
+      sv[u] = in ? sm[k] : 0.f;
+      av[u] = in ? ac[static_cast<int64_t>(k) * D] : 0.f;
+    }
+    float gm = m;
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) gm = fmaxf(gm, mv[u]);
+    if (gm == -INFINITY) continue;          // nothing visible yet
+    if (gm > m) {
+      const float a = m == -INFINITY ? 0.f : fast_exp2(m - gm);
+      l *= a;
+      o *= a;
+      m = gm;
+    }
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {
+      if (i0 + u < n) {
+        const float w = fast_exp2(mv[u] - m);
+        l = fmaf(w, sv[u], l);
+        o = fmaf(w, av[u], o);
+      }
+    }
+  }
   if (n == 0 || m == -INFINITY) {
     store_out<T>(out, 0.f);
     return;
-  }
-  float l = 0.f, o = 0.f;
-  for (int i = 0; i < n; ++i) {
-    const int k = slot(i);
-    const float w = fast_exp2(mx[k] - m);
-    l = fmaf(w, sm[k], l);
-    o = fmaf(w, ac[static_cast<int64_t>(k) * D], o);
   }
   store_out<T>(out, l > 0.f ? o / l * p.v_scale : 0.f);
 }
@@ -783,7 +809,7 @@ __device__ __forceinline__ int plan_bin(const DecodeParams& p, int item) {
 __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(
     DecodeParams p, int32_t* __restrict__ order) {
   __shared__ int bins[kPlanBins];
-  __shared__ int part_sum[kPlanThreads];
+  __shared__ int wave_sum[kPlanThreads / kWave];
   const int tid = threadIdx.x;
   const int n = p.num_seqs * p.num_partitions;
   for (int i = tid; i < kPlanBins; i += kPlanThreads) bins[i] = 0;
@@ -791,7 +817,8 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(
   for (int item = tid; item < n; item += kPlanThreads)
     atomicAdd(&bins[plan_bin(p, item)], 1);
   __syncthreads();
-  // Exclusive prefix from the heaviest bin down.
+  // Exclusive prefix from the heaviest bin down: a scan inside each wave,
+  // then the totals of the waves before it.
   int cnt[kBinsPerThread];
   int mine = 0;
 #pragma unroll
@@ -799,15 +826,19 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(
     cnt[k] = bins[kPlanBins - 1 - (kBinsPerThread * tid + k)];
     mine += cnt[k];
   }
-  part_sum[tid] = mine;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off *= 2) {
-    const int add = tid >= off ? part_sum[tid - off] : 0;
-    __syncthreads();
-    part_sum[tid] += add;
-    __syncthreads();
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < kWave; off *= 2) {
+    const int y = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += y;
   }
-  int start = part_sum[tid] - mine;
+  if (lane == kWave - 1) wave_sum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wave_sum[w];
+  int start = before + incl - mine;
 #pragma unroll
   for (int k = 0; k < kBinsPerThread; ++k) {
     bins[kPlanBins - 1 - (kBinsPerThread * tid + k)] = start;
