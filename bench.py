@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--prefix-steps", type=int, default=20,
                     help="timed steps of the prefix-sharing decode workload "
                          "(0 skips it)")
+    ap.add_argument("--small-steps", type=int, default=20,
+                    help="timed calls of the small-model decode workload "
+                         "(0 skips it)")
     ap.add_argument("--fp8-steps", type=int, default=20,
                     help="timed steps of the 8B-shaped decode step over an "
                          "8-bit (E4M3) cache (0 skips it)")
@@ -408,6 +411,61 @@ def run_fp8(steps, warmup, dev, flush):
     }
 
 
+def run_small(steps, warmup, dev, flush):
+    """Small-model decode: 64 sequences, contexts uniform in [128, 4096],
+    16 query / 8 KV heads, D = 128, bf16.  Decode only: the cache is filled
+    up front, so the timed call is pa_decode."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from paged_kv_cache_slot_amd import metadata as pm
+    from paged_kv_cache_slot_amd import ops
+
+    cfg = wl.get_config("small")
+    lay = wl.config_decode_layout(cfg)
+    hq, hkv, d, bs = cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, 16
+    b = len(lay.lens)
+    kc, vc = wl.fill_pool(lay.num_blocks, bs, hkv, d, "bf16", cfg.seed, dev)
+    q = wl.make_values((b, hq, d), "bf16", cfg.seed + 1, dev)
+    meta = pm.decode_inputs(lay.tables, lay.lens, bs)
+    bt = torch.as_tensor(meta["block_tables"], device=dev)
+    cl = torch.as_tensor(meta["context_lens"], device=dev)
+    maxlen = meta["max_context_len"]
+    out = torch.empty_like(q)
+    ws = torch.empty(max(ops.decode_workspace_bytes(b, hq, hkv, d, maxlen), 1),
+                     dtype=torch.uint8, device=dev)
+
+    def call(ev):
+        ev[0].record()
+        ops.decode(q, kc, vc, bt, cl, maxlen, out=out, workspace=ws)
+        ev[1].record()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+           for _ in range(steps + warmup)]
+    for i in range(warmup):
+        call(evs[steps + i])
+    torch.cuda.synchronize()
+    for i in range(steps):
+        flush()
+        call(evs[i])
+    torch.cuda.synchronize()
+    dec_all = [e[0].elapsed_time(e[1]) for e in evs[:steps]]
+    dec = float(np.median(dec_all))
+    dbytes = decode_bytes(lay.lens, hq, hkv, d, 2)
+    return {
+        "workload": cfg.title,
+        "steps": steps,
+        "decode_us": round(dec * 1e3, 2),
+        "decode_ms_stats": stats_ms(dec_all),
+        "algorithmic_bytes": dbytes,
+        "decode_tbs": round(dbytes / (dec * 1e-3) / 1e12, 4),
+        "frac_of_hbm_peak": round(dbytes / (dec * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(b / (dec * 1e-3), 1),
+        "kernel": "pa_decode (plan + decode_partition_kernel + decode_merge_kernel)",
+    }
+
+
 def cpu_baseline(case_tables, lens, h_q, h_kc, h_vc, hq, scale, budget_s):
     """Time the oracle on whole sequences until ~budget_s seconds pass."""
     import numpy as np
@@ -538,6 +596,11 @@ def main():
         prefix = run_prefix(args.prefix_steps, max(2, args.warmup // 2), dev,
                             flush)
         torch.cuda.empty_cache()
+    small = None
+    if args.small_steps > 0:
+        small = run_small(args.small_steps, max(2, args.warmup // 2), dev,
+                          flush)
+        torch.cuda.empty_cache()
     fp8 = None
     if args.fp8_steps > 0:
         fp8 = run_fp8(args.fp8_steps, max(2, args.warmup // 2), dev, flush)
@@ -590,6 +653,7 @@ def main():
         "cpu_baseline": cpu,
         "mixed_step": mixed,
         "prefix_step": prefix,
+        "small_step": small,
         "fp8_step": fp8,
         "wall_s_timed": round(wall, 3),
     }
