@@ -754,11 +754,15 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
     float mv[kGroup], sv[kGroup], av[kGroup];
 #pragma unroll
     for (int u = 0; u < kGroup; ++u) {
-      const bool in = i0 + u < n;
-      const int k = slot(in ? i0 + u : i0);
-      mv[u] = in ? mx[k] : -INFINITY;
-      sv[u] = in ? sm[k] : 0.f;
-      av[u] = in ? ac[static_cast<int64_t>(k) * D] : 0.f;
+      mv[u] = -INFINITY;
+      sv[u] = 0.f;
+      av[u] = 0.f;
+      if (i0 + u < n) {                       // uniform over the workgroup
+        const int k = slot(i0 + u);
+        mv[u] = mx[k];
+        sv[u] = sm[k];
+        av[u] = ac[static_cast<int64_t>(k) * D];
+      }
     }
     float gm = m;
 #pragma unroll
