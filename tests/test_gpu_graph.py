@@ -1,0 +1,75 @@
+"""The entry points can be captured in a HIP graph: a call makes no host
+synchronisation, no allocation and no memset node.  One graph holds a decode
+step (store, then decode through the longest-first plan kernel, the
+partition kernel and the merge) and a chunked prefill with more work items
+than a workgroup has threads (plan kernel, then attention).  It is replayed
+several times with q changed in place before each replay and eager calls in
+between; every replay must equal the eager calls on the same inputs bit for
+bit (both run the same kernels on the same data)."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from paged_kv_cache_slot_amd import ops
+from tests.gpu_harness import DecodeCase, PrefillCase, bits_equal, say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replay_matches_eager():
+    say("graph capture: decode step + chunked prefill")
+    rng = np.random.default_rng(91)
+    # 64 sequences x 8 KV heads x 8 partitions of 512 tokens = 4,096
+    # workgroups: the plan kernel, the partition kernel and the merge run.
+    lens = rng.integers(512, 4096, 64, endpoint=True).tolist()
+    lens[0] = 4096
+    dec = DecodeCase(wl.decode_layout(lens, 16, seed=92), 32, 8, 128, "bf16",
+                     seed=93)
+    # 40 sequences x 16 M-tiles = 640 items: the prefill plan kernel runs.
+    hist = rng.integers(0, 300, 40).tolist()
+    chunk = rng.integers(1, 100, 40).tolist()
+    chunk[5] = 1024
+    pre = PrefillCase(wl.prefill_layout(hist, chunk, 16, seed=94), 32, 8, 128,
+                      "bf16", seed=95)
+    dm, pm = dec.meta, pre.meta
+    dws = torch.empty(max(ops.decode_workspace_bytes(
+        len(lens), 32, 8, 128, dm["max_context_len"]), 1),
+        dtype=torch.uint8, device="cuda")
+    pws = torch.empty(max(ops.prefill_workspace_bytes(
+        len(hist), 32, 8, 128, pm["max_seqlen_q"], pm["max_seqlen_k"]), 1),
+        dtype=torch.uint8, device="cuda")
+    dout = torch.empty_like(dec.q)
+    pout = torch.empty_like(pre.q)
+
+    def calls():
+        dec.run_store()
+        dec.run_decode(out=dout, workspace=dws)
+        pre.run_store()
+        pre.run_prefill(out=pout, workspace=pws)
+
+    calls()                       # once eagerly: one-time set-up stays outside
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    torch.cuda.synchronize()
+
+    for r in range(3):
+        dec.q.copy_(wl.make_values(tuple(dec.q.shape), "bf16", 200 + r, "cuda"))
+        pre.q.copy_(wl.make_values(tuple(pre.q.shape), "bf16", 300 + r, "cuda"))
+        dout.fill_(float("nan"))
+        pout.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got_d, got_p = wl.host_bits(dout).copy(), wl.host_bits(pout).copy()
+        assert np.isfinite(dout.float().cpu().numpy()).all(), f"replay {r}"
+        assert np.isfinite(pout.float().cpu().numpy()).all(), f"replay {r}"
+        dout.fill_(float("nan"))
+        pout.fill_(float("nan"))
+        calls()
+        torch.cuda.synchronize()
+        assert bits_equal(got_d, wl.host_bits(dout)), f"decode, replay {r}"
+        assert bits_equal(got_p, wl.host_bits(pout)), f"prefill, replay {r}"
