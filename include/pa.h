@@ -138,7 +138,8 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache,
 
 /*
  * Bytes of workspace pa_decode needs for these sizes (0 when one context
- * partition covers max_context_len and no merge pass is needed).  The
+ * partition covers max_context_len and no merge pass is needed, and 0 for a
+ * non-positive size, which pa_decode rejects).  The
  * workspace holds the partitions' partial results and, for large grids, a
  * longest-first work order that a one-workgroup plan kernel writes at the
  * start of each call (every call rewrites it, so calls that share a

@@ -104,7 +104,8 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache,
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads,
                                  int32_t num_kv_heads, int32_t head_dim,
                                  int32_t max_context_len) {
-  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0)
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_context_len <= 0)
     return 0;
   return pa::plan_decode(num_seqs, num_heads, num_kv_heads, head_dim,
                          max_context_len)

@@ -95,6 +95,8 @@ def test_decode_workspace_query():
     assert one >= 256 * 32 * 2 * (128 + 2) * 4
     assert one % 256 == 0
     assert lib.pa_decode_workspace_bytes(0, 8, 2, 64, 100) == 0
+    assert lib.pa_decode_workspace_bytes(256, 32, 0, 128, 8192) == 0
+    assert lib.pa_decode_workspace_bytes(256, 32, -8, 128, 8192) == 0
 
 
 def _store(lib, **kw):
