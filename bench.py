@@ -147,7 +147,27 @@ def prefill_flops(lq, lk, hq, d):
     return 4 * d * hq * pairs
 
 
-def run_mixed(steps, warmup, dev, flush):
+def cpu_prefill_baseline(h_q, h_kc, h_vc, cu_q, cu_k, tables, hq, d, scale,
+                         budget_s):
+    """Time the oracle's chunked prefill, one whole chunk at a time (its rows
+    and its block table), in a fixed shuffled order, until ~budget_s pass."""
+    import numpy as np
+    import oracle.attention as oa
+    order = np.random.default_rng(0).permutation(len(tables)).tolist()
+    flops, done, t0 = 0, 0, time.perf_counter()
+    for b in order:
+        q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+        lk = int(cu_k[b + 1] - cu_k[b])
+        oa.prefill_attention(h_q[q0:q1], h_kc, h_vc, [0, q1 - q0], [0, lk],
+                             [[int(x) for x in tables[b]]], scale, True, "bf16")
+        flops += prefill_flops(np.array([q1 - q0]), np.array([lk]), hq, d)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    return done, flops, time.perf_counter() - t0
+
+
+def run_mixed(steps, warmup, dev, flush, cpu_s=0.0):
     """Mixed step: one pa_store_kv of every new row (8 x 512 chunk rows + 192
     decode rows), then pa_prefill_varlen of the chunks, then pa_decode of the
     decode rows, on one stream.  Returns a dict for the JSON line."""
@@ -223,6 +243,18 @@ def run_mixed(steps, warmup, dev, flush):
     row = 2 * hkv * d * 2
     sbytes = 2 * (tq + nd) * row + 4 * (tq + nd)
     tflops = flops / (pf * 1e-3) / 1e12
+    cpu = None
+    if cpu_s > 0:
+        # the oracle on the cache as the timed steps left it
+        done, cflops, dt = cpu_prefill_baseline(
+            wl.host_bits(qp), wl.host_bits(kc), wl.host_bits(vc),
+            mp["cu_seqlens_q"], mp["cu_seqlens_k"], pre.tables, hq, d, scale,
+            cpu_s)
+        cpu = {"value": round(cflops / dt / 1e12, 6), "unit": "TFLOP/s",
+               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"{done} of {len(pre.chunk)} chunks "
+                         f"({cflops / 1e9:.1f} GFLOP), fp64 numpy oracle, "
+                         f"{dt:.1f} s"}
     return {
         "workload": cfg.title,
         "steps": steps,
@@ -242,6 +274,7 @@ def run_mixed(steps, warmup, dev, flush):
                      "traffic": committed_traffic(
                          "prefill_mixed_hbm_counters.md", PREFILL_SOURCES),
                      "algorithmic_flops": flops},
+        "cpu_baseline": cpu,
     }
 
 
@@ -411,7 +444,7 @@ def run_fp8(steps, warmup, dev, flush):
     }
 
 
-def run_small(steps, warmup, dev, flush):
+def run_small(steps, warmup, dev, flush, cpu_s=0.0):
     """Small-model decode: 64 sequences, contexts uniform in [128, 4096],
     16 query / 8 KV heads, D = 128, bf16.  Decode only: the cache is filled
     up front, so the timed call is pa_decode."""
@@ -453,9 +486,20 @@ def run_small(steps, warmup, dev, flush):
     dec_all = [e[0].elapsed_time(e[1]) for e in evs[:steps]]
     dec = float(np.median(dec_all))
     dbytes = decode_bytes(lay.lens, hq, hkv, d, 2)
+    cpu = None
+    if cpu_s > 0:
+        done, toks, dt = cpu_baseline(lay.tables, lay.lens, wl.host_bits(q),
+                                      wl.host_bits(kc), wl.host_bits(vc), hq,
+                                      1.0 / math.sqrt(d), cpu_s)
+        cpu = {"value": round(toks * 2 * hkv * d * 2 / dt / 1e12, 6),
+               "unit": "TB/s", "cores": len(os.sched_getaffinity(0)),
+               "kind": "oracle", "tokens_per_s": round(done / dt, 2),
+               "sample": f"{done} of {b} sequences ({toks} context tokens), "
+                         f"fp64 numpy oracle, {dt:.1f} s"}
     return {
         "workload": cfg.title,
         "steps": steps,
+        "cpu_baseline": cpu,
         "decode_us": round(dec * 1e3, 2),
         "decode_ms_stats": stats_ms(dec_all),
         "algorithmic_bytes": dbytes,
@@ -589,7 +633,8 @@ def main():
     mixed = None
     if args.mixed_steps > 0:
         mixed = run_mixed(args.mixed_steps, max(2, args.warmup // 2), dev,
-                          flush)
+                          flush, 0.0 if args.no_cpu_baseline
+                          else args.cpu_seconds / 3)
         torch.cuda.empty_cache()
     prefix = None
     if args.prefix_steps > 0:
@@ -599,7 +644,8 @@ def main():
     small = None
     if args.small_steps > 0:
         small = run_small(args.small_steps, max(2, args.warmup // 2), dev,
-                          flush)
+                          flush, 0.0 if args.no_cpu_baseline
+                          else args.cpu_seconds / 3)
         torch.cuda.empty_cache()
     fp8 = None
     if args.fp8_steps > 0:
