@@ -278,7 +278,7 @@ def run_mixed(steps, warmup, dev, flush, cpu_s=0.0):
     }
 
 
-def run_prefix(steps, warmup, dev, flush):
+def run_prefix(steps, warmup, dev, flush, cpu_s=0.0):
     """Prefix-sharing decode step: pa_store_kv of each sequence's new token
     (private suffix blocks), then pa_decode; 128 sequences share their first
     128 blocks.  Reports unique-byte (each physical block once) and
@@ -353,9 +353,21 @@ def run_prefix(steps, warmup, dev, flush):
     pre_tok = cfg.shared_prefix_blocks * bs
     uniq_tok = pre_tok + int(sum(int(n) - pre_tok for n in lay.lens))
     unique = logical - (int(sum(int(n) for n in lay.lens)) - uniq_tok) * row
+    cpu = None
+    if cpu_s > 0:
+        # the oracle's plain decode: every sequence reads its whole context
+        done, toks, dt = cpu_baseline(lay.tables, lay.lens, wl.host_bits(q),
+                                      wl.host_bits(kc), wl.host_bits(vc), hq,
+                                      scale, cpu_s)
+        cpu = {"value": round(toks * row / dt / 1e12, 6), "unit": "TB/s",
+               "bytes": "logical", "cores": len(os.sched_getaffinity(0)),
+               "kind": "oracle", "tokens_per_s": round(done / dt, 2),
+               "sample": f"{done} of {b} sequences ({toks} context tokens), "
+                         f"fp64 numpy oracle, {dt:.1f} s"}
     return {
         "workload": cfg.title,
         "steps": steps,
+        "cpu_baseline": cpu,
         "decode_us": round(dec * 1e3, 2),
         "unique_bytes": unique,
         "logical_bytes": logical,
@@ -639,7 +651,8 @@ def main():
     prefix = None
     if args.prefix_steps > 0:
         prefix = run_prefix(args.prefix_steps, max(2, args.warmup // 2), dev,
-                            flush)
+                            flush, 0.0 if args.no_cpu_baseline
+                            else args.cpu_seconds / 3)
         torch.cuda.empty_cache()
     small = None
     if args.small_steps > 0:
