@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--prefix-steps", type=int, default=20,
                     help="timed steps of the prefix-sharing decode workload "
                          "(0 skips it)")
+    ap.add_argument("--tiny-steps", type=int, default=20,
+                    help="timed steps of the tiny fp32 decode workload "
+                         "(0 skips it)")
     ap.add_argument("--small-steps", type=int, default=20,
                     help="timed calls of the small-model decode workload "
                          "(0 skips it)")
@@ -456,6 +459,63 @@ def run_fp8(steps, warmup, dev, flush):
     }
 
 
+def run_tiny(steps, warmup, dev, flush):
+    """Tiny decode step (4 sequences, contexts 7 / 16 / 33 / 100, 8 query /
+    2 KV heads, D = 64, fp32): pa_store_kv of the 4 newest rows, then
+    pa_decode.  Launch-bound; reported in microseconds."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from paged_kv_cache_slot_amd import metadata as pm
+    from paged_kv_cache_slot_amd import ops
+
+    cfg = wl.get_config("tiny")
+    lay = wl.config_decode_layout(cfg)
+    hq, hkv, d, bs = cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, 16
+    b = len(lay.lens)
+    kc, vc = wl.fill_pool(lay.num_blocks, bs, hkv, d, "f32", cfg.seed, dev)
+    q = wl.make_values((b, hq, d), "f32", cfg.seed + 1, dev)
+    k_new = wl.make_values((b, hkv, d), "f32", cfg.seed + 2, dev)
+    v_new = wl.make_values((b, hkv, d), "f32", cfg.seed + 3, dev)
+    meta = pm.decode_inputs(lay.tables, lay.lens, bs)
+    slot = torch.as_tensor(meta["slot_mapping"], device=dev)
+    bt = torch.as_tensor(meta["block_tables"], device=dev)
+    cl = torch.as_tensor(meta["context_lens"], device=dev)
+    maxlen = meta["max_context_len"]
+    out = torch.empty_like(q)
+    ws = torch.empty(max(ops.decode_workspace_bytes(b, hq, hkv, d, maxlen), 1),
+                     dtype=torch.uint8, device=dev)
+
+    def step(ev):
+        ev[0].record()
+        ops.store_kv(k_new, v_new, kc, vc, slot)
+        ev[1].record()
+        ops.decode(q, kc, vc, bt, cl, maxlen, out=out, workspace=ws)
+        ev[2].record()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+           for _ in range(steps + warmup)]
+    for i in range(warmup):
+        step(evs[steps + i])
+    torch.cuda.synchronize()
+    for i in range(steps):
+        flush()
+        step(evs[i])
+    torch.cuda.synchronize()
+    step_all = [e[0].elapsed_time(e[2]) for e in evs[:steps]]
+    dec_all = [e[1].elapsed_time(e[2]) for e in evs[:steps]]
+    return {
+        "workload": cfg.title + "; store 4 rows then decode",
+        "steps": steps,
+        "step_us": round(float(np.median(step_all)) * 1e3, 2),
+        "decode_us": round(float(np.median(dec_all)) * 1e3, 2),
+        "step_ms_stats": stats_ms(step_all),
+        "bound": "launch / latency (159,744 B of K/V)",
+        "kernel": "pa_store_kv + pa_decode (one partition, no merge)",
+    }
+
+
 def run_small(steps, warmup, dev, flush, cpu_s=0.0):
     """Small-model decode: 64 sequences, contexts uniform in [128, 4096],
     16 query / 8 KV heads, D = 128, bf16.  Decode only: the cache is filled
@@ -654,6 +714,9 @@ def main():
                             flush, 0.0 if args.no_cpu_baseline
                             else args.cpu_seconds / 3)
         torch.cuda.empty_cache()
+    tiny = None
+    if args.tiny_steps > 0:
+        tiny = run_tiny(args.tiny_steps, max(2, args.warmup // 2), dev, flush)
     small = None
     if args.small_steps > 0:
         small = run_small(args.small_steps, max(2, args.warmup // 2), dev,
@@ -712,6 +775,7 @@ def main():
         "cpu_baseline": cpu,
         "mixed_step": mixed,
         "prefix_step": prefix,
+        "tiny_step": tiny,
         "small_step": small,
         "fp8_step": fp8,
         "wall_s_timed": round(wall, 3),
