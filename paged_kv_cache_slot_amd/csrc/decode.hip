@@ -620,14 +620,38 @@ decode_partition_kernel(
           for (int h = 0; h < G; ++h) wp[h] = s_wp[(j * S::kPairsPerBlock + q) * G + h];
 #pragma unroll
           for (int cc = 0; cc < VL::kCpl; ++cc) {
-            const uint4 x = v_chunk(s, 2 * pi, cc);
-            const uint4 y = v_chunk(s, 2 * pi + 1, cc);
-            const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
-            const uint32_t ys[4] = {y.x, y.y, y.z, y.w};
+            // pr[2 dw] = (token 0, token 1) of dimension 2 dw, pr[2 dw + 1]
+            // of dimension 2 dw + 1, as bfloat16 pairs.
+            uint32_t pr[8];
+            if constexpr (F8) {
+              // Interleave the two tokens' codes first (one byte permute per
+              // four codes), then each conversion yields a pair directly.
+              const uint2 a = vr8[s][2 * pi];
+              const uint2 c = vr8[s][2 * pi + 1];
+              const uint32_t il[4] = {__builtin_amdgcn_perm(c.x, a.x, 0x05010400u),
+                                      __builtin_amdgcn_perm(c.x, a.x, 0x07030602u),
+                                      __builtin_amdgcn_perm(c.y, a.y, 0x05010400u),
+                                      __builtin_amdgcn_perm(c.y, a.y, 0x07030602u)};
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                pr[2 * k] = e4m3x2_to_bf16<false>(il[k]);
+                pr[2 * k + 1] = e4m3x2_to_bf16<true>(il[k]);
+              }
+            } else {
+              const uint4 x = v_chunk(s, 2 * pi, cc);
+              const uint4 y = v_chunk(s, 2 * pi + 1, cc);
+              const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+              const uint32_t ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+              for (int dw = 0; dw < 4; ++dw) {
+                pr[2 * dw] = pack_lo(xs[dw], ys[dw]);
+                pr[2 * dw + 1] = pack_hi(xs[dw], ys[dw]);
+              }
+            }
 #pragma unroll
             for (int dw = 0; dw < 4; ++dw) {
-              const uint32_t lo = pack_lo(xs[dw], ys[dw]);
-              const uint32_t hi = pack_hi(xs[dw], ys[dw]);
+              const uint32_t lo = pr[2 * dw];
+              const uint32_t hi = pr[2 * dw + 1];
 #pragma unroll
               for (int h = 0; h < G; ++h) {
                 acc[h][cc][2 * dw] = dot2_bf16(lo, wp[h], acc[h][cc][2 * dw]);
