@@ -82,6 +82,7 @@ def _decode_case(lens, hq, hkv, k_scale, v_scale, seed, seqs=None, lay=None):
                                 "bf16", seqs=seqs)
     got = f64(out)
     rows = list(range(len(lay.lens))) if seqs is None else seqs
+    _decode_case.last = (got[rows], want[rows])
     assert np.all(np.isfinite(got[rows]))
     err = float(np.max(np.abs(got[rows] - want[rows])))
     assert err <= TOL["bf16"], f"max abs err {err}"
