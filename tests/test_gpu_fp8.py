@@ -63,7 +63,11 @@ def _poison(kc, vc, tables, lens, nb, bs):
     vc[bad] = 0x7F
 
 
-def _decode_case(lens, hq, hkv, k_scale, v_scale, seed, seqs=None, lay=None):
+def _decode_case(lens, hq, hkv, k_scale, v_scale, seed, seqs=None, lay=None,
+                 abs_check=True):
+    """Decode over an E4M3 pool against the oracle.  With abs_check the
+    outputs must be within the absolute bf16 tolerance; returns (got, want)
+    for the sequences compared."""
     bs, d = 16, 128
     if lay is None:
         lay = wl.decode_layout(lens, bs, seed=seed)
@@ -82,11 +86,11 @@ def _decode_case(lens, hq, hkv, k_scale, v_scale, seed, seqs=None, lay=None):
                                 "bf16", seqs=seqs)
     got = f64(out)
     rows = list(range(len(lay.lens))) if seqs is None else seqs
-    _decode_case.last = (got[rows], want[rows])
     assert np.all(np.isfinite(got[rows]))
-    err = float(np.max(np.abs(got[rows] - want[rows])))
-    assert err <= TOL["bf16"], f"max abs err {err}"
-    return got, want
+    if abs_check:
+        err = float(np.max(np.abs(got[rows] - want[rows])))
+        assert err <= TOL["bf16"], f"max abs err {err}"
+    return got[rows], want[rows]
 
 
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (32, 8), (16, 2)])
