@@ -166,3 +166,15 @@ def test_multi_chunk_partitions(dtype):
     lay = wl.decode_layout(lens, 16, seed=78)
     case = DecodeCase(lay, hq, hkv, d, dtype, seed=79)
     _check(case, seqs=list(range(10)) + [20, 40, 63])
+
+
+@pytest.mark.parametrize("dtype,longest", [("bf16", 131072), ("f32", 65536)])
+def test_very_long_context(dtype, longest):
+    """A 128K-token (bf16) or 64K-token (fp32) context beside a mid-size and
+    a tiny one: hundreds of 512-token partitions per sequence, so the merge
+    folds hundreds of partials per head, and fp32 sums run over 64K keys."""
+    say("decode very long context", dtype, longest)
+    lens = [longest, 70001 if dtype == "bf16" else 33333, 5]
+    lay = wl.decode_layout(lens, 16, seed=9401)
+    case = DecodeCase(lay, 8, 2, 128, dtype, seed=9402)
+    _check(case)

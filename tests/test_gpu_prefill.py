@@ -232,3 +232,16 @@ def test_inline_ranked_schedule(causal):
     assert np.max(np.abs(got - want)) <= TOL["bf16"]
     assert bits_equal(wl.host_bits(out), wl.host_bits(case.run_prefill()))
     assert bool((ws == -7).all())
+
+
+def test_very_long_history():
+    """A 1,024-row chunk over 32,768 cached tokens next to a short sequence:
+    the longest work items read ~33K keys through the block table; rows
+    sampled across the chunk (first, last and 14 random) of the long
+    sequence, every row of the short one."""
+    say("prefill very long history")
+    lay = wl.prefill_layout([32768, 40], [1024, 9], 16, seed=9411)
+    case = PrefillCase(lay, 8, 2, 128, "bf16", seed=9412)
+    rng = np.random.default_rng(9413)
+    rows = sorted({0, 1023, *rng.integers(1, 1023, 14).tolist()})
+    _check(case, seqs=[0, 1], rows={0: rows})
