@@ -246,3 +246,32 @@ def _decode8(lib, **kw):
 ])
 def test_decode_fp8_validation(kw, code, no_device):
     assert _decode8(_lib.load(), **kw) == code
+
+
+def test_missing_library_raises(monkeypatch):
+    """No fallback: with the library absent, loading it raises."""
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libpa.so")
+    with pytest.raises(RuntimeError, match="no fallback"):
+        _lib.load()
+
+
+def test_ops_reject_host_tensors():
+    """Every operation refuses CPU tensors instead of computing on the host."""
+    import torch
+
+    from paged_kv_cache_slot_amd import ops
+    f = torch.zeros((2, 16, 2, 64), dtype=torch.float32)
+    q = torch.zeros((1, 4, 64), dtype=torch.float32)
+    i = torch.zeros((1, 1), dtype=torch.int32)
+    n = torch.ones(1, dtype=torch.int32)
+    calls = [
+        lambda: ops.store_kv(q[:, :2], q[:, :2], f, f, n),
+        lambda: ops.copy_blocks(f, f, torch.zeros((1, 2), dtype=torch.int32)),
+        lambda: ops.decode(q, f, f, i, n, 1),
+        lambda: ops.prefill_varlen(q, f, f, torch.tensor([0, 1], dtype=torch.int32),
+                                   torch.tensor([0, 1], dtype=torch.int32), 1, 1, i),
+    ]
+    for call in calls:
+        with pytest.raises(ValueError, match="GPU tensors only"):
+            call()
