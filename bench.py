@@ -606,8 +606,8 @@ def cpu_baseline(case_tables, lens, h_q, h_kc, h_vc, hq, scale, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
-              "this build has no multi-GPU path.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): "
+              "the kernels have no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
