@@ -24,7 +24,7 @@ def _shape(rng):
     return dtype, d, g * hkv, hkv
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(20))
 def test_random_decode(seed):
     rng = np.random.default_rng(7100 + seed)
     dtype, d, hq, hkv = _shape(rng)
@@ -36,7 +36,7 @@ def test_random_decode(seed):
     check_decode(DecodeCase(lay, hq, hkv, d, dtype, seed=7300 + seed))
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(20))
 def test_random_prefill(seed):
     rng = np.random.default_rng(7400 + seed)
     dtype, d, hq, hkv = _shape(rng)
@@ -51,7 +51,7 @@ def test_random_prefill(seed):
                               causal=causal))
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(10))
 def test_random_fp8_decode(seed):
     """8-bit (E4M3) cache: random GQA ratio, lengths and per-cache scales.
     k_scale spans two orders of magnitude (it only sharpens the softmax);
@@ -75,7 +75,7 @@ def test_random_fp8_decode(seed):
     assert err <= 2.0 ** -7 * max(1.0, float(np.max(np.abs(want)))), err
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(10))
 def test_random_shared_prefix(seed):
     """Shared-prefix decode: random runs of sequences sharing 1..24 leading
     blocks, independent sequences between them, random dtype and shape."""
