@@ -206,6 +206,15 @@ def check_e4m3_hand_values():
     assert of8.e4m3_value(0x7E) == 448.0 and math.isnan(of8.e4m3_value(0xFF))
 
 
+def check_fp8_dequantize_closed_form():
+    """code * scale for codes whose values the E4M3 definition fixes (bias
+    7, subnormals m/8 * 2^-6): 0x38 = 1, 0x40 = 2, 0xB8 = -1, 0x01 = 2^-9,
+    0x7E = 448; with scale 0.25."""
+    got = of8.dequantize(np.array([0x38, 0x40, 0xB8, 0x01, 0x7E]), 0.25)
+    want = np.array([0.25, 0.5, -0.25, 2.0 ** -11, 112.0])
+    assert np.array_equal(got, want), got
+
+
 def check_fp8_decode_equals_dequantized():
     """Decode over an E4M3 cache equals plain decode over float32 caches
     holding code * scale (exact in float32), for random codes and scales."""
@@ -658,6 +667,7 @@ ALL_CHECKS = [
     check_e4m3_codes_against_library,
     check_e4m3_encode_against_library,
     check_e4m3_hand_values,
+    check_fp8_dequantize_closed_form,
     check_fp8_decode_equals_dequantized,
     check_copy_blocks_against_brute,
     check_kv_bytes,

@@ -242,6 +242,28 @@ def _e4m3_subnormal_exponent(code):
     return _orig_e4m3_value(code)
 
 
+_orig_dequantize = of8.dequantize
+_orig_quantize = of8.quantize
+_orig_fp8_decode = of8.decode_attention
+
+
+def _dequantize_no_scale(codes, scale):
+    """Forgets the per-cache scale."""
+    return _orig_dequantize(codes, 1.0)
+
+
+def _quantize_divides(x, inv_scale):
+    """Divides by the inverse scale instead of multiplying."""
+    return _orig_quantize(x, 1.0 / inv_scale)
+
+
+def _fp8_decode_swapped_scales(q, k_codes, v_codes, block_tables, context_lens,
+                               scale, k_scale, v_scale, *args, **kwargs):
+    """Applies the V scale to K and the K scale to V."""
+    return _orig_fp8_decode(q, k_codes, v_codes, block_tables, context_lens,
+                            scale, v_scale, k_scale, *args, **kwargs)
+
+
 MUTATIONS = {
     "drop_scale": (oa, "attend", _attend_factory(drop_scale=True)),
     "no_normalize": (oa, "attend", _attend_factory(no_normalize=True)),
@@ -267,6 +289,10 @@ MUTATIONS = {
     "e4m3_round_half_up": (of8, "e4m3_encode", _e4m3_round_half_up),
     "e4m3_no_saturation": (of8, "e4m3_encode", _e4m3_no_saturation),
     "e4m3_subnormal_exponent": (of8, "e4m3_value", _e4m3_subnormal_exponent),
+    "fp8_dequantize_no_scale": (of8, "dequantize", _dequantize_no_scale),
+    "fp8_quantize_divides": (of8, "quantize", _quantize_divides),
+    "fp8_decode_swapped_scales": (of8, "decode_attention",
+                                  _fp8_decode_swapped_scales),
 }
 
 
