@@ -93,17 +93,21 @@ def store_kv(k_cache, v_cache, k, v, slot_mapping, k_inv_scale, v_inv_scale,
     As ``attention.store_kv`` (ModelRunner page, sections 2 and 5: row t goes
     to flat slot slot_mapping[t], a negative slot writes nothing), with each
     element stored as its E4M3 code.  k, v: [T, Hkv, D] of ``src_dtype``
-    (bf16 bits or float32); the caches: uint8 [NB, bs, Hkv, D].
+    (bf16 bits or float32); the caches: uint8 [NB, bs, Hkv, D].  A slot
+    past the cache is a precondition violation and raises IndexError, as in
+    ``attention.store_kv``.
     """
     k_out = np.array(k_cache, copy=True)
     v_out = np.array(v_cache, copy=True)
-    bs = k_out.shape[1]
+    num_blocks, bs = k_out.shape[0], k_out.shape[1]
     k32 = to_f64(k, src_dtype).astype(np.float32)   # exact: inputs are f32/bf16
     v32 = to_f64(v, src_dtype).astype(np.float32)
     for t, slot in enumerate(slot_mapping):
         slot = int(slot)
         if slot < 0:
             continue
+        if slot >= num_blocks * bs:
+            raise IndexError(f"slot {slot} outside the cache")
         k_out[slot // bs, slot % bs] = quantize(k32[t], k_inv_scale)
         v_out[slot // bs, slot % bs] = quantize(v32[t], v_inv_scale)
     return k_out, v_out

@@ -93,3 +93,52 @@ def brute_store(k_cache, v_cache, k, v, slot_mapping):
                 kc[blk][off][h][d] = k[t][h][d]
                 vc[blk][off][h][d] = v[t][h][d]
     return kc, vc
+
+
+def f32_round(x):
+    """Nearest float32 to a Python float (ties to even), via the IEEE
+    single-precision packing of the struct module."""
+    import struct
+    return struct.unpack("f", struct.pack("f", x))[0]
+
+
+def nearest_code(a, values):
+    """Code of the magnitude ``a`` (>= 0, already saturated) by exhaustive
+    search over ``values`` -- values[c] is the value of code c, c = 0..126,
+    the non-negative finite codes -- nearest value first, and between two
+    equally near codes the even one (an even code has an even last
+    mantissa bit)."""
+    best, best_d = None, None
+    for c, val in enumerate(values):
+        d = abs(a - val)
+        if best is None or d < best_d or (d == best_d and c % 2 == 0):
+            best, best_d = c, d
+    return best
+
+
+def brute_store_fp8(k_codes, v_codes, k, v, slot_mapping, k_inv_scale,
+                    v_inv_scale, values, max_value):
+    """Quantising scatter, one element at a time, on nested lists.
+
+    Row t goes to flat slot slot_mapping[t] (block slot // bs, offset
+    slot % bs; a negative slot writes nothing).  Element x becomes the code
+    of p = float32(x * inv_scale): sign bit 0x80 if p is negative (also -0),
+    magnitude min(|p|, max_value) matched by ``nearest_code``.  ``values``
+    lists the non-negative finite code values (taken from a library's
+    decoding, not from the oracle)."""
+    import copy
+    kc = copy.deepcopy(k_codes)
+    vc = copy.deepcopy(v_codes)
+    block_size = len(kc[0])
+    for t, slot in enumerate(slot_mapping):
+        if slot < 0:
+            continue
+        blk, off = divmod(slot, block_size)
+        for cache, rows, inv in ((kc, k, k_inv_scale), (vc, v, v_inv_scale)):
+            for h in range(len(rows[t])):
+                for d in range(len(rows[t][h])):
+                    p = f32_round(rows[t][h][d] * inv)
+                    sign = 0x80 if math.copysign(1.0, p) < 0 else 0
+                    mag = min(abs(p), max_value)
+                    cache[blk][off][h][d] = sign | nearest_code(mag, values)
+    return kc, vc

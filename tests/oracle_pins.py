@@ -358,6 +358,67 @@ def check_bf16_widening():
     assert got[5] == 2.0 ** -133
 
 
+def _e4m3_values_from_library():
+    """Values of the non-negative finite E4M3 codes 0..126, decoded by
+    torch's float8_e4m3fn (an implementation of the OCP format independent
+    of the oracle)."""
+    import torch
+    return torch.arange(127, dtype=torch.uint8).view(torch.float8_e4m3fn) \
+        .to(torch.float64).tolist()
+
+
+def check_fp8_store_against_brute():
+    """The quantising store equals an element-by-element brute force (float32
+    product, nearest code by exhaustive search over the library's code
+    values, ties to the even code, saturation at 448) for bf16 and float32
+    rows, with different K and V scales (not powers of two, so the float32
+    product rounds), slots in random order, two -1 slots that must write
+    nothing ("3.6 ModelRunner, CUDA Graph, and benchmarks", section 5) and
+    a gain that pushes some elements far past 448.  A slot past the cache
+    raises.  Sources: the cache-precision flag of "10 Serving Engines"
+    section 10.2.2 (format readings in oracle/fp8.py)."""
+    values = _e4m3_values_from_library()
+    rng = np.random.default_rng(29)
+    nb, bs, hkv, d, t = 5, 4, 2, 8, 9
+    k_inv = float(np.float32(1.0) / np.float32(0.07))
+    v_inv = float(np.float32(1.0) / np.float32(0.3))
+    assert k_inv != v_inv
+    for src in ("f32", "bf16"):
+        kc = rng.integers(0, 256, size=(nb, bs, hkv, d)).astype(np.uint8)
+        vc = rng.integers(0, 256, size=(nb, bs, hkv, d)).astype(np.uint8)
+        k = (rng.standard_normal((t, hkv, d)) *
+             rng.choice([0.01, 1.0, 8.0, 60.0], size=(t, hkv, 1))).astype(np.float32)
+        v = (rng.standard_normal((t, hkv, d)) *
+             rng.choice([0.01, 1.0, 8.0, 200.0], size=(t, hkv, 1))).astype(np.float32)
+        k[0, 0, :3] = [0.0, -0.0, 1e-9]
+        if src == "bf16":
+            k, v = _bf16_bits(k), _bf16_bits(v)
+        k32 = oa.to_f64(k, src)
+        v32 = oa.to_f64(v, src)
+        assert np.max(np.abs(k32)) * k_inv > 448 and np.max(np.abs(v32)) * v_inv > 448
+        slots = [int(s) for s in rng.permutation(nb * bs)[:t]]
+        slots[1] = -1
+        slots[6] = -1
+        nk, nv = of8.store_kv(kc, vc, k, v, slots, k_inv, v_inv, src)
+        bk, bv = bf.brute_store_fp8(kc.tolist(), vc.tolist(), k32.tolist(),
+                                    v32.tolist(), slots, k_inv, v_inv,
+                                    values, 448.0)
+        assert nk.tolist() == bk, "K codes differ from the brute force"
+        assert nv.tolist() == bv, "V codes differ from the brute force"
+        # the -1 rows left every slot they might have named untouched
+        named = {s for s in slots if s >= 0}
+        for s in range(nb * bs):
+            if s not in named:
+                assert nk[s // bs, s % bs].tobytes() == kc[s // bs, s % bs].tobytes()
+                assert nv[s // bs, s % bs].tobytes() == vc[s // bs, s % bs].tobytes()
+    try:
+        of8.store_kv(kc, vc, k[:1], v[:1], [nb * bs], k_inv, v_inv, "bf16")
+    except IndexError:
+        pass
+    else:
+        raise AssertionError("a slot past the cache must raise")
+
+
 # -------------------------------------------------------------------- store
 
 def _tiny_pool(rng, nb, bs, hkv, d, dtype):
@@ -669,6 +730,7 @@ ALL_CHECKS = [
     check_e4m3_hand_values,
     check_fp8_dequantize_closed_form,
     check_fp8_decode_equals_dequantized,
+    check_fp8_store_against_brute,
     check_copy_blocks_against_brute,
     check_kv_bytes,
     check_bf16_widening,

@@ -264,6 +264,50 @@ def _fp8_decode_swapped_scales(q, k_codes, v_codes, block_tables, context_lens,
                             scale, v_scale, k_scale, *args, **kwargs)
 
 
+_orig_fp8_store = of8.store_kv
+
+
+def _fp8_store_swapped_scales(k_cache, v_cache, k, v, slot_mapping,
+                              k_inv_scale, v_inv_scale, src_dtype):
+    """Quantises K with the V inverse scale and V with the K one."""
+    return _orig_fp8_store(k_cache, v_cache, k, v, slot_mapping, v_inv_scale,
+                           k_inv_scale, src_dtype)
+
+
+def _fp8_store_slot_split(k_cache, v_cache, k, v, slot_mapping, k_inv_scale,
+                          v_inv_scale, src_dtype):
+    """Splits the flat slot with the head count instead of the block size."""
+    k_out = np.array(k_cache, copy=True)
+    v_out = np.array(v_cache, copy=True)
+    split = k_out.shape[2]                      # planted: Hkv, not bs
+    k32 = oa.to_f64(k, src_dtype).astype(np.float32)
+    v32 = oa.to_f64(v, src_dtype).astype(np.float32)
+    for t, slot in enumerate(slot_mapping):
+        slot = int(slot)
+        if slot < 0:
+            continue
+        k_out[slot // split % k_out.shape[0], slot % split] = \
+            of8.quantize(k32[t], k_inv_scale)
+        v_out[slot // split % k_out.shape[0], slot % split] = \
+            of8.quantize(v32[t], v_inv_scale)
+    return k_out, v_out
+
+
+def _fp8_store_no_skip(k_cache, v_cache, k, v, slot_mapping, k_inv_scale,
+                       v_inv_scale, src_dtype):
+    """Writes the rows of -1 slots too (numpy wraps -1 to the last slot)."""
+    k_out = np.array(k_cache, copy=True)
+    v_out = np.array(v_cache, copy=True)
+    bs = k_out.shape[1]
+    k32 = oa.to_f64(k, src_dtype).astype(np.float32)
+    v32 = oa.to_f64(v, src_dtype).astype(np.float32)
+    for t, slot in enumerate(slot_mapping):
+        slot = int(slot)                        # planted: no skip of < 0
+        k_out[slot // bs, slot % bs] = of8.quantize(k32[t], k_inv_scale)
+        v_out[slot // bs, slot % bs] = of8.quantize(v32[t], v_inv_scale)
+    return k_out, v_out
+
+
 MUTATIONS = {
     "drop_scale": (oa, "attend", _attend_factory(drop_scale=True)),
     "no_normalize": (oa, "attend", _attend_factory(no_normalize=True)),
@@ -293,6 +337,9 @@ MUTATIONS = {
     "fp8_quantize_divides": (of8, "quantize", _quantize_divides),
     "fp8_decode_swapped_scales": (of8, "decode_attention",
                                   _fp8_decode_swapped_scales),
+    "fp8_store_swapped_scales": (of8, "store_kv", _fp8_store_swapped_scales),
+    "fp8_store_slot_split": (of8, "store_kv", _fp8_store_slot_split),
+    "fp8_store_no_skip": (of8, "store_kv", _fp8_store_no_skip),
 }
 
 
