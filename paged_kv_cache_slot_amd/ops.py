@@ -34,6 +34,28 @@ def _need_gpu(*tensors):
             raise ValueError("libpa needs contiguous tensors")
 
 
+def _check_out(out, q):
+    """A caller's output buffer must be exactly the result's: the kernels
+    write q.numel() elements of q's dtype to it, so a smaller buffer, another
+    dtype or another device would be written past or misread."""
+    if out is None:
+        return
+    if out.device != q.device:
+        raise ValueError(f"out is on {out.device}, q on {q.device}")
+    if out.dtype != q.dtype:
+        raise TypeError(f"out dtype {out.dtype} differs from q dtype {q.dtype}")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError(f"out shape {tuple(out.shape)} differs from q shape "
+                         f"{tuple(q.shape)}")
+
+
+def _check_workspace(workspace, q):
+    """The workspace must sit on q's device (its size is checked by the
+    library against the query)."""
+    if workspace is not None and workspace.device != q.device:
+        raise ValueError(f"workspace is on {workspace.device}, q on {q.device}")
+
+
 def _i32(t, name):
     if t.dtype != torch.int32:
         raise TypeError(f"{name} must be int32")
@@ -108,6 +130,8 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
     block_tables int32 [B, W]; context_lens int32 [B] (counting the new
     token); max_context_len a host-side upper bound.  Returns out [B, Hq, D].
     """
+    _check_out(out, q)
+    _check_workspace(workspace, q)
     _need_gpu(q, k_cache, v_cache, block_tables, context_lens, out, workspace)
     _i32(block_tables, "block_tables")
     _i32(context_lens, "context_lens")
@@ -156,6 +180,8 @@ def decode_shared_prefix(q, k_cache, v_cache, block_tables, context_lens,
     (shared tokens, 0 outside any group); groups int32 [G, 2] (first
     sequence, count); max_suffix_len / max_prefix_len / max_group_size are
     host-side bounds.  Returns out [B, Hq, D]."""
+    _check_out(out, q)
+    _check_workspace(workspace, q)
     _need_gpu(q, k_cache, v_cache, block_tables, context_lens, prefix_lens,
               groups, out, workspace)
     for t, n in ((block_tables, "block_tables"), (context_lens, "context_lens"),
@@ -220,6 +246,8 @@ def decode_fp8(q, k_cache, v_cache, block_tables, context_lens,
                workspace=None):
     """Paged decode over 8-bit E4M3 caches (uint8 [NB, 16, Hkv, 128]):
     K = code * k_scale, V = code * v_scale; q and out bf16 [B, Hq, 128]."""
+    _check_out(out, q)
+    _check_workspace(workspace, q)
     _need_gpu(q, k_cache, v_cache, block_tables, context_lens, out, workspace)
     _i32(block_tables, "block_tables")
     _i32(context_lens, "context_lens")
@@ -266,6 +294,8 @@ def prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k,
     """Varlen chunked prefill.  q [total_q, Hq, D] packed by cu_seqlens_q;
     keys are the first cu_seqlens_k[b+1]-cu_seqlens_k[b] tokens of each
     sequence's block table.  Returns out [total_q, Hq, D]."""
+    _check_out(out, q)
+    _check_workspace(workspace, q)
     _need_gpu(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_tables,
               out, workspace)
     for t, n in ((cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k"),

@@ -275,3 +275,53 @@ def test_ops_reject_host_tensors():
     for call in calls:
         with pytest.raises(ValueError, match="GPU tensors only"):
             call()
+
+
+def test_ops_reject_mismatched_out():
+    """A caller-supplied output buffer must match q in shape, dtype and
+    device (the kernels write q.numel() elements of q's dtype into it), and a
+    workspace must sit on q's device.  Checked before anything else, so no
+    GPU is needed to see the errors."""
+    import torch
+
+    from paged_kv_cache_slot_amd import ops
+    f = torch.zeros((2, 16, 2, 64), dtype=torch.float32)
+    q = torch.zeros((3, 4, 64), dtype=torch.float32)
+    qb = torch.zeros((3, 4, 128), dtype=torch.bfloat16)
+    i = torch.zeros((3, 1), dtype=torch.int32)
+    n = torch.ones(3, dtype=torch.int32)
+    cu = torch.tensor([0, 1, 2, 3], dtype=torch.int32)
+    u8 = torch.zeros((2, 16, 2, 128), dtype=torch.uint8)
+    g = torch.zeros((1, 2), dtype=torch.int32)
+    meta = torch.empty(16, dtype=torch.uint8, device="meta")
+
+    def ops_with(qq, out=None, workspace=None):
+        return [
+            lambda: ops.decode(qq, f, f, i, n, 1, out=out,
+                               workspace=workspace),
+            lambda: ops.prefill_varlen(qq, f, f, cu, cu, 1, 1, i, out=out,
+                                       workspace=workspace),
+            lambda: ops.decode_shared_prefix(qq, f, f, i, n, n, g, 1, 0, 1,
+                                             out=out, workspace=workspace),
+        ]
+
+    bad = [
+        (ValueError, "shape", dict(out=torch.zeros((2, 4, 64)))),
+        (ValueError, "shape", dict(out=torch.zeros((3, 4, 64)).view(-1))),
+        (TypeError, "dtype", dict(out=torch.zeros((3, 4, 64),
+                                                  dtype=torch.bfloat16))),
+        (ValueError, "is on", dict(out=torch.empty((3, 4, 64),
+                                                   device="meta"))),
+        (ValueError, "workspace is on", dict(workspace=meta)),
+    ]
+    for exc, msg, kw in bad:
+        for call in ops_with(q, **kw):
+            with pytest.raises(exc, match=msg):
+                call()
+    # the 8-bit decode takes bf16 q / out
+    with pytest.raises(TypeError, match="dtype"):
+        ops.decode_fp8(qb, u8, u8, i, n, 1, 1.0, 1.0,
+                       out=torch.zeros((3, 4, 128)))
+    with pytest.raises(ValueError, match="shape"):
+        ops.decode_fp8(qb, u8, u8, i, n, 1, 1.0, 1.0,
+                       out=torch.zeros((3, 4, 64), dtype=torch.bfloat16))
