@@ -61,6 +61,7 @@ constexpr int kBlock = 16;           // tokens per cache block
 constexpr int kWaves = 4;            // waves per workgroup
 constexpr int kThreads = kWaves * kWave;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr uint32_t kBf16PairOne = 0x3F803F80u;   // (1.0, 1.0) as bfloat16
 // Word 3 of a raw (unswizzled, untyped) gfx9 buffer resource.
 constexpr int kBufferRsrcWord3 = 0x00020000;
 // Cache-policy bits of a buffer load: non-temporal (streamed, used once).
@@ -107,10 +108,7 @@ struct DecodeShape {
   // Register floor of 3 waves per SIMD (168 VGPRs) for bf16 with G <= 4:
   // the chunk loop keeps the output accumulators live through the QK pass,
   // and a tighter cap made the compiler spill (measured slower).
-#ifndef PA_DECODE_MINWAVES
-#define PA_DECODE_MINWAVES 3
-#endif
-  static constexpr int kMinWaves = (sizeof(T) == 2 && G <= 4) ? PA_DECODE_MINWAVES : 1;
+  static constexpr int kMinWaves = (sizeof(T) == 2 && G <= 4) ? 3 : 1;
   // Blocks each wave has in flight: the next block's K (or V) is loaded
   // while the current one is consumed.  Deeper prefetch was measured and
   // gains nothing.
@@ -573,9 +571,12 @@ decode_partition_kernel(
           const int ta = j * kBlock + (q / VL::kRpi) * 2 * VL::kRpi + q % VL::kRpi;
           const float wa = weight(s_w[ta * G + h]);
           const float wb = weight(s_w[(ta + VL::kRpi) * G + h]);
-          s_wp[i] = static_cast<uint32_t>(f32_to_bf16_rne(wa)) |
-                    (static_cast<uint32_t>(f32_to_bf16_rne(wb)) << 16);
-          acc_l += wa + wb;
+          const uint32_t wp = static_cast<uint32_t>(f32_to_bf16_rne(wa)) |
+                              (static_cast<uint32_t>(f32_to_bf16_rne(wb)) << 16);
+          s_wp[i] = wp;
+          // The sum takes the rounded weights P V uses (one dot2 against
+          // a pair of bfloat16 ones), so numerator and denominator agree.
+          acc_l = dot2_bf16(wp, kBf16PairOne, acc_l);
         }
       } else {
         for (int i = tid; i < nblk * kBlock * G; i += kThreads) {
@@ -911,23 +912,15 @@ hipError_t dispatch_group(const DecodeParams& prm, int num_seqs,
 }
 
 // Tokens per chunk: the logits of one chunk sit in LDS.
-#ifndef PA_DECODE_CHUNK_TOKENS
-#define PA_DECODE_CHUNK_TOKENS 512
-#endif
-constexpr int kChunkTokens = PA_DECODE_CHUNK_TOKENS;
+constexpr int kChunkTokens = 512;
 // A partition spans one or more chunks.  Fewer, longer partitions write
 // fewer partial results (which slow the K/V stream far beyond their own
 // bytes) but leave fewer workgroups to balance; the plan takes the longest
 // partitions that still give at least this many workgroups.
-#ifndef PA_DECODE_TARGET_WGS
-#define PA_DECODE_TARGET_WGS 8192
-#endif
-constexpr int64_t kTargetWorkgroups = PA_DECODE_TARGET_WGS;
+constexpr int64_t kTargetWorkgroups = 8192;
 constexpr int kMaxChunksPerPartition = 16;
-#ifndef PA_PREFIX_TARGET_WGS
-#define PA_PREFIX_TARGET_WGS 128
-#endif
-constexpr int64_t kPrefixTargetWorkgroups = PA_PREFIX_TARGET_WGS;
+// Prefix pass of the shared-prefix decode: about this many workgroups.
+constexpr int64_t kPrefixTargetWorkgroups = 128;
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -975,13 +968,9 @@ DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads,
     return np < 1 ? 1 : np;
   };
   int chunks = 1;
-#ifdef PA_DECODE_CHUNKS
-  chunks = PA_DECODE_CHUNKS;
-#else
   while (chunks < kMaxChunksPerPartition &&
          groups * parts(kChunkTokens * chunks * 2) >= kTargetWorkgroups)
     chunks *= 2;
-#endif
   plan.partition_tokens = kChunkTokens * chunks;
   plan.num_partitions = parts(plan.partition_tokens);
   if (plan.num_partitions == 1) {
