@@ -41,7 +41,9 @@
  * Pointers.  Every tensor pointer is a device pointer, 16-byte aligned.  The
  * caller owns every buffer; the library never allocates, frees, or keeps a
  * pointer after the call returns.  Scratch space is a caller-provided
- * workspace sized by the *_workspace_bytes queries.
+ * workspace sized by the *_workspace_bytes queries -- except for
+ * pa_decode_noalloc, which uses a static scratch array the library holds on
+ * each GPU (see there).
  *
  * Streams.  Every call only enqueues work on `stream` (a hipStream_t; NULL
  * is the default stream) and returns; it never synchronises, allocates or
@@ -72,7 +74,9 @@ typedef enum {
   PA_ERR_UNSUPPORTED = 3,  /* head_dim, block_size, GQA ratio, dtype or
                               pointer alignment not supported               */
   PA_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than the query says */
-  PA_ERR_LAUNCH = 5        /* the HIP runtime rejected a kernel launch      */
+  PA_ERR_LAUNCH = 5,       /* the HIP runtime rejected a kernel launch      */
+  PA_ERR_SCRATCH_LIMIT = 6 /* pa_decode_noalloc: the sizes need more than the
+                              static scratch holds                          */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
@@ -191,6 +195,38 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache,
                     int32_t num_heads, int32_t num_kv_heads,
                     int32_t head_dim, float scale, void* workspace,
                     size_t workspace_bytes, pa_dtype dtype, void* stream);
+
+/*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation, kernels and arguments as
+ * pa_decode, without the workspace.  The partial results and the schedule
+ * go to a static scratch array of 32 MiB (33,554,432 bytes) that the
+ * library holds on each GPU it runs on until the process ends.  The call
+ * allocates nothing; on its first call on a device it looks up that
+ * device's array address once (hipGetSymbolAddress).
+ *
+ * Limit: sizes for which pa_decode_workspace_bytes(num_seqs, num_heads,
+ * num_kv_heads, head_dim, max_context_len) exceeds 33,554,432 return
+ * PA_ERR_SCRATCH_LIMIT and launch nothing (256 sequences x 32 query heads
+ * of head_dim 128 at max_context_len 8192 need about 17 MB).
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last
+ * call's contents (nothing needs to start at zero: each call writes what
+ * it reads).  Calls that overlap on one GPU -- on different streams, or
+ * from different host threads without stream ordering -- race on the
+ * array and give wrong results; calls in order on one stream are safe.
+ * Other arguments, errors and supported shapes: as pa_decode.
+ */
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache,
+                            const void* v_cache, int64_t num_blocks,
+                            int32_t block_size, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq,
+                            const int32_t* context_lens,
+                            int32_t max_context_len, int32_t num_seqs,
+                            int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, float scale, pa_dtype dtype,
+                            void* stream);
 
 /* Bytes of workspace pa_prefill_varlen needs for these sizes: the work
  * schedule, one int32 per (sequence, 128-row M-tile) item (0 when

@@ -20,6 +20,7 @@ STATUS = {
     3: "PA_ERR_UNSUPPORTED",
     4: "PA_ERR_WORKSPACE",
     5: "PA_ERR_LAUNCH",
+    6: "PA_ERR_SCRATCH_LIMIT",
 }
 
 _c_void_p = ctypes.c_void_p
@@ -41,6 +42,10 @@ SIGNATURES = {
         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32,
         _c_void_p, _i32, _c_void_p, _i32, _i32, _i32, _i32, _i32, _f32,
         _c_void_p, _size, ctypes.c_int, _c_void_p]),
+    "pa_decode_noalloc": (ctypes.c_int, [
+        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32,
+        _c_void_p, _i32, _c_void_p, _i32, _i32, _i32, _i32, _i32, _f32,
+        ctypes.c_int, _c_void_p]),
     "pa_prefill_workspace_bytes": (_size, [_i32, _i32, _i32, _i32, _i32,
                                            _i32]),
     "pa_prefill_varlen": (ctypes.c_int, [

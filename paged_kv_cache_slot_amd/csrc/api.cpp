@@ -57,6 +57,10 @@ const char* pa_status_string(pa_status status) {
     case PA_ERR_WORKSPACE:
       return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: kernel launch failed";
+    case PA_ERR_SCRATCH_LIMIT:
+      return "PA_ERR_SCRATCH_LIMIT: these sizes need more workspace than the "
+             "library's static 32 MiB decode scratch holds; call pa_decode "
+             "with a workspace instead";
   }
   return "PA_ERR_?: unknown status";
 }
@@ -167,6 +171,56 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads,
     return 0;
   return pa::prefill_workspace_bytes(num_seqs, num_heads, num_kv_heads,
                                      head_dim, max_seqlen_q, max_seqlen_k);
+}
+
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache,
+                            const void* v_cache, int64_t num_blocks,
+                            int32_t block_size, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq,
+                            const int32_t* context_lens,
+                            int32_t max_context_len, int32_t num_seqs,
+                            int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, float scale, pa_dtype dtype,
+                            void* stream) {
+  pa_status st = check_attention(block_size, num_seqs, num_heads, num_kv_heads,
+                                 head_dim, max_blocks_per_seq, num_blocks,
+                                 dtype);
+  if (st != PA_OK) return st;
+  if (max_context_len < 0) return PA_ERR_SHAPE;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !context_lens) return PA_ERR_NULL;
+  if (max_context_len > 0 && (!k_cache || !v_cache || !block_tables))
+    return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return PA_ERR_UNSUPPORTED;
+  const pa::DecodePlan plan = pa::plan_decode(num_seqs, num_heads, num_kv_heads,
+                                              head_dim, max_context_len);
+  if (plan.workspace_bytes > pa::kDecodeScratchBytes) return PA_ERR_SCRATCH_LIMIT;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  void* scratch = nullptr;
+  if (plan.workspace_bytes > 0 && pa::decode_scratch(s, &scratch) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_blocks = num_blocks;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.max_context_len = max_context_len;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.scale = scale;
+  a.workspace = scratch;
+  a.bf16 = dtype == PA_BF16;
+  hipError_t e = pa::launch_decode(a, plan, s);
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 pa_status pa_prefill_varlen(void* out, const void* q, int64_t total_q,

@@ -50,6 +50,8 @@
 //    unused slots cannot reach the output.
 #include <math.h>
 
+#include <mutex>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -1056,6 +1058,47 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan,
     if (plan.use_order) prm.order = reinterpret_cast<int32_t*>(ws + plan.off_order);
   }
   return dispatch_decode(prm, a, stream);
+}
+
+// Workspace of the no-allocation decode: a file-scope device array, of which
+// every GPU that loads the library holds its own copy for the life of the
+// process.  Host code never uses its name as an address (on the host it is
+// only a stand-in for the symbol); the device address comes from
+// hipGetSymbolAddress, per device.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(hipStream_t stream, void** ptr) {
+  int dev = 0;
+  hipError_t e = stream == nullptr ? hipGetDevice(&dev)
+                                   : hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    // Look the symbol up with the stream's device current: each device has
+    // its own copy of the array at its own address.
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode_suffix(const DecodeArgs& a, const SharedPrefixPlan& plan,

@@ -70,6 +70,15 @@ struct DecodeArgs {
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan,
                          hipStream_t stream);
 
+// Size of the library's static decode scratch array (one per GPU, kept
+// until the process ends): the workspace of pa_decode_noalloc.
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+
+// Device address of the static scratch array on the device `stream`
+// belongs to (the current device for the null stream).  The address is
+// looked up once per device, with that device current, and cached.
+hipError_t decode_scratch(hipStream_t stream, void** ptr);
+
 // ---- shared-prefix (cascade) decode ------------------------------------
 struct SharedPrefixPlan {
   DecodePlan suffix;         // partitions over [prefix, L_b) (workspace unused)

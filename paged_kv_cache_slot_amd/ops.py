@@ -163,6 +163,42 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
     return out
 
 
+DECODE_SCRATCH_BYTES = 32 << 20   # the library's static decode scratch
+
+
+def decode_noalloc(q, k_cache, v_cache, block_tables, context_lens,
+                   max_context_len, scale=None, out=None):
+    """decode() without a workspace: the library keeps the partial results
+    in its static per-GPU scratch (32 MiB), so the C call allocates nothing.
+    Calls that overlap on one GPU race on that scratch.  With ``out`` given,
+    this function allocates nothing either."""
+    _check_out(out, q)
+    _need_gpu(q, k_cache, v_cache, block_tables, context_lens, out)
+    _i32(block_tables, "block_tables")
+    _i32(context_lens, "context_lens")
+    b, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if d2 != d or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shape does not match q")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b:
+        raise ValueError("block_tables must be [B, W]")
+    if context_lens.numel() != b:
+        raise ValueError("context_lens must be [B]")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and caches must share a dtype")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    lib = _lib.load()
+    st = lib.pa_decode_noalloc(_ptr(out), _ptr(q), _ptr(k_cache),
+                               _ptr(v_cache), nb, bs, _ptr(block_tables),
+                               block_tables.shape[1], _ptr(context_lens),
+                               int(max_context_len), b, hq, hkv, d, scale,
+                               _dtype_code(q), _stream(q))
+    _lib.check("pa_decode_noalloc", st)
+    return out
+
+
 def shared_prefix_workspace_bytes(num_seqs, num_heads, num_kv_heads,
                                   head_dim, max_suffix_len, max_prefix_len,
                                   num_groups, max_group_size):

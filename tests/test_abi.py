@@ -85,6 +85,42 @@ def test_decode_validation(kw, code, no_device):
     assert _decode(_lib.load(), **kw) == code
 
 
+def _decode_noalloc(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, nb=64, bs=16, bt=FAKE, w=8,
+             cl=FAKE, maxlen=100, b=4, hq=8, hkv=2, d=64, scale=0.125,
+             dtype=_lib.PA_F32, stream=None)
+    a.update(kw)
+    return lib.pa_decode_noalloc(
+        a["out"], a["q"], a["k"], a["v"], a["nb"], a["bs"], a["bt"], a["w"],
+        a["cl"], a["maxlen"], a["b"], a["hq"], a["hkv"], a["d"], a["scale"],
+        a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(b=-1), 2), (dict(hkv=3), 2), (dict(d=96), 3), (dict(bs=32), 3),
+    (dict(hq=32, hkv=2), 3), (dict(dtype=9), 3), (dict(maxlen=-1), 2),
+    (dict(scale=0.0), 2), (dict(scale=float("inf")), 2),
+    (dict(out=None), 1), (dict(cl=None), 1), (dict(bt=None), 1),
+    (dict(q=MISALIGNED), 3),
+    (dict(b=0), 0),                                # empty batch: no-op
+    # 64 sequences x 64 query heads over 2^20-token contexts: ~272 MB of
+    # partials, past the 32 MiB static scratch -> rejected, nothing launched
+    (dict(b=64, hq=64, hkv=8, d=128, maxlen=1 << 20, dtype=_lib.PA_BF16), 6),
+])
+def test_decode_noalloc_validation(kw, code, no_device):
+    assert _decode_noalloc(_lib.load(), **kw) == code
+
+
+def test_decode_noalloc_limit_matches_workspace_query():
+    """The static scratch is 32 MiB: sizes whose pa_decode workspace fits
+    are the ones pa_decode_noalloc accepts."""
+    lib = _lib.load()
+    big = lib.pa_decode_workspace_bytes(64, 64, 8, 128, 1 << 20)
+    assert big > 32 << 20
+    fits = lib.pa_decode_workspace_bytes(256, 32, 8, 128, 8192)
+    assert 0 < fits <= 32 << 20
+
+
 def test_decode_workspace_query():
     lib = _lib.load()
     assert lib.pa_decode_workspace_bytes(4, 8, 2, 64, 100) == 0
