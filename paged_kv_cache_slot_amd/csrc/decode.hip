@@ -107,10 +107,12 @@ struct DecodeShape {
   // bf16 PV runs on v_dot2 over token pairs (i, i + 1 of a lane's tokens).
   static constexpr bool kPairPv = sizeof(T) == 2 && V::kTpl % 2 == 0;
   static constexpr int kPairsPerBlock = kBlock / 2;
-  // Register floor of 3 waves per SIMD (168 VGPRs) for bf16 with G <= 4:
-  // the chunk loop keeps the output accumulators live through the QK pass,
-  // and a tighter cap made the compiler spill (measured slower).
-  static constexpr int kMinWaves = (sizeof(T) == 2 && G <= 4) ? 3 : 1;
+  // Register floor per SIMD for bf16: 5 waves (96 VGPRs) with G <= 2, 3
+  // waves (168) with G = 4.  The chunk loop keeps the output accumulators
+  // live through the QK pass; a tighter cap for G = 4 made the compiler
+  // spill (measured slower).
+  static constexpr int kMinWaves =
+      sizeof(T) == 2 ? (G <= 2 ? 5 : (G <= 4 ? 3 : 1)) : 1;
   // Blocks each wave has in flight: the next block's K (or V) is loaded
   // while the current one is consumed.  Deeper prefetch was measured and
   // gains nothing.
@@ -215,8 +217,9 @@ struct DecodeParams {
   int num_kv_heads;
   float scale_log2;  // scale * log2(e): logits live in the base-2 domain
   float* ws_max;     // [B, Hq, ws_stride]   (multi-partition only)
-  float* ws_sum;     // [B, Hq, ws_stride]
-  float* ws_acc;     // [B, Hq, ws_stride, D]
+  float* ws_sum;     // [B, Hq, ws_stride]; negative: partial stored scaled
+  float* ws_acc;     // [B, Hq, ws_stride, D]: fp32 acc (fp32 I/O)
+  uint16_t* ws_acc_h;  // same memory: binary16 acc / l (bfloat16 I/O)
   int num_partitions;
   int partition_tokens;  // tokens per partition, a multiple of the chunk
   int ws_stride;         // partial slots per (sequence, head) >= num_partitions
@@ -723,23 +726,49 @@ decode_partition_kernel(
   }
   __syncthreads();
 
-  for (int i = tid; i < G * D; i += kThreads) {
-    const int h = i / D;
-    const int d = i % D;
-    float o = 0.f;
+  // Head h is written by wave h % kWaves (lanes cover its D dimensions), so
+  // a per-head decision is one wave vote.
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) o += s_acc[w][h][d];
+  for (int h = wave; h < G; h += kWaves) {
     const int64_t head = static_cast<int64_t>(b) * p.num_heads + head0 + h;
+    const float l = s_lrun[h];
+    float ov[D / kWave];
+#pragma unroll
+    for (int e = 0; e < D / kWave; ++e) {
+      ov[e] = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) ov[e] += s_acc[w][h][e * kWave + lane];
+    }
     if (single) {
-      const float l = s_lrun[h];
-      T* out = reinterpret_cast<T*>(p.out) + head * D + d;
-      store_out<T>(out, l > 0.f ? o / l * p.v_scale : 0.f);
-    } else {
-      const int64_t slot = head * p.ws_stride + part;
-      p.ws_acc[slot * D + d] = o;
-      if (d == 0) {
+      T* out = reinterpret_cast<T*>(p.out) + head * D;
+#pragma unroll
+      for (int e = 0; e < D / kWave; ++e)
+        store_out<T>(out + e * kWave + lane, l > 0.f ? ov[e] / l * p.v_scale : 0.f);
+      continue;
+    }
+    const int64_t slot = head * p.ws_stride + part;
+    if constexpr (sizeof(T) == 2) {
+      // Normalised binary16 partial (see kPartialBig).
+      bool big = false;
+#pragma unroll
+      for (int e = 0; e < D / kWave; ++e) {
+        ov[e] = l > 0.f ? ov[e] / l : 0.f;
+        big = big || fabsf(ov[e]) >= kPartialBig;
+      }
+      big = __any(big);
+#pragma unroll
+      for (int e = 0; e < D / kWave; ++e)
+        p.ws_acc_h[slot * D + e * kWave + lane] = partial_f16(ov[e], big);
+      if (lane == 0) {
         p.ws_max[slot] = s_mrun[h];
-        p.ws_sum[slot] = s_lrun[h];
+        p.ws_sum[slot] = big ? -l : l;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < D / kWave; ++e) p.ws_acc[slot * D + e * kWave + lane] = ov[e];
+      if (lane == 0) {
+        p.ws_max[slot] = s_mrun[h];
+        p.ws_sum[slot] = l;
       }
     }
   }
@@ -767,6 +796,20 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
   const float* mx = p.ws_max + head * p.ws_stride;
   const float* sm = p.ws_sum + head * p.ws_stride;
   const float* ac = p.ws_acc + head * p.ws_stride * D + d;
+  const uint16_t* ach = p.ws_acc_h + head * p.ws_stride * D + d;
+  // Partial k as (sum l, unnormalised output l * o): fp32 acc for fp32 I/O,
+  // binary16 o (scaled by 2^-16 where l is stored negated) for bfloat16.
+  auto load_partial = [&](int k, float& l, float& acc) __attribute__((always_inline)) {
+    const float lraw = sm[k];
+    if constexpr (sizeof(T) == 2) {
+      const float o = f16_to_f32(ach[static_cast<int64_t>(k) * D]);
+      l = fabsf(lraw);
+      acc = l * (lraw < 0.f ? o * kPartialGrow : o);
+    } else {
+      l = lraw;
+      acc = ac[static_cast<int64_t>(k) * D];
+    }
+  };
   // Slots 0 .. np - 1 (this call's partitions), then num_partitions ..
   // num_partitions + npre - 1 (the prefix partials).
   auto slot = [&](int i) { return i < np ? i : p.num_partitions + (i - np); };
@@ -787,8 +830,7 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
       if (i0 + u < n) {                       // uniform over the workgroup
         const int k = slot(i0 + u);
         mv[u] = mx[k];
-        sv[u] = sm[k];
-        av[u] = ac[static_cast<int64_t>(k) * D];
+        load_partial(k, sv[u], av[u]);
       }
     }
     float gm = m;
@@ -837,15 +879,30 @@ __device__ __forceinline__ int plan_bin(const DecodeParams& p, int item) {
   return bin < kPlanBins ? bin : kPlanBins - 1;
 }
 
+// Items of the first kPlanRegItems rounds keep their bin in registers, so
+// the second pass does not load the context lengths again.
+constexpr int kPlanRegItems = 4;
+
 __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(
     DecodeParams p, int32_t* __restrict__ order) {
   __shared__ int bins[kPlanBins];
   __shared__ int wave_sum[kPlanThreads / kWave];
   const int tid = threadIdx.x;
   const int n = p.num_seqs * p.num_partitions;
+  // Bins of this thread's first items (their context lengths are loaded
+  // while the bins are cleared).
+  int mybin[kPlanRegItems];
+#pragma unroll
+  for (int k = 0; k < kPlanRegItems; ++k) {
+    const int item = tid + k * kPlanThreads;
+    mybin[k] = item < n ? plan_bin(p, item) : 0;
+  }
   for (int i = tid; i < kPlanBins; i += kPlanThreads) bins[i] = 0;
   __syncthreads();
-  for (int item = tid; item < n; item += kPlanThreads)
+#pragma unroll
+  for (int k = 0; k < kPlanRegItems; ++k)
+    if (tid + k * kPlanThreads < n) atomicAdd(&bins[mybin[k]], 1);
+  for (int item = tid + kPlanRegItems * kPlanThreads; item < n; item += kPlanThreads)
     atomicAdd(&bins[plan_bin(p, item)], 1);
   __syncthreads();
   // Exclusive prefix from the heaviest bin down: a scan inside each wave,
@@ -876,7 +933,12 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(
     start += cnt[k];
   }
   __syncthreads();
-  for (int item = tid; item < n; item += kPlanThreads)
+#pragma unroll
+  for (int k = 0; k < kPlanRegItems; ++k) {
+    const int item = tid + k * kPlanThreads;
+    if (item < n) order[atomicAdd(&bins[mybin[k]], 1)] = item;
+  }
+  for (int item = tid + kPlanRegItems * kPlanThreads; item < n; item += kPlanThreads)
     order[atomicAdd(&bins[plan_bin(p, item)], 1)] = item;
 }
 
@@ -1055,6 +1117,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan,
     prm.ws_max = reinterpret_cast<float*>(ws + plan.off_max);
     prm.ws_sum = reinterpret_cast<float*>(ws + plan.off_sum);
     prm.ws_acc = reinterpret_cast<float*>(ws + plan.off_acc);
+    prm.ws_acc_h = reinterpret_cast<uint16_t*>(ws + plan.off_acc);
     if (plan.use_order) prm.order = reinterpret_cast<int32_t*>(ws + plan.off_order);
   }
   return dispatch_decode(prm, a, stream);
@@ -1129,6 +1192,7 @@ hipError_t launch_decode_suffix(const DecodeArgs& a, const SharedPrefixPlan& pla
   prm.ws_max = reinterpret_cast<float*>(ws + plan.off_max);
   prm.ws_sum = reinterpret_cast<float*>(ws + plan.off_sum);
   prm.ws_acc = reinterpret_cast<float*>(ws + plan.off_acc);
+  prm.ws_acc_h = reinterpret_cast<uint16_t*>(ws + plan.off_acc);
   if (plan.suffix.use_order)
     prm.order = reinterpret_cast<int32_t*>(ws + plan.suffix.off_order);
   return dispatch_decode(prm, a, stream);

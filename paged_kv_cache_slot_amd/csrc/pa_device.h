@@ -108,6 +108,29 @@ __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }
 
+// float <-> IEEE binary16 bits (v_cvt_f16_f32 rounds to nearest even).
+__device__ __forceinline__ uint16_t f32_to_f16(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// Partial results of a split (partitioned) attention row with bfloat16 I/O
+// are stored normalised, o = acc / l, as binary16: half the bytes of fp32,
+// and interleaved partial writes slow the K/V read stream far beyond their
+// own size.  A partial with |o| >= 2^15 somewhere is stored as o * 2^-16
+// and flagged by storing its sum l negated; the merge undoes both.
+constexpr float kPartialBig = 32768.f;
+constexpr float kPartialShrink = 1.f / 65536.f;
+constexpr float kPartialGrow = 65536.f;
+constexpr float kHalfMax = 65504.f;
+
+__device__ __forceinline__ uint16_t partial_f16(float o, bool big) {
+  const float v = big ? o * kPartialShrink : o;
+  return f32_to_f16(fminf(fmaxf(v, -kHalfMax), kHalfMax));
+}
+
 // 16-byte global load / store.
 __device__ __forceinline__ uint4 ld16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);

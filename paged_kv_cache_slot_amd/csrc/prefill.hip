@@ -159,8 +159,9 @@ struct PrefillParams {
   int chunk_tiles;
   int chunks;
   float* ws_max;
-  float* ws_sum;
-  float* ws_acc;
+  float* ws_sum;       // negative: the partial is stored scaled (bf16 I/O)
+  float* ws_acc;       // fp32 acc (fp32 I/O)
+  uint16_t* ws_acc_h;  // same memory: binary16 acc / sum (bfloat16 I/O)
   int ws_stride;
   int slot0;
 };
@@ -751,21 +752,48 @@ prefill_kernel(PrefillParams p) {
   const float total = run_sum + swap_halves(run_sum);
   if (!row_ok) return;
   if (p.group_mode) {
-    // A partial: the unnormalised output, its reference max and its sum.
+    // A partial: its output (bf16 I/O: normalised, binary16; fp32 I/O: the
+    // unnormalised fp32 sum), its reference max and its sum.
     const int64_t slot =
         ((static_cast<int64_t>(q0) + i_pos) * p.num_heads + kvh * G + h) *
             p.ws_stride + p.slot0 + chunk;
-    float* acc = p.ws_acc + slot * D;
+    if constexpr (S::kBf16) {
+      const float inv = total > 0.f ? 1.f / total : 0.f;
+      float big = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < S::kDTiles; ++dt)
+      for (int dt = 0; dt < S::kDTiles; ++dt)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-        *reinterpret_cast<float4*>(acc + dt * 32 + g4 * 8 + hh * 4) =
-            make_float4(oacc[dt][g4 * 4], oacc[dt][g4 * 4 + 1],
-                        oacc[dt][g4 * 4 + 2], oacc[dt][g4 * 4 + 3]);
-    if (hh == 0) {
-      p.ws_max[slot] = run_max;
-      p.ws_sum[slot] = total;
+        for (int r = 0; r < 16; ++r) big = fmaxf(big, fabsf(oacc[dt][r] * inv));
+      const bool is_big = fmaxf(big, swap_halves(big)) >= kPartialBig;   // whole row
+      uint16_t* acc = p.ws_acc_h + slot * D;
+#pragma unroll
+      for (int dt = 0; dt < S::kDTiles; ++dt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          uint16_t hv[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) hv[u] = partial_f16(oacc[dt][g4 * 4 + u] * inv, is_big);
+          *reinterpret_cast<uint2*>(acc + dt * 32 + g4 * 8 + hh * 4) =
+              make_uint2(hv[0] | (static_cast<uint32_t>(hv[1]) << 16),
+                         hv[2] | (static_cast<uint32_t>(hv[3]) << 16));
+        }
+      if (hh == 0) {
+        p.ws_max[slot] = run_max;
+        p.ws_sum[slot] = is_big ? -total : total;
+      }
+    } else {
+      float* acc = p.ws_acc + slot * D;
+#pragma unroll
+      for (int dt = 0; dt < S::kDTiles; ++dt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *reinterpret_cast<float4*>(acc + dt * 32 + g4 * 8 + hh * 4) =
+              make_float4(oacc[dt][g4 * 4], oacc[dt][g4 * 4 + 1],
+                          oacc[dt][g4 * 4 + 2], oacc[dt][g4 * 4 + 3]);
+      if (hh == 0) {
+        p.ws_max[slot] = run_max;
+        p.ws_sum[slot] = total;
+      }
     }
     return;
   }
@@ -1023,6 +1051,7 @@ hipError_t launch_prefix_partials(const PrefixArgs& a,
   prm.ws_max = reinterpret_cast<float*>(ws + plan.off_max);
   prm.ws_sum = reinterpret_cast<float*>(ws + plan.off_sum);
   prm.ws_acc = reinterpret_cast<float*>(ws + plan.off_acc);
+  prm.ws_acc_h = reinterpret_cast<uint16_t*>(ws + plan.off_acc);
   prm.ws_stride = plan.total_slots;
   prm.slot0 = plan.suffix.num_partitions;
   if (a.bf16) {

@@ -178,3 +178,36 @@ def test_very_long_context(dtype, longest):
     lay = wl.decode_layout(lens, 16, seed=9401)
     case = DecodeCase(lay, 8, 2, 128, dtype, seed=9402)
     _check(case)
+
+
+def _scale_v(case, factor):
+    """Multiply the V pool and the new V rows by a power of two (exact in
+    bf16 and fp32) and retake the oracle's host copies."""
+    case.vc.mul_(factor)
+    case.v_new.mul_(factor)
+    case.h_vc = wl.host_bits(case.vc)
+    case.h_vn = wl.host_bits(case.v_new)
+
+
+def test_large_values_split_context():
+    """V values near 2^20 (bf16): split-context partials whose normalised
+    outputs reach 2^15 are stored scaled (flagged by a negative sum) and
+    must merge back exactly; 18 partitions per long sequence, so the merge
+    also folds several groups of partials.  Checked relative to the output
+    size (bf16 outputs of ~1e5 are 256-512 apart)."""
+    say("decode large values, split context")
+    lay = wl.decode_layout([3000, 9000, 700, 5000], 16, seed=91)
+    case = DecodeCase(lay, 32, 8, 128, "bf16", seed=92)
+    _scale_v(case, 2.0 ** 20)
+    case.run_store()
+    out = case.run_decode()
+    torch.cuda.synchronize()
+    ek, ev = case.oracle_store()
+    assert bits_equal(wl.host_bits(case.vc), ev), "store mismatch"
+    want = case.oracle_decode(ek, ev)
+    got = f64(out)
+    assert np.all(np.isfinite(got))
+    big = np.max(np.abs(want))
+    assert big > 65504, "the case must exceed the binary16 range"
+    err = float(np.max(np.abs(got - want)))
+    assert err <= big * 2.0 ** -7, (err, big)

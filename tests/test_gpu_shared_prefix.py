@@ -120,3 +120,33 @@ def test_prefix_workload_full_size_sampled():
                       cfg.dtype, seed=cfg.seed)
     _run(case, seqs=sample_seqs(lay.lens, 10, cfg.seed),
          expect_groups=[(0, 128)])
+
+
+def test_large_values_prefix_partials():
+    """V values near 2^20 (bf16): the prefix pass's partials and the suffix
+    partitions' partials reach 2^15 and are stored scaled; the merge must
+    undo it.  Checked relative to the output size."""
+    say("shared prefix large values")
+    case = DecodeCase(_grouped_layout(SPEC, seed=93), 32, 8, 128, "bf16",
+                      seed=94)
+    case.vc.mul_(2.0 ** 20)
+    case.v_new.mul_(2.0 ** 20)
+    case.h_vc = wl.host_bits(case.vc)
+    case.h_vn = wl.host_bits(case.v_new)
+    case.run_store()
+    sp = pm.shared_prefix_inputs(case.tables, case.lens, case.bs)
+    assert len(sp["groups"]) > 0
+    out = ops.decode_shared_prefix(
+        case.q, case.kc, case.vc, case.block_tables, case.context_lens,
+        dev_i32(sp["prefix_lens"]),
+        dev_i32(sp["groups"].reshape(-1, 2)), sp["max_suffix_len"],
+        sp["max_prefix_len"], sp["max_group_size"], scale=case.scale)
+    torch.cuda.synchronize()
+    ek, ev = case.oracle_store()
+    want = case.oracle_decode(ek, ev)
+    got = f64(out)
+    assert np.all(np.isfinite(got))
+    big = np.max(np.abs(want))
+    assert big > 65504
+    err = float(np.max(np.abs(got - want)))
+    assert err <= big * 2.0 ** -7, (err, big)
