@@ -64,6 +64,12 @@ def parse():
     ap.add_argument("--fp8-steps", type=int, default=20,
                     help="timed steps of the 8B-shaped decode step over an "
                          "8-bit (E4M3) cache (0 skips it)")
+    ap.add_argument("--indirection-steps", type=int, default=20,
+                    help="timed calls per placement of the block-table "
+                         "indirection leg (0 skips it)")
+    ap.add_argument("--no-check", action="store_true",
+                    help="skip the oracle check of each timed workload's "
+                         "outputs")
     ap.add_argument("--flush-mb", type=int, default=512,
                     help="MiB read between timed steps (outside the timed "
                          "events) so that no step reads the previous step's "
@@ -85,6 +91,11 @@ class Flusher:
     def __call__(self):
         if self.buf is not None:
             self.sink = [self.buf.sum()]
+
+
+def f64(t):
+    import torch
+    return t.detach().to("cpu", torch.float64).numpy()
 
 
 def stats_ms(ms):
@@ -170,7 +181,7 @@ def cpu_prefill_baseline(h_q, h_kc, h_vc, cu_q, cu_k, tables, hq, d, scale,
     return done, flops, time.perf_counter() - t0
 
 
-def run_mixed(steps, warmup, dev, flush, cpu_s=0.0):
+def run_mixed(steps, warmup, dev, flush, cpu_s=0.0, check=True):
     """Mixed step: one pa_store_kv of every new row (8 x 512 chunk rows + 192
     decode rows), then pa_prefill_varlen of the chunks, then pa_decode of the
     decode rows, on one stream.  Returns a dict for the JSON line."""
@@ -201,6 +212,9 @@ def run_mixed(steps, warmup, dev, flush, cpu_s=0.0):
     btd = torch.as_tensor(md["block_tables"], device=dev)
     cl = torch.as_tensor(md["context_lens"], device=dev)
     scale = 1.0 / math.sqrt(d)
+    # host copies for the oracle check, taken before any kernel runs
+    host = [wl.host_bits(x) for x in (kc, vc, k_new, v_new, qp, qd)] \
+        if check else None
     outp = torch.empty_like(qp)
     outd = torch.empty_like(qd)
     wsd = torch.empty(max(ops.decode_workspace_bytes(
@@ -258,9 +272,16 @@ def run_mixed(steps, warmup, dev, flush, cpu_s=0.0):
                "sample": f"{done} of {len(pre.chunk)} chunks "
                          f"({cflops / 1e9:.1f} GFLOP), fp64 numpy oracle, "
                          f"{dt:.1f} s"}
+    chk = None
+    if check:
+        chk = cpu_check_mixed(pre, dec, *host[:4], host[4], host[5],
+                              f64(outp), f64(outd), scale,
+                              {b: [0, 255, 511] for b in range(len(pre.chunk))},
+                              sample_sequences(dec.lens, 10, 5))
     return {
         "workload": cfg.title,
         "steps": steps,
+        "check": chk,
         "ms_per_step": round(total, 4),
         "store_us": round(st * 1e3, 2),
         "store_gbs": round(sbytes / (st * 1e-3) / 1e9, 1),
@@ -281,7 +302,7 @@ def run_mixed(steps, warmup, dev, flush, cpu_s=0.0):
     }
 
 
-def run_prefix(steps, warmup, dev, flush, cpu_s=0.0):
+def run_prefix(steps, warmup, dev, flush, cpu_s=0.0, check=True):
     """Prefix-sharing decode step: pa_store_kv of each sequence's new token
     (private suffix blocks), then pa_decode; 128 sequences share their first
     128 blocks.  Reports unique-byte (each physical block once) and
@@ -306,6 +327,8 @@ def run_prefix(steps, warmup, dev, flush, cpu_s=0.0):
     bt = torch.as_tensor(meta["block_tables"], device=dev)
     cl = torch.as_tensor(meta["context_lens"], device=dev)
     scale = 1.0 / math.sqrt(d)
+    host = [wl.host_bits(x) for x in (q, kc, vc, k_new, v_new)] \
+        if check else None
     out = torch.empty_like(q)
     ws = torch.empty(max(ops.decode_workspace_bytes(
         b, hq, hkv, d, meta["max_context_len"]), 1), dtype=torch.uint8,
@@ -351,6 +374,13 @@ def run_prefix(steps, warmup, dev, flush, cpu_s=0.0):
     dec = timed(attend_plain)
     shared = timed(attend_shared)
     diff = float((out.float() - out2.float()).abs().max())
+    chk = chk2 = None
+    if check:
+        seqs = sample_sequences(lay.lens, 8, 4)
+        chk = cpu_check_decode(lay.tables, lay.lens, *host, f64(out), scale,
+                               "bf16", seqs)
+        chk2 = cpu_check_decode(lay.tables, lay.lens, *host, f64(out2), scale,
+                                "bf16", seqs)
     row = 2 * hkv * d * 2
     logical = decode_bytes(lay.lens, hq, hkv, d, 2)
     pre_tok = cfg.shared_prefix_blocks * bs
@@ -371,6 +401,7 @@ def run_prefix(steps, warmup, dev, flush, cpu_s=0.0):
         "workload": cfg.title,
         "steps": steps,
         "cpu_baseline": cpu,
+        "check": chk,
         "decode_us": round(dec * 1e3, 2),
         "unique_bytes": unique,
         "logical_bytes": logical,
@@ -389,11 +420,12 @@ def run_prefix(steps, warmup, dev, flush, cpu_s=0.0):
             "decode_tokens_per_s": round(b / (shared * 1e-3), 1),
             "speedup_vs_pa_decode": round(dec / shared, 3),
             "max_abs_diff_vs_pa_decode": round(diff, 6),
+            "check": chk2,
         },
     }
 
 
-def run_fp8(steps, warmup, dev, flush):
+def run_fp8(steps, warmup, dev, flush, check=True):
     """The 8B-shaped decode step over an 8-bit (E4M3) cache: pa_store_kv_fp8
     of the 256 new rows, then pa_decode_fp8.  Bytes count one byte per
     cached element."""
@@ -421,6 +453,8 @@ def run_fp8(steps, warmup, dev, flush):
     ws = torch.empty(max(ops.decode_workspace_bytes(b, hq, hkv, d, maxlen), 1),
                      dtype=torch.uint8, device=dev)
     ks, vs = 1 / 16, 1 / 16
+    host = [wl.host_bits(x) for x in (q, kc, vc, k_new, v_new)] \
+        if check else None
 
     def step(ev):
         ev[0].record()
@@ -445,9 +479,15 @@ def run_fp8(steps, warmup, dev, flush):
     stp = float(np.median(step_all))
     dbytes = decode_bytes(lay.lens, hq, hkv, d, 1) + \
         len(lay.lens) * hq * d * (2 - 1) * 2      # q and out stay bf16
+    chk = None
+    if check:
+        chk = cpu_check_fp8_decode(lay.tables, lay.lens, *host, f64(out),
+                                   1.0 / math.sqrt(d), ks, vs,
+                                   sample_sequences(lay.lens, 6, 3))
     return {
         "workload": cfg.title + "; 8-bit E4M3 cache",
         "steps": steps,
+        "check": chk,
         "decode_us": round(dec * 1e3, 2),
         "step_us": round(stp * 1e3, 2),
         "decode_ms_stats": stats_ms(dec_all),
@@ -459,7 +499,7 @@ def run_fp8(steps, warmup, dev, flush):
     }
 
 
-def run_tiny(steps, warmup, dev, flush):
+def run_tiny(steps, warmup, dev, flush, check=True):
     """Tiny decode step (4 sequences, contexts 7 / 16 / 33 / 100, 8 query /
     2 KV heads, D = 64, fp32): pa_store_kv of the 4 newest rows, then
     pa_decode.  Launch-bound; reported in microseconds."""
@@ -486,6 +526,8 @@ def run_tiny(steps, warmup, dev, flush):
     out = torch.empty_like(q)
     ws = torch.empty(max(ops.decode_workspace_bytes(b, hq, hkv, d, maxlen), 1),
                      dtype=torch.uint8, device=dev)
+    host = [wl.host_bits(x) for x in (q, kc, vc, k_new, v_new)] \
+        if check else None
 
     def step(ev):
         ev[0].record()
@@ -505,9 +547,14 @@ def run_tiny(steps, warmup, dev, flush):
     torch.cuda.synchronize()
     step_all = [e[0].elapsed_time(e[2]) for e in evs[:steps]]
     dec_all = [e[1].elapsed_time(e[2]) for e in evs[:steps]]
+    chk = None
+    if check:
+        chk = cpu_check_decode(lay.tables, lay.lens, *host, f64(out),
+                               1.0 / math.sqrt(d), "f32", list(range(b)))
     return {
         "workload": cfg.title + "; store 4 rows then decode",
         "steps": steps,
+        "check": chk,
         "step_us": round(float(np.median(step_all)) * 1e3, 2),
         "decode_us": round(float(np.median(dec_all)) * 1e3, 2),
         "step_ms_stats": stats_ms(step_all),
@@ -516,7 +563,7 @@ def run_tiny(steps, warmup, dev, flush):
     }
 
 
-def run_small(steps, warmup, dev, flush, cpu_s=0.0):
+def run_small(steps, warmup, dev, flush, cpu_s=0.0, check=True):
     """Small-model decode: 64 sequences, contexts uniform in [128, 4096],
     16 query / 8 KV heads, D = 128, bf16.  Decode only: the cache is filled
     up front, so the timed call is pa_decode."""
@@ -540,6 +587,7 @@ def run_small(steps, warmup, dev, flush, cpu_s=0.0):
     out = torch.empty_like(q)
     ws = torch.empty(max(ops.decode_workspace_bytes(b, hq, hkv, d, maxlen), 1),
                      dtype=torch.uint8, device=dev)
+    host = [wl.host_bits(x) for x in (q, kc, vc)] if check else None
 
     def call(ev):
         ev[0].record()
@@ -568,10 +616,16 @@ def run_small(steps, warmup, dev, flush, cpu_s=0.0):
                "kind": "oracle", "tokens_per_s": round(done / dt, 2),
                "sample": f"{done} of {b} sequences ({toks} context tokens), "
                          f"fp64 numpy oracle, {dt:.1f} s"}
+    chk = None
+    if check:
+        chk = cpu_check_decode(lay.tables, lay.lens, *host, None, None,
+                               f64(out), 1.0 / math.sqrt(d), "bf16",
+                               sample_sequences(lay.lens, 8, 2))
     return {
         "workload": cfg.title,
         "steps": steps,
         "cpu_baseline": cpu,
+        "check": chk,
         "decode_us": round(dec * 1e3, 2),
         "decode_ms_stats": stats_ms(dec_all),
         "algorithmic_bytes": dbytes,
@@ -580,6 +634,183 @@ def run_small(steps, warmup, dev, flush, cpu_s=0.0):
         "tokens_per_s": round(b / (dec * 1e-3), 1),
         "kernel": "pa_decode (plan + decode_partition_kernel + decode_merge_kernel)",
     }
+
+
+def run_indirection(steps, warmup, dev, flush):
+    """Cost of the block-table indirection ("Warmup Guide -- Inference
+    Serving Internals", Chapter 3 calls it cheap): the 8B-shaped decode
+    workload's tokens are placed twice -- once with each sequence's blocks
+    at consecutive physical ids, once through the workload's shuffled block
+    tables -- by pa_store_kv of the same rows, and pa_decode is timed on
+    both, interleaved, with the cache flushed before every call.  The same
+    tokens in the same logical order give bit-identical outputs."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from paged_kv_cache_slot_amd import metadata as pm
+    from paged_kv_cache_slot_amd import ops
+
+    cfg = wl.get_config(WORKLOAD)
+    lay = wl.config_decode_layout(cfg)
+    hq, hkv, d, bs = cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, 16
+    b = len(lay.lens)
+    counts = [-(-int(n) // bs) for n in lay.lens]
+    starts = np.cumsum([0] + counts[:-1])
+    consecutive = [np.arange(s0, s0 + c) for s0, c in zip(starts, counts)]
+    total = int(sum(int(n) for n in lay.lens))
+    k_all = wl.make_values((total, hkv, d), "bf16", cfg.seed + 10, dev)
+    v_all = wl.make_values((total, hkv, d), "bf16", cfg.seed + 11, dev)
+    q = wl.make_values((b, hq, d), "bf16", cfg.seed + 12, dev)
+    zeros = np.zeros(b, dtype=np.int64)
+    placements = []
+    for name, tables, nb in (("consecutive", consecutive, int(sum(counts))),
+                             ("permuted", lay.tables, lay.num_blocks)):
+        kc = torch.empty((nb, bs, hkv, d), dtype=torch.bfloat16, device=dev)
+        vc = torch.empty_like(kc)
+        rows = pm.prefill_inputs(tables, zeros, lay.lens, bs)["slot_mapping"]
+        ops.store_kv(k_all, v_all, kc, vc, torch.as_tensor(rows, device=dev))
+        meta = pm.decode_inputs(tables, lay.lens, bs)
+        bt = torch.as_tensor(meta["block_tables"], device=dev)
+        cl = torch.as_tensor(meta["context_lens"], device=dev)
+        ws = torch.empty(max(ops.decode_workspace_bytes(
+            b, hq, hkv, d, meta["max_context_len"]), 1), dtype=torch.uint8,
+            device=dev)
+        out = torch.empty_like(q)
+        placements.append((name, kc, vc, bt, cl, meta["max_context_len"], ws,
+                           out))
+    del k_all, v_all
+    torch.cuda.synchronize()
+
+    def call(pl, ev=None):
+        _, kc, vc, bt, cl, mcl, ws, out = pl
+        if ev is not None:
+            ev[0].record()
+        ops.decode(q, kc, vc, bt, cl, mcl, out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(warmup):
+        for pl in placements:
+            call(pl)
+    torch.cuda.synchronize()
+    times = {pl[0]: [] for pl in placements}
+    for _ in range(steps):
+        for pl in placements:
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            flush()
+            call(pl, ev)
+            torch.cuda.synchronize()
+            times[pl[0]].append(ev[0].elapsed_time(ev[1]))
+    cons = float(np.median(times["consecutive"]))
+    perm = float(np.median(times["permuted"]))
+    same = bool(torch.equal(placements[0][7].view(torch.int16),
+                            placements[1][7].view(torch.int16)))
+    return {
+        "workload": cfg.title + "; the same tokens at consecutive block ids "
+                    "and through shuffled block tables",
+        "steps": steps,
+        "consecutive_us": round(cons * 1e3, 2),
+        "permuted_us": round(perm * 1e3, 2),
+        "indirection_cost": round(perm / cons - 1.0, 4),
+        "consecutive_ms_stats": stats_ms(times["consecutive"]),
+        "permuted_ms_stats": stats_ms(times["permuted"]),
+        "outputs_bit_identical": same,
+    }
+
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def sample_sequences(lens, k, seed):
+    """Longest, shortest and k - 2 random sequences (sorted)."""
+    import numpy as np
+    lens = np.asarray(lens)
+    pick = {int(np.argmax(lens)), int(np.argmin(lens))}
+    for b in np.random.default_rng(seed).permutation(len(lens)).tolist():
+        if len(pick) >= k:
+            break
+        pick.add(int(b))
+    return sorted(pick)
+
+
+def cpu_check_decode(tables, lens, h_q, h_kc, h_vc, h_kn, h_vn, got, scale,
+                     dtype, seqs):
+    """Correctness of a timed decode step: the oracle's own metadata, store
+    and attention on host copies of the inputs taken before any kernel ran
+    (h_kn / h_vn None: nothing stored), against the GPU output `got`
+    (float64 [B, Hq, D]) on the sequences `seqs`."""
+    import numpy as np
+    import oracle.attention as oa
+    import oracle.metadata as om
+    meta = om.decode_metadata([{"block_table": [int(x) for x in t],
+                                "length": int(n)}
+                               for t, n in zip(tables, lens)], 16)
+    if h_kn is not None:
+        h_kc, h_vc = oa.store_kv(h_kc, h_vc, h_kn, h_vn,
+                                 meta["slot_mapping"])
+    want = oa.decode_attention(h_q, h_kc, h_vc, meta["block_tables"],
+                               meta["context_lens"], scale, dtype, seqs=seqs)
+    err = float(np.max(np.abs(got[seqs] - want[seqs])))
+    return {"max_abs_err": err, "tolerance": TOL[dtype],
+            "sequences_checked": len(seqs), "ok": bool(err <= TOL[dtype])}
+
+
+def cpu_check_fp8_decode(tables, lens, h_q, h_kc, h_vc, h_kn, h_vn, got,
+                         scale, k_scale, v_scale, seqs):
+    """As cpu_check_decode over an 8-bit (E4M3) cache: the oracle's
+    quantising store and E4M3 decode."""
+    import numpy as np
+    import oracle.fp8 as of8
+    import oracle.metadata as om
+    meta = om.decode_metadata([{"block_table": [int(x) for x in t],
+                                "length": int(n)}
+                               for t, n in zip(tables, lens)], 16)
+    inv_k = float(np.float32(1.0) / np.float32(k_scale))
+    inv_v = float(np.float32(1.0) / np.float32(v_scale))
+    ek, ev = of8.store_kv(h_kc, h_vc, h_kn, h_vn, meta["slot_mapping"],
+                          inv_k, inv_v, "bf16")
+    want = of8.decode_attention(h_q, ek, ev, meta["block_tables"],
+                                meta["context_lens"], scale, k_scale, v_scale,
+                                "bf16", seqs=seqs)
+    err = float(np.max(np.abs(got[seqs] - want[seqs])))
+    return {"max_abs_err": err, "tolerance": TOL["bf16"],
+            "sequences_checked": len(seqs), "ok": bool(err <= TOL["bf16"])}
+
+
+def cpu_check_mixed(pre, dec, h_kc, h_vc, h_kn, h_vn, h_qp, h_qd, gotp, gotd,
+                    scale, rows, seqs):
+    """Correctness of the mixed step: the oracle's store of every new row,
+    then its chunked prefill on the given rows of each chunk and its decode
+    on the given decode sequences."""
+    import numpy as np
+    import oracle.attention as oa
+    import oracle.metadata as om
+    mp = om.prefill_metadata([{"block_table": [int(x) for x in t],
+                               "num_cached": int(h), "num_scheduled": int(c)}
+                              for t, h, c in zip(pre.tables, pre.history,
+                                                 pre.chunk)], 16)
+    md = om.decode_metadata([{"block_table": [int(x) for x in t],
+                              "length": int(n)}
+                             for t, n in zip(dec.tables, dec.lens)], 16)
+    ek, ev = oa.store_kv(h_kc, h_vc, h_kn, h_vn,
+                         list(mp["slot_mapping"]) + list(md["slot_mapping"]))
+    width = max(len(t) for t in pre.tables)
+    tables = [[int(x) for x in t] + [-1] * (width - len(t))
+              for t in pre.tables]
+    wantp = oa.prefill_attention(h_qp, ek, ev, mp["cu_seqlens_q"],
+                                 mp["cu_seqlens_k"], tables, scale, True,
+                                 "bf16", rows=rows)
+    cu = mp["cu_seqlens_q"]
+    sel = [cu[b] + i for b in rows for i in rows[b]]
+    errp = float(np.max(np.abs(gotp[sel] - wantp[sel])))
+    wantd = oa.decode_attention(h_qd, ek, ev, md["block_tables"],
+                                md["context_lens"], scale, "bf16", seqs=seqs)
+    errd = float(np.max(np.abs(gotd[seqs] - wantd[seqs])))
+    tol = TOL["bf16"]
+    return {"prefill_max_abs_err": errp, "prefill_rows_checked": len(sel),
+            "decode_max_abs_err": errd, "decode_rows_checked": len(seqs),
+            "tolerance": tol, "ok": bool(errp <= tol and errd <= tol)}
 
 
 def cpu_baseline(case_tables, lens, h_q, h_kc, h_vc, hq, scale, budget_s):
@@ -643,6 +874,11 @@ def main():
     ws_bytes = ops.decode_workspace_bytes(b, hq, hkv, d, maxlen)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
+    # Host copies of the inputs, taken before any kernel runs: the oracle
+    # check and the CPU baseline read these.
+    keep_host = not (args.no_check and args.no_cpu_baseline)
+    host = [wl.host_bits(x) for x in (q, kc, vc, k_new, v_new)] \
+        if keep_host else None
 
     def step(ev=None):
         if ev is not None:
@@ -694,45 +930,54 @@ def main():
     traffic = committed_traffic("decode_8b_step_hbm_counters.md",
                                 DECODE_SOURCES)
 
+    check = None
+    if not args.no_check:
+        check = cpu_check_decode(lay.tables, lay.lens, *host, f64(out), scale,
+                                 "bf16", sample_sequences(lay.lens, 8, 3))
+
     # The other workloads get their own pools: free the 8B-shaped one first
-    # (the mixed pool is ~3.5 GB), keeping host copies for the CPU baseline.
-    keep_cpu = not args.no_cpu_baseline
-    h_kc = wl.host_bits(kc) if keep_cpu else None
-    h_vc = wl.host_bits(vc) if keep_cpu else None
-    h_q = wl.host_bits(q) if keep_cpu else None
+    # (the mixed pool is ~3.5 GB).
     del kc, vc, ws
     torch.cuda.empty_cache()
+    chk = not args.no_check
     mixed = None
     if args.mixed_steps > 0:
         mixed = run_mixed(args.mixed_steps, max(2, args.warmup // 2), dev,
                           flush, 0.0 if args.no_cpu_baseline
-                          else args.cpu_seconds / 3)
+                          else args.cpu_seconds / 3, chk)
         torch.cuda.empty_cache()
     prefix = None
     if args.prefix_steps > 0:
         prefix = run_prefix(args.prefix_steps, max(2, args.warmup // 2), dev,
                             flush, 0.0 if args.no_cpu_baseline
-                            else args.cpu_seconds / 3)
+                            else args.cpu_seconds / 3, chk)
         torch.cuda.empty_cache()
     tiny = None
     if args.tiny_steps > 0:
-        tiny = run_tiny(args.tiny_steps, max(2, args.warmup // 2), dev, flush)
+        tiny = run_tiny(args.tiny_steps, max(2, args.warmup // 2), dev, flush,
+                        chk)
     small = None
     if args.small_steps > 0:
         small = run_small(args.small_steps, max(2, args.warmup // 2), dev,
                           flush, 0.0 if args.no_cpu_baseline
-                          else args.cpu_seconds / 3)
+                          else args.cpu_seconds / 3, chk)
         torch.cuda.empty_cache()
     fp8 = None
     if args.fp8_steps > 0:
-        fp8 = run_fp8(args.fp8_steps, max(2, args.warmup // 2), dev, flush)
+        fp8 = run_fp8(args.fp8_steps, max(2, args.warmup // 2), dev, flush,
+                      chk)
+        torch.cuda.empty_cache()
+    indirection = None
+    if args.indirection_steps > 0:
+        indirection = run_indirection(args.indirection_steps,
+                                      max(2, args.warmup // 2), dev, flush)
         torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
         # bounded oracle sample over host copies of the same pool
-        done, toks, dt = cpu_baseline(lay.tables, lay.lens, h_q, h_kc, h_vc,
-                                      hq, scale, args.cpu_seconds)
+        done, toks, dt = cpu_baseline(lay.tables, lay.lens, host[0], host[1],
+                                      host[2], hq, scale, args.cpu_seconds)
         cpu_bytes = toks * row
         cores = len(os.sched_getaffinity(0))
         cpu = {"value": cpu_bytes / dt / 1e12, "unit": "TB/s",
@@ -773,11 +1018,13 @@ def main():
                      "traffic": traffic,
                      "algorithmic_bytes": dbytes},
         "cpu_baseline": cpu,
+        "check": check,
         "mixed_step": mixed,
         "prefix_step": prefix,
         "tiny_step": tiny,
         "small_step": small,
         "fp8_step": fp8,
+        "indirection_step": indirection,
         "wall_s_timed": round(wall, 3),
     }
     print(json.dumps(line), flush=True)
