@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--fp8-steps", type=int, default=20,
                     help="timed steps of the 8B-shaped decode step over an "
                          "8-bit (E4M3) cache (0 skips it)")
+    ap.add_argument("--verify-steps", type=int, default=20,
+                    help="timed calls per Lq of the 8B-shaped verify step "
+                         "(0 skips it)")
     ap.add_argument("--indirection-steps", type=int, default=20,
                     help="timed calls per placement of the block-table "
                          "indirection leg (0 skips it)")
@@ -636,6 +639,99 @@ def run_small(steps, warmup, dev, flush, cpu_s=0.0, check=True):
     }
 
 
+def verify_bytes(lens, lq, hq, hkv, d, elem, bs=16):
+    """Algorithmic HBM bytes of one verify launch: every sequence's K/V once
+    (Lk tokens x Hkv x D, K and V), its Lq query rows in and out, its block
+    ids and cu_seqlens."""
+    kv = int(sum(int(n) for n in lens)) * 2 * hkv * d * elem
+    qo = len(lens) * lq * hq * d * elem * 2
+    ids = 4 * int(sum(-(-int(n) // bs) for n in lens)) + 8 * (len(lens) + 1)
+    return kv + qo + ids
+
+
+def run_verify(steps, warmup, dev, flush, check=True, lqs=(2, 4, 8)):
+    """The verify pass of speculative decoding on the 8B-shaped decode
+    workload ("Warmup Guide -- Inference Serving Internals", Chapter 7; "10
+    Serving Engines", section 10.6): each of the 256 sequences (contexts
+    uniform in [512, 8192], the last Lq tokens being the proposed ones)
+    attends Lq causal query rows, 32 query / 8 KV heads, D = 128, bf16 --
+    one pa_prefill_varlen launch, which takes its small-row path (G * Lq <=
+    64 packed rows per KV head).  Timed per Lq with HIP events on the
+    launch's stream, the cache flushed before every call."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from paged_kv_cache_slot_amd import metadata as pm
+    from paged_kv_cache_slot_amd import ops
+
+    cfg = wl.get_config(WORKLOAD)
+    lay = wl.config_decode_layout(cfg)
+    hq, hkv, d, bs = cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, 16
+    b = len(lay.lens)
+    kc, vc = wl.fill_pool(lay.num_blocks, bs, hkv, d, "bf16", cfg.seed, dev)
+    hk = [wl.host_bits(kc), wl.host_bits(vc)] if check else None
+    scale = 1.0 / math.sqrt(d)
+    legs = {}
+    for lq in lqs:
+        q = wl.make_values((b * lq, hq, d), "bf16", cfg.seed + 20 + lq, dev)
+        hq_bits = wl.host_bits(q) if check else None
+        meta = pm.prefill_inputs(lay.tables, lay.lens - lq, np.full(b, lq), bs)
+        cu_q = torch.as_tensor(meta["cu_seqlens_q"], device=dev)
+        cu_k = torch.as_tensor(meta["cu_seqlens_k"], device=dev)
+        bt = torch.as_tensor(meta["block_tables"], device=dev)
+        out = torch.empty_like(q)
+        need = ops.prefill_workspace_bytes(b, hq, hkv, d, meta["max_seqlen_q"],
+                                           meta["max_seqlen_k"])
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+        def call(ev=None):
+            if ev is not None:
+                ev[0].record()
+            ops.prefill_varlen(q, kc, vc, cu_q, cu_k, meta["max_seqlen_q"],
+                               meta["max_seqlen_k"], bt, scale=scale,
+                               causal=True, out=out, workspace=ws)
+            if ev is not None:
+                ev[1].record()
+
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+               for _ in range(steps)]
+        for i in range(steps):
+            flush()
+            call(evs[i])
+        torch.cuda.synchronize()
+        t_all = [e[0].elapsed_time(e[1]) for e in evs]
+        t = float(np.median(t_all))
+        vbytes = verify_bytes(lay.lens, lq, hq, hkv, d, 2)
+        chk = None
+        if check:
+            chk = cpu_check_verify(lay.tables, lay.lens, lq, hq_bits, hk[0],
+                                   hk[1], f64(out), scale,
+                                   sample_sequences(lay.lens, 6, 30 + lq))
+        legs[f"lq{lq}"] = {
+            "us": round(t * 1e3, 2),
+            "ms_stats": stats_ms(t_all),
+            "algorithmic_bytes": vbytes,
+            "tbs": round(vbytes / (t * 1e-3) / 1e12, 4),
+            "frac_of_hbm_peak": round(vbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "query_rows_per_s": round(b * lq / (t * 1e-3), 1),
+            "check": chk,
+        }
+        del q, out, ws
+    return {
+        "workload": "verify pass on the 8B-shaped decode workload: 256 seqs, "
+                    "ctx U[512,8192] incl. Lq proposed tokens, Lq causal rows "
+                    "each, 32q/8kv, D=128, bf16",
+        "steps": steps,
+        "kernel": "pa_prefill_varlen small-row path (verify_kernel; one "
+                  "partition per sequence, workgroups rank the items)",
+        "legs": legs,
+    }
+
+
 def run_indirection(steps, warmup, dev, flush):
     """Cost of the block-table indirection ("Warmup Guide -- Inference
     Serving Internals", Chapter 3 calls it cheap): the 8B-shaped decode
@@ -754,6 +850,25 @@ def cpu_check_decode(tables, lens, h_q, h_kc, h_vc, h_kn, h_vn, got, scale,
     err = float(np.max(np.abs(got[seqs] - want[seqs])))
     return {"max_abs_err": err, "tolerance": TOL[dtype],
             "sequences_checked": len(seqs), "ok": bool(err <= TOL[dtype])}
+
+
+def cpu_check_verify(tables, lens, lq, h_q, h_kc, h_vc, got, scale, seqs):
+    """Correctness of a timed verify launch: the oracle's varlen prefill
+    (its own cu_seqlens) on the sequences `seqs`, every row."""
+    import numpy as np
+    import oracle.attention as oa
+    b = len(lens)
+    cu_q = np.concatenate([[0], np.cumsum(np.full(b, lq))])
+    cu_k = np.concatenate([[0], np.cumsum(np.asarray(lens))])
+    width = max(len(t) for t in tables)
+    tab = [[int(x) for x in t] + [-1] * (width - len(t)) for t in tables]
+    want = oa.prefill_attention(h_q, h_kc, h_vc, cu_q, cu_k, tab, scale, True,
+                                "bf16", seqs=seqs)
+    sel = [r for s in seqs for r in range(cu_q[s], cu_q[s + 1])]
+    err = float(np.max(np.abs(got[sel] - want[sel])))
+    ok = bool(err <= TOL["bf16"] and np.all(np.isfinite(got)))
+    return {"max_abs_err": err, "tolerance": TOL["bf16"],
+            "rows_checked": len(sel), "ok": ok}
 
 
 def cpu_check_fp8_decode(tables, lens, h_q, h_kc, h_vc, h_kn, h_vn, got,
@@ -967,6 +1082,11 @@ def main():
         fp8 = run_fp8(args.fp8_steps, max(2, args.warmup // 2), dev, flush,
                       chk)
         torch.cuda.empty_cache()
+    verify = None
+    if args.verify_steps > 0:
+        verify = run_verify(args.verify_steps, max(2, args.warmup // 2), dev,
+                            flush, chk)
+        torch.cuda.empty_cache()
     indirection = None
     if args.indirection_steps > 0:
         indirection = run_indirection(args.indirection_steps,
@@ -1024,6 +1144,7 @@ def main():
         "tiny_step": tiny,
         "small_step": small,
         "fp8_step": fp8,
+        "verify_step": verify,
         "indirection_step": indirection,
         "wall_s_timed": round(wall, 3),
     }

@@ -54,6 +54,7 @@
 
 #include "pa_device.h"
 #include "pa_internal.h"
+#include "pa_tile.h"
 
 namespace pa {
 
@@ -68,14 +69,6 @@ constexpr uint32_t kBf16PairOne = 0x3F803F80u;   // (1.0, 1.0) as bfloat16
 constexpr int kBufferRsrcWord3 = 0x00020000;
 // Cache-policy bits of a buffer load: non-temporal (streamed, used once).
 constexpr int kCacheNT = 2;
-
-__device__ __forceinline__ int load_uniform_i32(const int32_t* base, int idx) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  return ((const __attribute__((address_space(4))) int32_t*)base)[idx];
-#else
-  return base[idx];
-#endif
-}
 
 // How a wave covers one 16-token block of one KV head: kLpr lanes share a
 // row (token), each lane takes kCpl 16-byte chunks of it, and one load
@@ -813,50 +806,13 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
   // Slots 0 .. np - 1 (this call's partitions), then num_partitions ..
   // num_partitions + npre - 1 (the prefix partials).
   auto slot = [&](int i) { return i < np ? i : p.num_partitions + (i - np); };
-  const int n = np + npre;
-  // Groups of up to kGroup partials: all their loads are issued together
-  // (one memory round trip per group), then the group's max becomes the
-  // reference, rescaling what earlier groups summed.  With n <= kGroup this
-  // is the plain two-pass merge: max over all, then weighted sums in order.
-  constexpr int kGroup = 8;
-  float m = -INFINITY, l = 0.f, o = 0.f;
-  for (int i0 = 0; i0 < n; i0 += kGroup) {
-    float mv[kGroup], sv[kGroup], av[kGroup];
-#pragma unroll
-    for (int u = 0; u < kGroup; ++u) {
-      mv[u] = -INFINITY;
-      sv[u] = 0.f;
-      av[u] = 0.f;
-      if (i0 + u < n) {                       // uniform over the workgroup
-        const int k = slot(i0 + u);
-        mv[u] = mx[k];
-        load_partial(k, sv[u], av[u]);
-      }
-    }
-    float gm = m;
-#pragma unroll
-    for (int u = 0; u < kGroup; ++u) gm = fmaxf(gm, mv[u]);
-    if (gm == -INFINITY) continue;          // nothing visible yet
-    if (gm > m) {
-      const float a = m == -INFINITY ? 0.f : fast_exp2(m - gm);
-      l *= a;
-      o *= a;
-      m = gm;
-    }
-#pragma unroll
-    for (int u = 0; u < kGroup; ++u) {
-      if (i0 + u < n) {
-        const float w = fast_exp2(mv[u] - m);
-        l = fmaf(w, sv[u], l);
-        o = fmaf(w, av[u], o);
-      }
-    }
-  }
-  if (n == 0 || m == -INFINITY) {
-    store_out<T>(out, 0.f);
-    return;
-  }
-  store_out<T>(out, l > 0.f ? o / l * p.v_scale : 0.f);
+  const float o = merge_partials<8>(np + npre, [&](int i, float& m, float& l, float& acc)
+                                                   __attribute__((always_inline)) {
+    const int k = slot(i);
+    m = mx[k];
+    load_partial(k, l, acc);
+  });
+  store_out<T>(out, o * p.v_scale);
 }
 
 // Longest-first schedule of the (sequence, partition) items: one workgroup
@@ -867,7 +823,6 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
 // land in any order; the results do not depend on the schedule.
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanBins = 1024;
-constexpr int kBinsPerThread = kPlanBins / kPlanThreads;
 
 __device__ __forceinline__ int plan_bin(const DecodeParams& p, int item) {
   const int b = item % p.num_seqs;
@@ -887,59 +842,9 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(
     DecodeParams p, int32_t* __restrict__ order) {
   __shared__ int bins[kPlanBins];
   __shared__ int wave_sum[kPlanThreads / kWave];
-  const int tid = threadIdx.x;
-  const int n = p.num_seqs * p.num_partitions;
-  // Bins of this thread's first items (their context lengths are loaded
-  // while the bins are cleared).
-  int mybin[kPlanRegItems];
-#pragma unroll
-  for (int k = 0; k < kPlanRegItems; ++k) {
-    const int item = tid + k * kPlanThreads;
-    mybin[k] = item < n ? plan_bin(p, item) : 0;
-  }
-  for (int i = tid; i < kPlanBins; i += kPlanThreads) bins[i] = 0;
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < kPlanRegItems; ++k)
-    if (tid + k * kPlanThreads < n) atomicAdd(&bins[mybin[k]], 1);
-  for (int item = tid + kPlanRegItems * kPlanThreads; item < n; item += kPlanThreads)
-    atomicAdd(&bins[plan_bin(p, item)], 1);
-  __syncthreads();
-  // Exclusive prefix from the heaviest bin down: a scan inside each wave,
-  // then the totals of the waves before it.
-  int cnt[kBinsPerThread];
-  int mine = 0;
-#pragma unroll
-  for (int k = 0; k < kBinsPerThread; ++k) {
-    cnt[k] = bins[kPlanBins - 1 - (kBinsPerThread * tid + k)];
-    mine += cnt[k];
-  }
-  const int lane = tid % kWave;
-  const int wave = tid / kWave;
-  int incl = mine;
-#pragma unroll
-  for (int off = 1; off < kWave; off *= 2) {
-    const int y = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += y;
-  }
-  if (lane == kWave - 1) wave_sum[wave] = incl;
-  __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += wave_sum[w];
-  int start = before + incl - mine;
-#pragma unroll
-  for (int k = 0; k < kBinsPerThread; ++k) {
-    bins[kPlanBins - 1 - (kBinsPerThread * tid + k)] = start;
-    start += cnt[k];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < kPlanRegItems; ++k) {
-    const int item = tid + k * kPlanThreads;
-    if (item < n) order[atomicAdd(&bins[mybin[k]], 1)] = item;
-  }
-  for (int item = tid + kPlanRegItems * kPlanThreads; item < n; item += kPlanThreads)
-    order[atomicAdd(&bins[plan_bin(p, item)], 1)] = item;
+  longest_first_order<kPlanThreads, kPlanBins, kPlanRegItems>(
+      p.num_seqs * p.num_partitions, [&](int item) { return plan_bin(p, item); },
+      order, bins, wave_sum);
 }
 
 template <typename T, int D, int G, int C, bool F8>

@@ -6,6 +6,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 namespace pa {
@@ -129,6 +130,48 @@ constexpr float kHalfMax = 65504.f;
 __device__ __forceinline__ uint16_t partial_f16(float o, bool big) {
   const float v = big ? o * kPartialShrink : o;
   return f32_to_f16(fminf(fmaxf(v, -kHalfMax), kHalfMax));
+}
+
+// Log-sum-exp merge of n partial results of one output element.  Partial
+// k has a reference max m_k (base-2 logits), a sum l_k and an unnormalised
+// output a_k; the result is sum_k 2^(m_k - m) a_k / sum_k 2^(m_k - m) l_k
+// with m the largest m_k, or 0 when no partial saw a key.  load(k, m, l, a)
+// fetches partial k.  The loads of a group of kGroup partials are issued
+// together (one memory round trip per group); the group's max then becomes
+// the reference, rescaling what earlier groups summed.  With n <= kGroup
+// this is the plain two-pass merge: max over all, then weighted sums.
+template <int kGroup, typename LoadFn>
+__device__ __forceinline__ float merge_partials(int n, LoadFn load) {
+  float m = -INFINITY, l = 0.f, o = 0.f;
+  for (int i0 = 0; i0 < n; i0 += kGroup) {
+    float mv[kGroup], sv[kGroup], av[kGroup];
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {
+      mv[u] = -INFINITY;
+      sv[u] = 0.f;
+      av[u] = 0.f;
+      if (i0 + u < n) load(i0 + u, mv[u], sv[u], av[u]);
+    }
+    float gm = m;
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) gm = fmaxf(gm, mv[u]);
+    if (gm == -INFINITY) continue;          // nothing visible yet
+    if (gm > m) {
+      const float a = m == -INFINITY ? 0.f : fast_exp2(m - gm);
+      l *= a;
+      o *= a;
+      m = gm;
+    }
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {
+      if (i0 + u < n) {
+        const float w = fast_exp2(mv[u] - m);
+        l = fmaf(w, sv[u], l);
+        o = fmaf(w, av[u], o);
+      }
+    }
+  }
+  return (m == -INFINITY || !(l > 0.f)) ? 0.f : o / l;
 }
 
 // 16-byte global load / store.

@@ -160,4 +160,25 @@ size_t prefill_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads,
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
+// Small-row path of the varlen prefill (bfloat16): used when the packed
+// rows per KV head, G * max_seqlen_q, are at most 64 (a verify pass, a
+// one-row chunk).  Split-context partitions over the keys, merged when
+// there are several.
+struct VerifyPlan {
+  bool use;              // these sizes take the small-row path
+  int row_tiles;         // 16-row tiles per KV head: 1, 2 or 4
+  int partition_tokens;  // keys per partition (multiple of 64)
+  int num_partitions;    // >= 1
+  bool use_order;        // longest-first schedule from a plan kernel
+  size_t workspace_bytes;
+  size_t off_max, off_sum, off_acc;  // partials (num_partitions > 1)
+  size_t off_order;                  // int32 [num_seqs * num_partitions]
+};
+
+VerifyPlan plan_verify(int num_seqs, int num_heads, int num_kv_heads,
+                       int head_dim, int max_seqlen_q, int max_seqlen_k);
+
+hipError_t launch_verify(const PrefillArgs& a, const VerifyPlan& plan,
+                         hipStream_t stream);
+
 }  // namespace pa

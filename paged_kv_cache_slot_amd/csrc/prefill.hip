@@ -45,6 +45,7 @@
 
 #include "pa_device.h"
 #include "pa_internal.h"
+#include "pa_tile.h"
 
 namespace pa {
 
@@ -166,41 +167,6 @@ struct PrefillParams {
   int slot0;
 };
 
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-
-// A wave-uniform int32 that stays constant for the whole kernel (a block id),
-// read through the constant address space so it arrives by a scalar load
-// counted by lgkmcnt.  Read as a vector load it would be counted by vmcnt,
-// and each wait for it would also wait for every DMA load issued before.
-__device__ __forceinline__ int load_uniform_i32(const int32_t* base, int idx) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  return ((const __attribute__((address_space(4))) int32_t*)base)[idx];
-#else
-  return base[idx];
-#endif
-}
-
-// Query rows and cached keys of sequence b, clamped so that no index leaves
-// the buffers: rows q0 .. q0 + lq - 1 of q, keys 0 .. lk - 1.
-struct SeqExtent {
-  int q0, lq, lk;
-};
-__device__ __forceinline__ SeqExtent seq_extent(const int32_t* cu_q,
-                                                const int32_t* cu_k, int b,
-                                                int max_q, int max_k,
-                                                int64_t total_q,
-                                                int max_blocks) {
-  int q0 = cu_q[b];
-  int lq = cu_q[b + 1] - q0;
-  int lk = cu_k[b + 1] - cu_k[b];
-  q0 = q0 < 0 ? 0 : q0;
-  lq = lq < 0 ? 0 : (lq > max_q ? max_q : lq);
-  if (q0 + lq > total_q) lq = static_cast<int>(total_q - q0 < 0 ? 0 : total_q - q0);
-  lk = lk < 0 ? 0 : (lk > max_k ? max_k : lk);
-  if (lk > max_blocks * kBlock) lk = max_blocks * kBlock;
-  return {q0, lq, lk};
-}
-
 // Keys an M-tile reads: the causal limit of its last row, or all lk.
 __device__ __forceinline__ int tile_key_end(const SeqExtent& e, int g, int m0,
                                             int bm, int causal) {
@@ -230,65 +196,6 @@ __device__ __forceinline__ int v_swz(int row) {
   return ((row % 4) << 2) & (kChunks - 1);
 }
 
-// 16 bytes per lane from global memory straight into LDS
-// (global_load_lds_dwordx4): lane l's bytes land at lds + 16 l; `lds` must be
-// the same for the whole wave (it goes to M0).  Completion is counted by
-// vmcnt.  Issued from inline assembly: the compiler cannot tell which LDS
-// bytes the load writes and, seeing the builtin, would wait for it before
-// the next LDS read of any buffer -- which would make the prefetch of later
-// tiles wait for the current one.  The caller orders the loads against LDS
-// reads with explicit vmcnt waits and barriers.
-// The source is base + off: base uniform (an SGPR pair), off this lane's
-// 32-bit byte offset.
-__device__ __forceinline__ void dma16(const char* base, uint32_t off, char* lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  const unsigned m0 = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds)));
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(off), "s"(base), "s"(m0) : "memory", "m0");
-#else
-  (void)base;
-  (void)off;
-  (void)lds;
-#endif
-}
-
-// Wait until at most N vector memory loads of this lane are in flight
-// (they complete in issue order).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-#endif
-}
-
-// Workgroup barrier after this wave's LDS reads have completed.  Unlike
-// __syncthreads it does not also wait for every vector load in flight (the
-// prefetched K/V tiles).
-__device__ __forceinline__ void lds_barrier() {
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-#endif
-}
-
-// LDS transpose read (ds_read_b64_tr_b16).  In each group of 16 lanes, if
-// lane s reads the four 16-bit values M[s][0..3] at its address, lane i
-// receives M[4k + i/4][i % 4] for k = 0..3 (checked on gfx950).  With four
-// lanes per key row covering 16 dimensions and four rows, every lane gets
-// four consecutive keys of one dimension -- an MFMA A operand of V^T.
-// (The host compilation pass has no LDS address space; it only needs the
-// declaration.)
-__device__ __forceinline__ uint2 lds_read_tr16(const char* p) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16_t*)(p));
-  return __builtin_bit_cast(uint2, r);
-#else
-  (void)p;
-  return make_uint2(0, 0);
-#endif
-}
-
 template <typename T>
 __device__ __forceinline__ void store4(T* p, const float* v);
 template <>
@@ -299,17 +206,6 @@ template <>
 __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const float* v) {
   *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]),
                                              pack_bf16x2(v[2], v[3]));
-}
-
-// The value lane l ^ 32 holds (v_permlane32_swap: no LDS round trip).
-__device__ __forceinline__ float swap_halves(float x) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
-                                                  __float_as_uint(x), false, false);
-  return __uint_as_float(__lane_id() < 32 ? r[1] : r[0]);
-#else
-  return x;
-#endif
 }
 
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
@@ -373,31 +269,12 @@ prefill_kernel(PrefillParams p) {
     // tile loop's first barrier.
     int* s_w = reinterpret_cast<int*>(
         smem + (2 * S::kStages - 1) * static_cast<size_t>(S::kTile));
-    int* s_item = s_w + S::kThreads;
-    const int n = p.num_seqs * p.mtiles;
-    const int n4 = (n + 3) & ~3;
-    int w = -1;
-    if (tid < n) {
-      const SeqExtent e = seq_extent(p.cu_q, p.cu_k, tid / p.mtiles, p.max_seqlen_q,
+    auto weight = [&](int it) {
+      const SeqExtent e = seq_extent(p.cu_q, p.cu_k, it / p.mtiles, p.max_seqlen_q,
                                      p.max_seqlen_k, p.total_q, p.max_blocks_per_seq);
-      w = item_weight(e, tid, p.mtiles, S::kBM, G, p.causal);
-    }
-    if (tid < n4) s_w[tid] = w;               // padding -1: lighter than any item
-    if (tid == 0) *s_item = -1;
-    __syncthreads();
-    if (tid < n) {
-      int r = 0;
-      for (int j = 0; j < n4; j += 4) {
-        const int4 x = *reinterpret_cast<const int4*>(s_w + j);
-        r += (x.x > w || (x.x == w && j < tid)) ? 1 : 0;
-        r += (x.y > w || (x.y == w && j + 1 < tid)) ? 1 : 0;
-        r += (x.z > w || (x.z == w && j + 2 < tid)) ? 1 : 0;
-        r += (x.w > w || (x.w == w && j + 3 < tid)) ? 1 : 0;
-      }
-      if (r == rank) *s_item = tid;
-    }
-    __syncthreads();
-    item = __builtin_amdgcn_readfirstlane(*s_item);
+      return item_weight(e, it, p.mtiles, S::kBM, G, p.causal);
+    };
+    item = inline_ranked_item<S::kThreads>(p.num_seqs * p.mtiles, rank, weight, s_w);
   }
   if (item < 0 || item >= p.num_seqs * p.mtiles) return;   // uniform
   const int b = item / p.mtiles;
@@ -818,7 +695,6 @@ prefill_kernel(PrefillParams p) {
 // the last bin share it).  Items of equal weight land in any order; the
 // attention results do not depend on the schedule.
 constexpr int kPlanThreads = 1024;
-constexpr int kBinsPerThread = kPlanBins / kPlanThreads;
 
 struct PlanParams {
   const int32_t* cu_q;
@@ -843,40 +719,10 @@ __device__ __forceinline__ int plan_bin(const PlanParams& q, int item) {
 __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
     PlanParams q, int32_t* __restrict__ order) {
   __shared__ int bins[kPlanBins];
-  __shared__ int part[kPlanThreads];
-  const int tid = threadIdx.x;
-  const int n = q.num_seqs * q.mtiles;
-  for (int i = tid; i < kPlanBins; i += kPlanThreads) bins[i] = 0;
-  __syncthreads();
-  for (int item = tid; item < n; item += kPlanThreads)
-    atomicAdd(&bins[plan_bin(q, item)], 1);
-  __syncthreads();
-  // Exclusive prefix over the bins from the heaviest down: thread t owns
-  // bins kPlanBins - 1 - (kBinsPerThread * t + k).
-  int cnt[kBinsPerThread];
-  int mine = 0;
-#pragma unroll
-  for (int k = 0; k < kBinsPerThread; ++k) {
-    cnt[k] = bins[kPlanBins - 1 - (kBinsPerThread * tid + k)];
-    mine += cnt[k];
-  }
-  part[tid] = mine;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off *= 2) {
-    const int add = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += add;
-    __syncthreads();
-  }
-  int start = part[tid] - mine;
-#pragma unroll
-  for (int k = 0; k < kBinsPerThread; ++k) {
-    bins[kPlanBins - 1 - (kBinsPerThread * tid + k)] = start;
-    start += cnt[k];
-  }
-  __syncthreads();
-  for (int item = tid; item < n; item += kPlanThreads)
-    order[atomicAdd(&bins[plan_bin(q, item)], 1)] = item;
+  __shared__ int wave_sum[kPlanThreads / kWave];
+  longest_first_order<kPlanThreads, kPlanBins, 1>(
+      q.num_seqs * q.mtiles, [&](int item) { return plan_bin(q, item); }, order,
+      bins, wave_sum);
 }
 
 int m_tiles(int max_seqlen_q, int group, int bm) {
@@ -994,11 +840,16 @@ hipError_t dispatch_prefix(const PrefillParams& prm, const PrefixArgs& a,
 // smallest M-tile of any shape and the G the launch dispatches on
 // (num_heads / num_kv_heads).
 size_t prefill_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads,
-                               int, int max_seqlen_q, int) {
+                               int head_dim, int max_seqlen_q, int max_seqlen_k) {
   const int g = num_heads / num_kv_heads;
   if (g < 1) return 0;
   const int64_t items = static_cast<int64_t>(num_seqs) * m_tiles(max_seqlen_q, g, kMinBM);
-  return static_cast<size_t>((items * 4 + 255) / 256 * 256);
+  const size_t tiles = static_cast<size_t>((items * 4 + 255) / 256 * 256);
+  // The small-row path (bfloat16 only; the size does not depend on the
+  // element type) may take these sizes: room for its partials too.
+  const VerifyPlan vp = plan_verify(num_seqs, num_heads, num_kv_heads, head_dim,
+                                    max_seqlen_q, max_seqlen_k);
+  return vp.use && vp.workspace_bytes > tiles ? vp.workspace_bytes : tiles;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
@@ -1021,6 +872,9 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   prm.causal = a.causal ? 1 : 0;
   const int g = a.num_heads / a.num_kv_heads;
   if (a.bf16) {
+    const VerifyPlan vp = plan_verify(a.num_seqs, a.num_heads, a.num_kv_heads,
+                                      a.head_dim, a.max_seqlen_q, a.max_seqlen_k);
+    if (vp.use) return launch_verify(a, vp, stream);
     if (a.head_dim == 128) return dispatch_group<bf16_t, 128>(prm, a, g, stream);
     return dispatch_group<bf16_t, 64>(prm, a, g, stream);
   }

@@ -1,0 +1,700 @@
+// Varlen attention of a few query rows per sequence over a paged context --
+// the shape of a speculative-decoding verify pass -- for gfx950, bfloat16.
+//
+// What it computes: exactly what the varlen prefill computes (sequence b
+// owns query rows cu_q[b] .. cu_q[b+1]-1, Lq of them, and its first Lk
+// cached tokens as keys; causal row i sees keys 0 .. Lk - Lq + i), for
+// launches whose packed rows per KV head, G * max Lq, are at most 64.  In a
+// verify pass the target model runs once over the k proposed positions of
+// every sequence ("Warmup Guide -- Inference Serving Internals", Chapter 7,
+// the scheme; "10 Serving Engines", sections 10.6.1-10.6.2: the gamma
+// proposed tokens are verified in one target pass): Lq = k + 1 rows per
+// sequence, each a decode row one position further, over a long cache.
+//
+// Design (MI355X-first).  Like decode this is an HBM stream -- every K/V
+// byte of a KV head serves only G * Lq rows -- but with up to 64 rows per
+// KV head the dot products belong on MFMA:
+//  * one workgroup (4 waves) per (sequence, partition, KV head); the G * Lq
+//    rows of a KV head are packed into NT tiles of 16 (row m = position
+//    m / G, head m % G), so one K/V byte loaded serves all of them;
+//  * wave w streams cache blocks w, w + 4, ... of its partition through its
+//    own ring of LDS stages (one 16-token K block and V block per stage),
+//    filled by LDS DMA (global_load_lds_dwordx4, 16-byte chunks XOR-
+//    swizzled by row); waves never wait for each other inside the loop, and
+//    kStages - 1 blocks per wave are in flight while one is computed;
+//  * per block: S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = 16 keys from
+//    LDS, B = Q^T held in registers), online softmax per lane (a lane holds
+//    four keys of one row), O^T += V^T P^T with v_mfma_f32_16x16x16_bf16
+//    (A = V^T by LDS transpose reads, B = P^T taken straight from the S^T
+//    accumulators, whose layout is already the B operand's);
+//  * the softmax reference max moves only when a logit exceeds it by more
+//    than 2^8 (exact rescale of O then); otherwise weights are taken
+//    against it directly, so most blocks need no cross-lane max;
+//  * the four waves' (max, sum, O) are combined through LDS at the end; a
+//    single partition writes the output, several write binary16 partials
+//    that a merge kernel combines with log-sum-exp weights;
+//  * masking by select: keys past a row's causal limit or past Lk get
+//    weight exactly 0, and V rows past Lk are zeroed in LDS (a NaN there
+//    would survive a multiplication by zero).
+#include <math.h>
+
+#include "pa_device.h"
+#include "pa_internal.h"
+#include "pa_tile.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kBlock = kTileBlock;   // tokens per cache block
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr uint32_t kBf16PairOne = 0x3F803F80u;   // (1.0, 1.0) as bfloat16
+
+typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+typedef float f32x4_v __attribute__((ext_vector_type(4)));
+
+// Operand layouts of the 16x16 shapes: lane l holds A[l % 16][k(l / 16, e)]
+// and B[k(l / 16, e)][l % 16] (the same k for both); accumulator register
+// r of lane l is C[4 (l / 16) + r][l % 16].  For 16x16x16, k(g, e) = 4 g +
+// e, which is what lets the S^T accumulators feed the PV step as B.
+__device__ __forceinline__ f32x4_v mfma_qk(uint4 a, uint4 b, f32x4_v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, a),
+                                                 __builtin_bit_cast(bf16x8_v, b),
+                                                 c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_v mfma_pv(uint2 a, uint2 b, f32x4_v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16_t, a),
+                                                   __builtin_bit_cast(v4i16_t, b),
+                                                   c, 0, 0, 0);
+}
+
+template <int D, int NT>
+struct VerifyShape {
+  static constexpr int kRow = D * 2;                   // bytes per key row
+  static constexpr int kChunks = kRow / 16;            // 16-byte chunks per row
+  static constexpr int kRowsPerBank = 256 / kRow;      // rows per 256-byte bank period
+  static constexpr int kBlockBytes = kBlock * kRow;    // one block of one KV head
+  static constexpr int kDmaPerBlock = kBlockBytes / 1024;
+  static constexpr int kStage = 2 * kBlockBytes;       // K block, then V block
+  // Each wave owns 32 KiB of ring: 4 stages at D = 128, 8 at D = 64.
+  static constexpr int kStages = 32768 / kStage;
+  static constexpr int kRing = kStages * kStage;
+  static constexpr int kLoadsPerStage = 2 * kDmaPerBlock;   // per lane
+  static constexpr int kRows = NT * 16;                // packed query rows
+  static constexpr int kQBytes = kRows * kRow;
+  static constexpr int kQDma = kQBytes / 1024;
+  static constexpr size_t kLds = static_cast<size_t>(kWaves) * kRing + kQBytes;
+  static constexpr int kQSteps = D / 32;               // QK MFMAs per row tile
+  static constexpr int kDTiles = D / 16;               // O^T tiles per row tile
+  // Combine: each wave's O as fp32 rows padded by 16 bytes (so the 16 rows
+  // a lane group writes fall in different banks), then (max, sum) per row.
+  static constexpr int kORow = D * 4 + 16;
+  static constexpr size_t kCombine =
+      static_cast<size_t>(kWaves) * kRows * kORow + kWaves * kRows * 8;
+  static constexpr int kTpr = D / 8;                   // combine threads per row
+  static constexpr int kRowsPerPass = kThreads / kTpr;
+  static_assert(kBlockBytes % 1024 == 0 && kQBytes % 1024 == 0, "DMA split");
+  static_assert(kStages >= 2 && kStages * kLoadsPerStage <= 56, "vmcnt range");
+  static_assert(kLds <= 160 * 1024 && kCombine <= kLds, "LDS per CU");
+  static_assert(kStage >= (kThreads + 5) * 4, "ranking scratch in one stage");
+};
+
+// 16-byte chunk swizzles (XOR on the chunk index, per row).  K and Q rows:
+// 16 lanes read one chunk of 16 consecutive rows; V rows: 16 lanes read two
+// adjacent chunks of 4 rows each (transpose reads), 64 lanes 16 rows.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+  constexpr int kRowsPerBank = 256 / (D * 2);
+  return (row / kRowsPerBank) % (D / 8);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+  constexpr int kRowsPerBank = 256 / (D * 2);
+  return 2 * ((row / kRowsPerBank) % (D / 16));
+}
+
+struct VerifyParams {
+  void* out;
+  const char* q;
+  int64_t total_q;
+  const char* k_cache;
+  const char* v_cache;
+  int64_t num_blocks;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int max_seqlen_q;
+  int max_seqlen_k;
+  const int32_t* block_tables;
+  int max_blocks_per_seq;
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  float scale_log2;
+  int causal;
+  int partition_tokens;      // keys per partition (a multiple of 64)
+  int num_partitions;
+  // Work items (partition * num_seqs + b), heaviest first: `order` from the
+  // plan kernel, or ranked by each workgroup itself (rank_inline), or the
+  // natural order.
+  const int32_t* order;
+  int rank_inline;
+  // Partials (num_partitions > 1): slot ((b * max_seqlen_q + i) * Hq + h) *
+  // num_partitions + partition.
+  float* ws_max;
+  float* ws_sum;             // negative: the partial is stored scaled
+  uint16_t* ws_acc_h;        // binary16 acc / sum, D per slot
+};
+
+// Keys of sequence extent e that partition `part` reads: [key0, key1).  The
+// last row sees every key, so the partition ends at Lk.
+__device__ __forceinline__ int partition_blocks(const VerifyParams& p,
+                                                const SeqExtent& e, int part) {
+  const int key0 = part * p.partition_tokens;
+  const int key1 = min(e.lk, key0 + p.partition_tokens);
+  return key1 > key0 ? (key1 + kBlock - 1) / kBlock - key0 / kBlock : 0;
+}
+
+__device__ __forceinline__ SeqExtent verify_extent(const VerifyParams& p, int b) {
+  return seq_extent(p.cu_q, p.cu_k, b, p.max_seqlen_q, p.max_seqlen_k, p.total_q,
+                    p.max_blocks_per_seq);
+}
+
+// Weight of a work item for the longest-first order: its blocks (capped
+// at kPlanBins - 1); 0 for a sequence without query rows.
+constexpr int kPlanBins = 1024;
+__device__ __forceinline__ int item_weight(const VerifyParams& p, int item) {
+  const int b = item % p.num_seqs;
+  const SeqExtent e = verify_extent(p, b);
+  if (e.lq == 0) return 0;
+  const int w = partition_blocks(p, e, item / p.num_seqs);
+  return w < kPlanBins ? w : kPlanBins - 1;
+}
+
+// One workgroup per CU (its LDS): one wave per SIMD, all registers to it.
+template <int D, int G, int NT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+verify_kernel(VerifyParams p) {
+  using S = VerifyShape<D, NT>;
+  extern __shared__ __align__(16) char smem[];
+  // [wave 0 ring .. wave 3 ring][Q rows]; reused by the final combine.
+
+  // Workgroup lin takes work item order[lin / Hkv] for KV head lin % Hkv:
+  // the Hkv workgroups of one item read adjacent 256-byte pieces of the same
+  // cache rows, and the dispatcher spreads them over the 8 XCDs.
+  const int tid = threadIdx.x;
+  const int kvh = blockIdx.x % p.num_kv_heads;
+  const int rank = blockIdx.x / p.num_kv_heads;
+  const int n_items = p.num_seqs * p.num_partitions;
+  int item = rank;
+  if (p.order != nullptr) {
+    item = load_uniform_i32(p.order, rank);
+  } else if (p.rank_inline) {
+    // Scratch: wave 0's last ring stage, which no DMA writes before that
+    // wave's first loop iteration (after the workgroup barrier below).
+    item = inline_ranked_item<kThreads>(
+        n_items, rank, [&](int it) { return item_weight(p, it); },
+        reinterpret_cast<int*>(smem + (S::kStages - 1) * S::kStage));
+  }
+  if (item < 0 || item >= n_items) return;   // uniform
+  const int part = item / p.num_seqs;
+  const int b = item % p.num_seqs;
+  const SeqExtent ext = verify_extent(p, b);
+  const int q0 = ext.q0, lq = ext.lq, lk = ext.lk;
+  if (lq == 0) return;
+  // Several partitions: one past Lk is never merged.  A single partition
+  // always writes its rows (zeros where a row sees no key).
+  const int nblk = partition_blocks(p, ext, part);
+  if (nblk == 0 && p.num_partitions > 1) return;
+  const int kb0 = part * p.partition_tokens / kBlock;
+
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int j = lane % 16;     // row (of a row tile) / key (of a block) of this lane
+  const int g = lane / 16;     // lane group: keys 4g .. 4g + 3 of S^T
+  const int nbw = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
+
+  char* ring = smem + wave * S::kRing;
+  char* qlds = smem + kWaves * S::kRing;
+  const int64_t row_stride = static_cast<int64_t>(p.num_kv_heads) * S::kRow;
+  const int64_t blk_bytes = row_stride * kBlock;
+  const int32_t* btab = p.block_tables + static_cast<int64_t>(b) * p.max_blocks_per_seq;
+  const int nblk_ctx = (lk + kBlock - 1) / kBlock;
+
+  // ---- DMA source offsets.  Load u of a block moves its rows r = (1024 u
+  // + 16 l) / kRow; lane l's 16 bytes land at byte 16 l of that KiB and hold
+  // chunk pos ^ swizzle(r) of row r.
+  uint32_t dma_k_off[S::kDmaPerBlock], dma_v_off[S::kDmaPerBlock];
+#pragma unroll
+  for (int u = 0; u < S::kDmaPerBlock; ++u) {
+    const int byte = u * 1024 + lane * 16;
+    const int r = byte / S::kRow;
+    const int pos = (byte % S::kRow) / 16;
+    const int64_t base = r * row_stride + kvh * S::kRow;
+    dma_k_off[u] = static_cast<uint32_t>(base + (pos ^ k_swz<D>(r)) * 16);
+    dma_v_off[u] = static_cast<uint32_t>(base + (pos ^ v_swz<D>(r)) * 16);
+  }
+  // Block ids are scalar loads (wave-uniform indices), clamped to the
+  // context's blocks; an id outside the pool reads block 0 instead.
+  auto block_id = [&](int jb) __attribute__((always_inline)) {
+    return load_uniform_i32(btab, min(kb0 + wave + kWaves * jb, nblk_ctx - 1));
+  };
+  auto dma_block = [&](int blk, int slot) __attribute__((always_inline)) {
+    blk = blk >= 0 && blk < p.num_blocks ? blk : 0;
+    const int64_t off = static_cast<int64_t>(blk) * blk_bytes;
+    char* st = ring + slot * S::kStage;
+#pragma unroll
+    for (int u = 0; u < S::kDmaPerBlock; ++u) {
+      dma16(p.k_cache + off, dma_k_off[u], st + u * 1024);
+      dma16(p.v_cache + off, dma_v_off[u], st + S::kBlockBytes + u * 1024);
+    }
+  };
+  // Wait until at most `ahead` stages of this wave are still in flight.
+  auto wait_stages = [&](int ahead) __attribute__((always_inline)) {
+    constexpr int L = S::kLoadsPerStage;
+    switch (ahead) {
+      case 0: wait_vm<0>(); break;
+      case 1: wait_vm<L>(); break;
+      case 2: wait_vm<(S::kStages > 2 ? 2 * L : 0)>(); break;
+      case 3: wait_vm<(S::kStages > 3 ? 3 * L : 0)>(); break;
+      case 4: wait_vm<(S::kStages > 4 ? 4 * L : 0)>(); break;
+      case 5: wait_vm<(S::kStages > 5 ? 5 * L : 0)>(); break;
+      case 6: wait_vm<(S::kStages > 6 ? 6 * L : 0)>(); break;
+      default: wait_vm<(S::kStages > 7 ? 7 * L : 0)>(); break;
+    }
+  };
+
+  // ---- Q rows: the workgroup's DMA loads 1 KiB pieces of the packed rows
+  // (wave w takes pieces w, w + 4, ...) into the Q area; rows past G * Lq
+  // repeat row 0 (finite values, results never written).
+  {
+    const char* qbase = p.q + static_cast<int64_t>(q0) * p.num_heads * S::kRow;
+    for (int u = wave; u < S::kQDma; u += kWaves) {
+      const int byte = u * 1024 + lane * 16;
+      const int m = byte / S::kRow;
+      const int pos = (byte % S::kRow) / 16;
+      const int mm = m < G * lq ? m : 0;
+      const uint32_t off = static_cast<uint32_t>(
+          ((mm / G) * p.num_heads + kvh * G + mm % G) * S::kRow +
+          (pos ^ k_swz<D>(m)) * 16);
+      dma16(qbase, off, qlds + u * 1024);
+    }
+  }
+  // ---- ring prologue: stages 0 .. kStages - 2.
+  const int npro = min(S::kStages - 1, nbw);
+  for (int jb = 0; jb < npro; ++jb) dma_block(block_id(jb), jb);
+  int next_id = nbw > S::kStages - 1 ? block_id(S::kStages - 1) : 0;
+  // Q loads were issued before the prologue: they are done once only the
+  // prologue's loads remain.
+  wait_stages(npro);
+  lds_barrier();
+  uint4 qb[S::kQSteps][NT];
+#pragma unroll
+  for (int s = 0; s < S::kQSteps; ++s)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int m = n * 16 + j;
+      qb[s][n] = *reinterpret_cast<const uint4*>(
+          qlds + m * S::kRow + ((4 * s + g) ^ k_swz<D>(m)) * 16);
+    }
+
+  // Row constants: the last key each of this lane's rows may see.
+  int lim[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int m = n * 16 + j;
+    lim[n] = (p.causal && m < G * lq) ? lk - lq + m / G : lk - 1;
+  }
+  const int min_lim = p.causal ? lk - lq : lk - 1;   // over the real rows
+
+  // LDS read offsets inside a stage.  K (A of S^T): row j, chunk 4 s + g.
+  const int k_off = j * S::kRow;
+  const int k_x = k_swz<D>(j) * 16;
+  // V^T (A of O^T, transpose reads): lane (g, s') reads row 4 g + s' / 4,
+  // dimensions 16 dt + 4 (s' % 4) .. + 3; lane (g, i) receives V[4 g + e]
+  // [16 dt + i] for e = 0..3.
+  const int v_row = 4 * g + j / 4;
+  const int v_off = S::kBlockBytes + v_row * S::kRow + ((j % 4) / 2) * 16 + (j % 2) * 8;
+  const int v_x = v_swz<D>(v_row) * 16;
+
+  f32x4_v oacc[S::kDTiles][NT];
+#pragma unroll
+  for (int dt = 0; dt < S::kDTiles; ++dt)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) oacc[dt][n] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  float run_max[NT], run_sum[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    run_max[n] = -INFINITY;   // reference max of the row (scaled, log2)
+    run_sum[n] = 0.f;         // this lane's share of the row sum
+  }
+
+  auto compute = [&](int kb, char* st) __attribute__((always_inline)) {
+    const int kbase = kb * kBlock;
+    // V rows past Lk: zeros (this wave's own stage; LDS ops of one wave run
+    // in order, so the transpose reads below see them).
+    if (kbase + kBlock > lk) {
+#pragma unroll
+      for (int u = 0; u < S::kBlockBytes / 16 / kWave; ++u) {
+        const int c = u * kWave + lane;
+        if (kbase + c / S::kChunks >= lk)
+          *reinterpret_cast<uint4*>(st + S::kBlockBytes + c * 16) = make_uint4(0, 0, 0, 0);
+      }
+    }
+    // ---- S^T = K Q^T
+    f32x4_v sacc[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) sacc[n] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < S::kQSteps; ++s) {
+      const uint4 a = *reinterpret_cast<const uint4*>(st + k_off + (((4 * s + g) * 16) ^ k_x));
+#pragma unroll
+      for (int n = 0; n < NT; ++n) sacc[n] = mfma_qk(a, qb[s][n], sacc[n]);
+    }
+    // ---- mask: key 4 g + r of the block against each row's limit
+    if (kbase + kBlock - 1 > min_lim || kbase + kBlock > lk) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          sacc[n][r] = kbase + 4 * g + r <= lim[n] ? sacc[n][r] : -INFINITY;
+    }
+    // ---- online softmax.  Fast path: weights against the reference max,
+    // summed over the bfloat16-rounded values the PV step uses; a lane
+    // share <= 2^13 means every weight is.  The exact path (max over the
+    // row's 16 keys, rescale of O) runs on a row's first visible block and
+    // where its max grows by more than 2^8.
+    uint2 pb[NT];
+    float psum[NT];
+    auto weights = [&](int n) __attribute__((always_inline)) {
+      const float neg = run_max[n] == -INFINITY ? 0.f : -run_max[n];
+      const float w0 = fast_exp2(fmaf(sacc[n][0], p.scale_log2, neg));
+      const float w1 = fast_exp2(fmaf(sacc[n][1], p.scale_log2, neg));
+      const float w2 = fast_exp2(fmaf(sacc[n][2], p.scale_log2, neg));
+      const float w3 = fast_exp2(fmaf(sacc[n][3], p.scale_log2, neg));
+      pb[n] = make_uint2(pack_bf16x2(w0, w1), pack_bf16x2(w2, w3));
+      psum[n] = dot2_bf16(pb[n].y, kBf16PairOne, dot2_bf16(pb[n].x, kBf16PairOne, 0.f));
+    };
+    bool exact = false;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      weights(n);
+      exact = exact || run_max[n] == -INFINITY || !(psum[n] <= 8192.f);
+    }
+    if (__any(exact)) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        float t = fmaxf(fmaxf(sacc[n][0], sacc[n][1]), fmaxf(sacc[n][2], sacc[n][3]));
+        t = fmaxf(t, __shfl_xor(t, 16, kWave));
+        t = fmaxf(t, swap_halves(t)) * p.scale_log2;
+        const bool grow = t > run_max[n] + 8.f;
+        if (__any(grow)) {
+          const float nm = grow ? t : run_max[n];
+          const float alpha = run_max[n] == -INFINITY ? 0.f : fast_exp2(run_max[n] - nm);
+          run_max[n] = nm;
+          run_sum[n] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < S::kDTiles; ++dt) oacc[dt][n] *= alpha;
+          weights(n);
+        }
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) run_sum[n] += psum[n];
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int dt = 0; dt < S::kDTiles; ++dt) {
+      const uint2 a = lds_read_tr16(st + v_off + ((dt * 32) ^ v_x));
+#pragma unroll
+      for (int n = 0; n < NT; ++n) oacc[dt][n] = mfma_pv(a, pb[n], oacc[dt][n]);
+    }
+  };
+
+  // ---- main loop: block jb of this wave lives in stage jb % kStages.
+  for (int jb = 0; jb < nbw; ++jb) {
+    wait_stages(min(S::kStages - 2, nbw - 1 - jb));
+    const int nj = jb + S::kStages - 1;
+    if (nj < nbw) {
+      // stage (jb - 1) % kStages: computed last iteration, its reads done
+      wait_lgkm();
+      dma_block(next_id, nj % S::kStages);
+      next_id = block_id(nj + 1);
+    }
+    compute(kb0 + wave + kWaves * jb, ring + (jb % S::kStages) * S::kStage);
+  }
+
+  // ---- combine the four waves.  Every wave is past its loop (and so past
+  // its last LDS read of the rings and of Q) after this barrier.
+  float total[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    float t = run_sum[n] + __shfl_xor(run_sum[n], 16, kWave);
+    total[n] = t + swap_halves(t);
+  }
+  __syncthreads();
+  {
+    char* ow = smem + static_cast<size_t>(wave) * S::kRows * S::kORow;
+    float2* ml = reinterpret_cast<float2*>(smem + kWaves * S::kRows * S::kORow);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int m = n * 16 + j;
+#pragma unroll
+      for (int dt = 0; dt < S::kDTiles; ++dt)
+        *reinterpret_cast<float4*>(ow + m * S::kORow + (dt * 16 + 4 * g) * 4) =
+            make_float4(oacc[dt][n][0], oacc[dt][n][1], oacc[dt][n][2], oacc[dt][n][3]);
+      if (g == 0) ml[wave * S::kRows + m] = make_float2(run_max[n], total[n]);
+    }
+  }
+  __syncthreads();
+  const float2* ml = reinterpret_cast<const float2*>(smem + kWaves * S::kRows * S::kORow);
+  const int c = tid % S::kTpr;   // dimensions 8 c .. 8 c + 7
+#pragma unroll
+  for (int m0 = 0; m0 < S::kRows; m0 += S::kRowsPerPass) {
+    const int m = m0 + tid / S::kTpr;
+    if (m >= S::kRows || m >= G * lq) continue;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, ml[w * S::kRows + m].x);
+    float l = 0.f, o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float2 st = ml[w * S::kRows + m];
+        const float a = fast_exp2(st.x - mx);   // 0 for a wave that saw nothing
+        l = fmaf(a, st.y, l);
+        const char* src = smem + static_cast<size_t>(w) * S::kRows * S::kORow +
+                          m * S::kORow + c * 32;
+        const float4 x = *reinterpret_cast<const float4*>(src);
+        const float4 y = *reinterpret_cast<const float4*>(src + 16);
+        o[0] = fmaf(a, x.x, o[0]); o[1] = fmaf(a, x.y, o[1]);
+        o[2] = fmaf(a, x.z, o[2]); o[3] = fmaf(a, x.w, o[3]);
+        o[4] = fmaf(a, y.x, o[4]); o[5] = fmaf(a, y.y, o[5]);
+        o[6] = fmaf(a, y.z, o[6]); o[7] = fmaf(a, y.w, o[7]);
+      }
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int i = m / G;
+    const int head = kvh * G + m % G;
+    if (p.num_partitions == 1) {
+      uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) +
+                       ((static_cast<int64_t>(q0) + i) * p.num_heads + head) * D + c * 8;
+      *reinterpret_cast<uint4*>(orow) =
+          make_uint4(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
+                     pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv));
+    } else {
+      // A partial: normalised output as binary16 (scaled by 2^-16, sum
+      // negated, when some |o| of the row reaches 2^15), max, sum.
+      float big = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) big = fmaxf(big, fabsf(o[e] * inv));
+#pragma unroll
+      for (int x = 1; x < S::kTpr; x *= 2) big = fmaxf(big, __shfl_xor(big, x, kWave));
+      const bool is_big = big >= kPartialBig;
+      const int64_t slot =
+          ((static_cast<int64_t>(b) * p.max_seqlen_q + i) * p.num_heads + head) *
+              p.num_partitions + part;
+      uint16_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = partial_f16(o[e] * inv, is_big);
+      *reinterpret_cast<uint4*>(p.ws_acc_h + slot * D + c * 8) =
+          make_uint4(h[0] | (static_cast<uint32_t>(h[1]) << 16),
+                     h[2] | (static_cast<uint32_t>(h[3]) << 16),
+                     h[4] | (static_cast<uint32_t>(h[5]) << 16),
+                     h[6] | (static_cast<uint32_t>(h[7]) << 16));
+      if (c == 0) {
+        p.ws_max[slot] = mx;
+        p.ws_sum[slot] = is_big ? -l : l;
+      }
+    }
+  }
+}
+
+// Merge the partitions of one (sequence, row, query head): row i of
+// sequence b reads the partitions that hold a key it sees.
+template <int D>
+__global__ __launch_bounds__(D) void verify_merge_kernel(VerifyParams p) {
+  const int h = blockIdx.x % p.num_heads;
+  const int rest = blockIdx.x / p.num_heads;
+  const int i = rest % p.max_seqlen_q;
+  const int b = rest / p.max_seqlen_q;
+  const int d = threadIdx.x;
+  const SeqExtent e = verify_extent(p, b);
+  if (i >= e.lq) return;
+  int kend = p.causal ? e.lk - e.lq + i + 1 : e.lk;
+  kend = kend < 0 ? 0 : kend;
+  int np = (kend + p.partition_tokens - 1) / p.partition_tokens;
+  np = np > p.num_partitions ? p.num_partitions : np;
+  const int64_t slot0 =
+      ((static_cast<int64_t>(b) * p.max_seqlen_q + i) * p.num_heads + h) * p.num_partitions;
+  const float o = merge_partials<8>(np, [&](int k, float& m, float& l, float& acc)
+                                            __attribute__((always_inline)) {
+    const int64_t s = slot0 + k;
+    const float lraw = p.ws_sum[s];
+    const float ov = f16_to_f32(p.ws_acc_h[s * D + d]);
+    m = p.ws_max[s];
+    l = fabsf(lraw);
+    acc = l * (lraw < 0.f ? ov * kPartialGrow : ov);
+  });
+  uint16_t* out = reinterpret_cast<uint16_t*>(p.out) +
+                  ((static_cast<int64_t>(e.q0) + i) * p.num_heads + h) * D + d;
+  *out = f32_to_bf16_rne(o);
+}
+
+constexpr int kPlanThreads = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void verify_plan_kernel(
+    VerifyParams p, int32_t* __restrict__ order) {
+  __shared__ int bins[kPlanBins];
+  __shared__ int wave_sum[kPlanThreads / kWave];
+  longest_first_order<kPlanThreads, kPlanBins, 4>(
+      p.num_seqs * p.num_partitions, [&](int item) { return item_weight(p, item); },
+      order, bins, wave_sum);
+}
+
+template <int D, int G, int NT>
+hipError_t launch_nt(const VerifyParams& prm, const VerifyPlan& plan, hipStream_t s) {
+  using S = VerifyShape<D, NT>;
+  static bool raised = false;   // once per kernel instantiation
+  if (!raised) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&verify_kernel<D, G, NT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(S::kLds));
+    if (e != hipSuccess) return e;
+    raised = true;
+  }
+  const int64_t wgs = static_cast<int64_t>(prm.num_seqs) * plan.num_partitions *
+                      prm.num_kv_heads;
+  if (plan.use_order) {
+    hipLaunchKernelGGL(verify_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, prm,
+                       const_cast<int32_t*>(prm.order));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((verify_kernel<D, G, NT>), dim3(static_cast<unsigned>(wgs)),
+                     dim3(kThreads), S::kLds, s, prm);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.num_partitions == 1) return e;
+  const int64_t merges = static_cast<int64_t>(prm.num_seqs) * prm.max_seqlen_q *
+                         prm.num_heads;
+  hipLaunchKernelGGL((verify_merge_kernel<D>), dim3(static_cast<unsigned>(merges)),
+                     dim3(D), 0, s, prm);
+  return hipGetLastError();
+}
+
+template <int D, int G>
+hipError_t launch_g(const VerifyParams& prm, const VerifyPlan& plan, hipStream_t s) {
+  switch (plan.row_tiles) {
+    case 1: return launch_nt<D, G, 1>(prm, plan, s);
+    case 2: return launch_nt<D, G, 2>(prm, plan, s);
+    case 4: return launch_nt<D, G, 4>(prm, plan, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+hipError_t launch_d(const VerifyParams& prm, const VerifyPlan& plan, int g,
+                    hipStream_t s) {
+  switch (g) {
+    case 1: return launch_g<D, 1>(prm, plan, s);
+    case 2: return launch_g<D, 2>(prm, plan, s);
+    case 4: return launch_g<D, 4>(prm, plan, s);
+    case 8: return launch_g<D, 8>(prm, plan, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Partitions: few enough that most launches need no merge, enough that a
+// small batch still fills the chip.  One workgroup per CU fits (its LDS),
+// so the plan aims at ~4 workgroups per CU.
+constexpr int64_t kTargetWorkgroups = 1024;
+constexpr int kMinPartitionTokens = 256;
+// The workgroups rank the items themselves up to one item per thread.
+constexpr int kInlineRankItems = kThreads;
+
+}  // namespace
+
+VerifyPlan plan_verify(int num_seqs, int num_heads, int num_kv_heads,
+                       int head_dim, int max_seqlen_q, int max_seqlen_k) {
+  VerifyPlan plan{};
+  if (num_seqs <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0)
+    return plan;
+  const int g = num_heads / num_kv_heads;
+  const int64_t rows = static_cast<int64_t>(g) * max_seqlen_q;
+  if ((g != 1 && g != 2 && g != 4 && g != 8) || (head_dim != 64 && head_dim != 128) ||
+      max_seqlen_q <= 0 || rows > 64 || max_seqlen_k <= 0)
+    return plan;
+  plan.use = true;
+  plan.row_tiles = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+  const int64_t groups = static_cast<int64_t>(num_seqs) * num_kv_heads;
+  int64_t parts = groups >= kTargetWorkgroups
+                      ? 1
+                      : (kTargetWorkgroups + groups - 1) / groups;
+  int64_t tokens = (max_seqlen_k + parts - 1) / parts;
+  tokens = (tokens + 63) / 64 * 64;
+  if (tokens < kMinPartitionTokens) tokens = kMinPartitionTokens;
+  plan.partition_tokens = static_cast<int>(tokens);
+  plan.num_partitions = static_cast<int>((max_seqlen_k + tokens - 1) / tokens);
+  size_t bytes = 0;
+  if (plan.num_partitions > 1) {
+    const size_t slots = static_cast<size_t>(num_seqs) * max_seqlen_q * num_heads *
+                         plan.num_partitions;
+    plan.off_max = 0;
+    plan.off_sum = align256(slots * sizeof(float));
+    plan.off_acc = plan.off_sum + align256(slots * sizeof(float));
+    bytes = plan.off_acc + align256(slots * static_cast<size_t>(head_dim) * 2);
+  }
+  const int64_t items = static_cast<int64_t>(num_seqs) * plan.num_partitions;
+  plan.use_order = items > kInlineRankItems;
+  if (plan.use_order) {
+    plan.off_order = bytes;
+    bytes += align256(static_cast<size_t>(items) * sizeof(int32_t));
+  }
+  plan.workspace_bytes = bytes;
+  return plan;
+}
+
+hipError_t launch_verify(const PrefillArgs& a, const VerifyPlan& plan,
+                         hipStream_t stream) {
+  const int64_t wgs = static_cast<int64_t>(a.num_seqs) * plan.num_partitions *
+                      a.num_kv_heads;
+  const int64_t merges = static_cast<int64_t>(a.num_seqs) * a.max_seqlen_q * a.num_heads;
+  if (wgs > 0x7fffffff || merges > 0x7fffffff) return hipErrorNotSupported;
+  VerifyParams prm{};
+  prm.out = a.out;
+  prm.q = static_cast<const char*>(a.q);
+  prm.total_q = a.total_q;
+  prm.k_cache = static_cast<const char*>(a.k_cache);
+  prm.v_cache = static_cast<const char*>(a.v_cache);
+  prm.num_blocks = a.num_blocks;
+  prm.cu_q = a.cu_seqlens_q;
+  prm.cu_k = a.cu_seqlens_k;
+  prm.max_seqlen_q = a.max_seqlen_q;
+  prm.max_seqlen_k = a.max_seqlen_k;
+  prm.block_tables = a.block_tables;
+  prm.max_blocks_per_seq = a.max_blocks_per_seq;
+  prm.num_seqs = a.num_seqs;
+  prm.num_heads = a.num_heads;
+  prm.num_kv_heads = a.num_kv_heads;
+  prm.scale_log2 = a.scale * kLog2e;
+  prm.causal = a.causal ? 1 : 0;
+  prm.partition_tokens = plan.partition_tokens;
+  prm.num_partitions = plan.num_partitions;
+  char* ws = static_cast<char*>(a.workspace);
+  if (plan.num_partitions > 1) {
+    prm.ws_max = reinterpret_cast<float*>(ws + plan.off_max);
+    prm.ws_sum = reinterpret_cast<float*>(ws + plan.off_sum);
+    prm.ws_acc_h = reinterpret_cast<uint16_t*>(ws + plan.off_acc);
+  }
+  if (plan.use_order) prm.order = reinterpret_cast<const int32_t*>(ws + plan.off_order);
+  else prm.rank_inline = 1;
+  const int g = a.num_heads / a.num_kv_heads;
+  if (a.head_dim == 128) return launch_d<128>(prm, plan, g, stream);
+  return launch_d<64>(prm, plan, g, stream);
+}
+
+}  // namespace pa
