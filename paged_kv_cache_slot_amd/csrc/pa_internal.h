@@ -163,16 +163,17 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 // Small-row path of the varlen prefill (bfloat16): used when the packed
 // rows per KV head, G * max_seqlen_q, are at most 64 (a verify pass, a
 // one-row chunk).  Split-context partitions over the keys, merged when
-// there are several.
+// there are several; a plan kernel orders the work longest first and
+// persistent workgroups draw it from a counter in the workspace.
 struct VerifyPlan {
   bool use;              // these sizes take the small-row path
   int row_tiles;         // 16-row tiles per KV head: 1, 2 or 4
   int partition_tokens;  // keys per partition (multiple of 64)
   int num_partitions;    // >= 1
-  bool use_order;        // longest-first schedule from a plan kernel
   size_t workspace_bytes;
   size_t off_max, off_sum, off_acc;  // partials (num_partitions > 1)
-  size_t off_order;                  // int32 [num_seqs * num_partitions]
+  size_t off_order;      // int32 [num_seqs * num_partitions], longest first
+  size_t off_counter;    // int32 ticket counter
 };
 
 VerifyPlan plan_verify(int num_seqs, int num_heads, int num_kv_heads,

@@ -14,14 +14,22 @@
 // Design (MI355X-first).  Like decode this is an HBM stream -- every K/V
 // byte of a KV head serves only G * Lq rows -- but with up to 64 rows per
 // KV head the dot products belong on MFMA:
-//  * one workgroup (4 waves) per (sequence, partition, KV head); the G * Lq
-//    rows of a KV head are packed into NT tiles of 16 (row m = position
-//    m / G, head m % G), so one K/V byte loaded serves all of them;
+//  * a work item is (sequence, partition, KV head), taken by a workgroup of
+//    4 waves; the G * Lq rows of a KV head are packed into NT tiles of 16
+//    (row m = position m / G, head m % G), so one K/V byte loaded serves all
+//    of them;
+//  * persistent workgroups, one per CU, draw (sequence, partition, KV head)
+//    tickets from a counter in the workspace, longest items first (a plan
+//    kernel orders them): the 8 XCDs of the chip stream at different rates
+//    (~0.72 to ~0.85 TB/s each, measured), and the dispatcher's fixed round
+//    robin share per XCD would leave the fast XCDs idle for the last ~15 %
+//    of the launch;
 //  * wave w streams cache blocks w, w + 4, ... of its partition through its
-//    own ring of LDS stages (one 16-token K block and V block per stage),
-//    filled by LDS DMA (global_load_lds_dwordx4, 16-byte chunks XOR-
-//    swizzled by row); waves never wait for each other inside the loop, and
-//    kStages - 1 blocks per wave are in flight while one is computed;
+//    own ring of LDS stages (one 16-token K block and V block per stage; 5
+//    stages at D = 128), filled by LDS DMA (global_load_lds_dwordx4, 16-byte
+//    chunks XOR-swizzled by row); waves never wait for each other inside
+//    the loop, and kStages - 1 blocks per wave are in flight while one is
+//    computed;
 //  * per block: S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = 16 keys from
 //    LDS, B = Q^T held in registers), online softmax per lane (a lane holds
 //    four keys of one row), O^T += V^T P^T with v_mfma_f32_16x16x16_bf16
@@ -37,6 +45,8 @@
 //    weight exactly 0, and V rows past Lk are zeroed in LDS (a NaN there
 //    would survive a multiplication by zero).
 #include <math.h>
+
+#include <atomic>
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -74,18 +84,24 @@ template <int D, int NT>
 struct VerifyShape {
   static constexpr int kRow = D * 2;                   // bytes per key row
   static constexpr int kChunks = kRow / 16;            // 16-byte chunks per row
-  static constexpr int kRowsPerBank = 256 / kRow;      // rows per 256-byte bank period
   static constexpr int kBlockBytes = kBlock * kRow;    // one block of one KV head
   static constexpr int kDmaPerBlock = kBlockBytes / 1024;
   static constexpr int kStage = 2 * kBlockBytes;       // K block, then V block
-  // Each wave owns 32 KiB of ring: 4 stages at D = 128, 8 at D = 64.
-  static constexpr int kStages = 32768 / kStage;
-  static constexpr int kRing = kStages * kStage;
+  // One workgroup per CU with all of its LDS: 5 stages per wave at
+  // D = 128, 10 at D = 64 (two workgroups per CU with 2-stage rings, whose
+  // set-up and epilogue overlap, measured slower once workgroups are
+  // persistent).  Stage-major: stage s of wave w at (s * kWaves + w) * kStage.
+  static constexpr int kWgsPerCu = 1;
+  static constexpr int kStages = 160 * 1024 / kWgsPerCu / (kWaves * kStage);
   static constexpr int kLoadsPerStage = 2 * kDmaPerBlock;   // per lane
   static constexpr int kRows = NT * 16;                // packed query rows
   static constexpr int kQBytes = kRows * kRow;
   static constexpr int kQDma = kQBytes / 1024;
-  static constexpr size_t kLds = static_cast<size_t>(kWaves) * kRing + kQBytes;
+  static constexpr size_t kRingBytes = static_cast<size_t>(kStages) * kWaves * kStage;
+  // The last stage of every wave is first written after the Q rows have
+  // been read into registers: it holds them (and the ranking scratch, at its
+  // end) before that.
+  static constexpr size_t kLastStage = static_cast<size_t>(kStages - 1) * kWaves * kStage;
   static constexpr int kQSteps = D / 32;               // QK MFMAs per row tile
   static constexpr int kDTiles = D / 16;               // O^T tiles per row tile
   // Combine: each wave's O as fp32 rows padded by 16 bytes (so the 16 rows
@@ -95,10 +111,16 @@ struct VerifyShape {
       static_cast<size_t>(kWaves) * kRows * kORow + kWaves * kRows * 8;
   static constexpr int kTpr = D / 8;                   // combine threads per row
   static constexpr int kRowsPerPass = kThreads / kTpr;
+  // The next ticket, broadcast through LDS past the combine area (written
+  // and read only while no DMA is in flight).
+  static constexpr size_t kTicket = kCombine;
+  static constexpr size_t kLds = kRingBytes > kCombine + 16 ? kRingBytes : kCombine + 16;
   static_assert(kBlockBytes % 1024 == 0 && kQBytes % 1024 == 0, "DMA split");
-  static_assert(kStages >= 2 && kStages * kLoadsPerStage <= 56, "vmcnt range");
-  static_assert(kLds <= 160 * 1024 && kCombine <= kLds, "LDS per CU");
-  static_assert(kStage >= (kThreads + 5) * 4, "ranking scratch in one stage");
+  static_assert(kStages >= 2 && (kStages - 1) * kLoadsPerStage <= 56, "vmcnt range");
+  static_assert(kStages <= 10, "wait_stages cases");
+  static_assert(kLds <= 160 * 1024 / kWgsPerCu, "LDS per CU");
+  static_assert(kStages * kWaves * kStage == 160 * 1024, "the whole LDS");
+  static_assert(kLastStage + kQBytes <= kRingBytes, "Q rows in the last stages");
 };
 
 // 16-byte chunk swizzles (XOR on the chunk index, per row).  K and Q rows:
@@ -135,11 +157,12 @@ struct VerifyParams {
   int causal;
   int partition_tokens;      // keys per partition (a multiple of 64)
   int num_partitions;
-  // Work items (partition * num_seqs + b), heaviest first: `order` from the
-  // plan kernel, or ranked by each workgroup itself (rank_inline), or the
-  // natural order.
+  // Work items (partition * num_seqs + b), heaviest first, from the plan
+  // kernel.  Ticket t is item order[t / Hkv] for KV head t % Hkv; the
+  // workgroups draw tickets from `counter` (zeroed by the plan kernel).
   const int32_t* order;
-  int rank_inline;
+  int* counter;
+  int num_tickets;
   // Partials (num_partitions > 1): slot ((b * max_seqlen_q + i) * Hq + h) *
   // num_partitions + partition.
   float* ws_max;
@@ -172,41 +195,34 @@ __device__ __forceinline__ int item_weight(const VerifyParams& p, int item) {
   return w < kPlanBins ? w : kPlanBins - 1;
 }
 
-// One workgroup per CU (its LDS): one wave per SIMD, all registers to it.
+// One work ticket: (sequence, partition, KV head).  Returns the next
+// ticket, drawn while the combine runs (no DMA in flight then).
 template <int D, int G, int NT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
-verify_kernel(VerifyParams p) {
+__device__ __forceinline__ int verify_item(const VerifyParams& p, int ticket, char* smem) {
   using S = VerifyShape<D, NT>;
-  extern __shared__ __align__(16) char smem[];
-  // [wave 0 ring .. wave 3 ring][Q rows]; reused by the final combine.
-
-  // Workgroup lin takes work item order[lin / Hkv] for KV head lin % Hkv:
-  // the Hkv workgroups of one item read adjacent 256-byte pieces of the same
-  // cache rows, and the dispatcher spreads them over the 8 XCDs.
+  // Stages, stage-major; reused by the final combine.
   const int tid = threadIdx.x;
-  const int kvh = blockIdx.x % p.num_kv_heads;
-  const int rank = blockIdx.x / p.num_kv_heads;
+  int* s_ticket = reinterpret_cast<int*>(smem + S::kTicket);
+  auto next_ticket = [&]() __attribute__((always_inline)) {
+    if (tid == 0) *s_ticket = atomicAdd(p.counter, 1);
+    __syncthreads();
+    return *s_ticket;
+  };
+  // The Hkv tickets of one item are consecutive: workgroups running at the
+  // same time read adjacent 256-byte pieces of the same cache rows.
+  const int kvh = ticket % p.num_kv_heads;
   const int n_items = p.num_seqs * p.num_partitions;
-  int item = rank;
-  if (p.order != nullptr) {
-    item = load_uniform_i32(p.order, rank);
-  } else if (p.rank_inline) {
-    // Scratch: wave 0's last ring stage, which no DMA writes before that
-    // wave's first loop iteration (after the workgroup barrier below).
-    item = inline_ranked_item<kThreads>(
-        n_items, rank, [&](int it) { return item_weight(p, it); },
-        reinterpret_cast<int*>(smem + (S::kStages - 1) * S::kStage));
-  }
-  if (item < 0 || item >= n_items) return;   // uniform
+  const int item = load_uniform_i32(p.order, ticket / p.num_kv_heads);
+  if (item < 0 || item >= n_items) return next_ticket();   // uniform
   const int part = item / p.num_seqs;
   const int b = item % p.num_seqs;
   const SeqExtent ext = verify_extent(p, b);
   const int q0 = ext.q0, lq = ext.lq, lk = ext.lk;
-  if (lq == 0) return;
+  if (lq == 0) return next_ticket();
   // Several partitions: one past Lk is never merged.  A single partition
   // always writes its rows (zeros where a row sees no key).
   const int nblk = partition_blocks(p, ext, part);
-  if (nblk == 0 && p.num_partitions > 1) return;
+  if (nblk == 0 && p.num_partitions > 1) return next_ticket();
   const int kb0 = part * p.partition_tokens / kBlock;
 
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -215,8 +231,10 @@ verify_kernel(VerifyParams p) {
   const int g = lane / 16;     // lane group: keys 4g .. 4g + 3 of S^T
   const int nbw = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
 
-  char* ring = smem + wave * S::kRing;
-  char* qlds = smem + kWaves * S::kRing;
+  char* qlds = smem + S::kLastStage;
+  auto stage = [&](int slot) __attribute__((always_inline)) {
+    return smem + (slot * kWaves + wave) * S::kStage;
+  };
   const int64_t row_stride = static_cast<int64_t>(p.num_kv_heads) * S::kRow;
   const int64_t blk_bytes = row_stride * kBlock;
   const int32_t* btab = p.block_tables + static_cast<int64_t>(b) * p.max_blocks_per_seq;
@@ -243,7 +261,7 @@ verify_kernel(VerifyParams p) {
   auto dma_block = [&](int blk, int slot) __attribute__((always_inline)) {
     blk = blk >= 0 && blk < p.num_blocks ? blk : 0;
     const int64_t off = static_cast<int64_t>(blk) * blk_bytes;
-    char* st = ring + slot * S::kStage;
+    char* st = stage(slot);
 #pragma unroll
     for (int u = 0; u < S::kDmaPerBlock; ++u) {
       dma16(p.k_cache + off, dma_k_off[u], st + u * 1024);
@@ -261,7 +279,8 @@ verify_kernel(VerifyParams p) {
       case 4: wait_vm<(S::kStages > 4 ? 4 * L : 0)>(); break;
       case 5: wait_vm<(S::kStages > 5 ? 5 * L : 0)>(); break;
       case 6: wait_vm<(S::kStages > 6 ? 6 * L : 0)>(); break;
-      default: wait_vm<(S::kStages > 7 ? 7 * L : 0)>(); break;
+      case 7: wait_vm<(S::kStages > 7 ? 7 * L : 0)>(); break;
+      default: wait_vm<(S::kStages > 8 ? 8 * L : 0)>(); break;
     }
   };
 
@@ -298,6 +317,8 @@ verify_kernel(VerifyParams p) {
       qb[s][n] = *reinterpret_cast<const uint4*>(
           qlds + m * S::kRow + ((4 * s + g) ^ k_swz<D>(m)) * 16);
     }
+  // The loop's first DMA goes to the last stages, which hold the Q rows.
+  lds_barrier();
 
   // Row constants: the last key each of this lane's rows may see.
   int lim[NT];
@@ -421,7 +442,7 @@ verify_kernel(VerifyParams p) {
       dma_block(next_id, nj % S::kStages);
       next_id = block_id(nj + 1);
     }
-    compute(kb0 + wave + kWaves * jb, ring + (jb % S::kStages) * S::kStage);
+    compute(kb0 + wave + kWaves * jb, stage(jb % S::kStages));
   }
 
   // ---- combine the four waves.  Every wave is past its loop (and so past
@@ -433,6 +454,8 @@ verify_kernel(VerifyParams p) {
     total[n] = t + swap_halves(t);
   }
   __syncthreads();
+  int next = 0;
+  if (tid == 0) next = atomicAdd(p.counter, 1);
   {
     char* ow = smem + static_cast<size_t>(wave) * S::kRows * S::kORow;
     float2* ml = reinterpret_cast<float2*>(smem + kWaves * S::kRows * S::kORow);
@@ -510,7 +533,31 @@ verify_kernel(VerifyParams p) {
       }
     }
   }
+  if (tid == 0) *s_ticket = next;
+  __syncthreads();
+  return *s_ticket;
 }
+
+// Persistent workgroups (as many as fit on the chip at once) draw tickets
+// until none are left: the XCDs of one chip do not stream at the same rate,
+// and a fixed share of the work per XCD (the dispatcher deals workgroups to
+// the XCDs round robin) would leave the fast ones idle at the end.
+template <int D, int G, int NT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
+    VerifyShape<D, NT>::kWgsPerCu, VerifyShape<D, NT>::kWgsPerCu))) void
+verify_kernel(VerifyParams p) {
+  using S = VerifyShape<D, NT>;
+  extern __shared__ __align__(16) char smem[];
+  int* s_ticket = reinterpret_cast<int*>(smem + S::kTicket);
+  if (threadIdx.x == 0) *s_ticket = atomicAdd(p.counter, 1);
+  __syncthreads();
+  int t = *s_ticket;
+  while (t < p.num_tickets) {
+    __syncthreads();   // every thread has read the ticket
+    t = verify_item<D, G, NT>(p, __builtin_amdgcn_readfirstlane(t), smem);
+  }
+}
+
 
 // Merge the partitions of one (sequence, row, query head): row i of
 // sequence b reads the partitions that hold a key it sees.
@@ -545,13 +592,30 @@ __global__ __launch_bounds__(D) void verify_merge_kernel(VerifyParams p) {
 
 constexpr int kPlanThreads = 1024;
 
+// The longest-first order of the work items, and a zero ticket counter.
 __global__ __launch_bounds__(kPlanThreads) void verify_plan_kernel(
     VerifyParams p, int32_t* __restrict__ order) {
   __shared__ int bins[kPlanBins];
   __shared__ int wave_sum[kPlanThreads / kWave];
+  if (threadIdx.x == 0) *p.counter = 0;
   longest_first_order<kPlanThreads, kPlanBins, 4>(
       p.num_seqs * p.num_partitions, [&](int item) { return item_weight(p, item); },
       order, bins, wave_sum);
+}
+
+// Compute units of the current device (looked up once per device).
+int device_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 template <int D, int G, int NT>
@@ -565,17 +629,16 @@ hipError_t launch_nt(const VerifyParams& prm, const VerifyPlan& plan, hipStream_
     if (e != hipSuccess) return e;
     raised = true;
   }
-  const int64_t wgs = static_cast<int64_t>(prm.num_seqs) * plan.num_partitions *
-                      prm.num_kv_heads;
-  if (plan.use_order) {
-    hipLaunchKernelGGL(verify_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, prm,
-                       const_cast<int32_t*>(prm.order));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  // As many workgroups as the chip holds at once (fewer for a small launch).
+  const int64_t slots = static_cast<int64_t>(device_cus()) * S::kWgsPerCu;
+  const int64_t wgs = prm.num_tickets < slots ? prm.num_tickets : slots;
+  hipLaunchKernelGGL(verify_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, prm,
+                     const_cast<int32_t*>(prm.order));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((verify_kernel<D, G, NT>), dim3(static_cast<unsigned>(wgs)),
                      dim3(kThreads), S::kLds, s, prm);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess || plan.num_partitions == 1) return e;
   const int64_t merges = static_cast<int64_t>(prm.num_seqs) * prm.max_seqlen_q *
                          prm.num_heads;
@@ -608,13 +671,10 @@ hipError_t launch_d(const VerifyParams& prm, const VerifyPlan& plan, int g,
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// Partitions: few enough that most launches need no merge, enough that a
-// small batch still fills the chip.  One workgroup per CU fits (its LDS),
-// so the plan aims at ~4 workgroups per CU.
+// Partitions: few enough that most launches need no merge, enough tickets
+// (~4 per workgroup slot) that a small batch still balances over the chip.
 constexpr int64_t kTargetWorkgroups = 1024;
 constexpr int kMinPartitionTokens = 256;
-// The workgroups rank the items themselves up to one item per thread.
-constexpr int kInlineRankItems = kThreads;
 
 }  // namespace
 
@@ -649,11 +709,10 @@ VerifyPlan plan_verify(int num_seqs, int num_heads, int num_kv_heads,
     bytes = plan.off_acc + align256(slots * static_cast<size_t>(head_dim) * 2);
   }
   const int64_t items = static_cast<int64_t>(num_seqs) * plan.num_partitions;
-  plan.use_order = items > kInlineRankItems;
-  if (plan.use_order) {
-    plan.off_order = bytes;
-    bytes += align256(static_cast<size_t>(items) * sizeof(int32_t));
-  }
+  plan.off_order = bytes;
+  bytes += align256(static_cast<size_t>(items) * sizeof(int32_t));
+  plan.off_counter = bytes;
+  bytes += 256;
   plan.workspace_bytes = bytes;
   return plan;
 }
@@ -690,8 +749,9 @@ hipError_t launch_verify(const PrefillArgs& a, const VerifyPlan& plan,
     prm.ws_sum = reinterpret_cast<float*>(ws + plan.off_sum);
     prm.ws_acc_h = reinterpret_cast<uint16_t*>(ws + plan.off_acc);
   }
-  if (plan.use_order) prm.order = reinterpret_cast<const int32_t*>(ws + plan.off_order);
-  else prm.rank_inline = 1;
+  prm.order = reinterpret_cast<const int32_t*>(ws + plan.off_order);
+  prm.counter = reinterpret_cast<int*>(ws + plan.off_counter);
+  prm.num_tickets = static_cast<int>(wgs);
   const int g = a.num_heads / a.num_kv_heads;
   if (a.head_dim == 128) return launch_d<128>(prm, plan, g, stream);
   return launch_d<64>(prm, plan, g, stream);
