@@ -8,6 +8,9 @@
 
 namespace pa {
 
+// Compute units of the current device (looked up once per device).
+int device_cus();
+
 // ---- store -------------------------------------------------------------
 hipError_t launch_store_kv(const void* k, const void* v, void* k_cache,
                            void* v_cache, const int32_t* slot_mapping,
@@ -168,6 +171,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 struct VerifyPlan {
   bool use;              // these sizes take the small-row path
   int row_tiles;         // 16-row tiles per KV head: 1, 2 or 4
+  int heads_per_item;    // KV heads one workgroup takes at a time: 1 or 2
   int partition_tokens;  // keys per partition (multiple of 64)
   int num_partitions;    // >= 1
   size_t workspace_bytes;

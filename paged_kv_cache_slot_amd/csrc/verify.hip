@@ -24,12 +24,16 @@
 //    (~0.72 to ~0.85 TB/s each, measured), and the dispatcher's fixed round
 //    robin share per XCD would leave the fast XCDs idle for the last ~15 %
 //    of the launch;
-//  * wave w streams cache blocks w, w + 4, ... of its partition through its
-//    own ring of LDS stages (one 16-token K block and V block per stage; 5
-//    stages at D = 128), filled by LDS DMA (global_load_lds_dwordx4, 16-byte
-//    chunks XOR-swizzled by row); waves never wait for each other inside
-//    the loop, and kStages - 1 blocks per wave are in flight while one is
-//    computed;
+//  * wave w streams cache blocks w, w + 4, ... of its partition with 16-byte
+//    loads into registers, kDepth blocks ahead, and writes each block to
+//    its own LDS stage (16-byte chunks XOR-swizzled by row) right before
+//    computing it; waves never wait for each other inside the loop.  Loads
+//    into registers stream faster than LDS DMA here (~6.7 against ~6.3 TB/s
+//    measured on this access pattern);
+//  * with one row tile and an even number of KV heads a work item takes
+//    two adjacent KV heads: each token's read is then one 512-byte piece,
+//    which streams at the chip's full read rate (~7.2 TB/s measured, 6.7
+//    for 256-byte pieces);
 //  * per block: S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = 16 keys from
 //    LDS, B = Q^T held in registers), online softmax per lane (a lane holds
 //    four keys of one row), O^T += V^T P^T with v_mfma_f32_16x16x16_bf16
@@ -80,61 +84,60 @@ __device__ __forceinline__ f32x4_v mfma_pv(uint2 a, uint2 b, f32x4_v c) {
                                                    c, 0, 0, 0);
 }
 
-template <int D, int NT>
+// HP KV heads per work item: their rows are adjacent in every cache row, so
+// one item reads HP * 2D contiguous bytes per token.
+template <int D, int NT, int HP>
 struct VerifyShape {
-  static constexpr int kRow = D * 2;                   // bytes per key row
-  static constexpr int kChunks = kRow / 16;            // 16-byte chunks per row
-  static constexpr int kBlockBytes = kBlock * kRow;    // one block of one KV head
-  static constexpr int kDmaPerBlock = kBlockBytes / 1024;
+  static constexpr int kRow = D * 2;                   // bytes of one head's row
+  static constexpr int kChunks = kRow / 16;            // 16-byte chunks per head row
+  static constexpr int kPiece = HP * kRow;             // bytes per token read
+  static constexpr int kBlockBytes = kBlock * kPiece;  // one block of the HP heads
+  static constexpr int kLoads = kBlockBytes / 1024;    // 16-byte loads per lane, K or V
   static constexpr int kStage = 2 * kBlockBytes;       // K block, then V block
-  // One workgroup per CU with all of its LDS: 5 stages per wave at
-  // D = 128, 10 at D = 64 (two workgroups per CU with 2-stage rings, whose
-  // set-up and epilogue overlap, measured slower once workgroups are
-  // persistent).  Stage-major: stage s of wave w at (s * kWaves + w) * kStage.
-  static constexpr int kWgsPerCu = 1;
-  static constexpr int kStages = 160 * 1024 / kWgsPerCu / (kWaves * kStage);
-  static constexpr int kLoadsPerStage = 2 * kDmaPerBlock;   // per lane
-  static constexpr int kRows = NT * 16;                // packed query rows
-  static constexpr int kQBytes = kRows * kRow;
-  static constexpr int kQDma = kQBytes / 1024;
-  static constexpr size_t kRingBytes = static_cast<size_t>(kStages) * kWaves * kStage;
-  // The last stage of every wave is first written after the Q rows have
-  // been read into registers: it holds them (and the ranking scratch, at its
-  // end) before that.
-  static constexpr size_t kLastStage = static_cast<size_t>(kStages - 1) * kWaves * kStage;
+  static constexpr int kRows = NT * 16;                // packed query rows per head
+  static constexpr int kQBytes = HP * kRows * kRow;    // [head][row][kRow]
+  // Four row tiles: Q^T stays in LDS (in registers it would not leave room
+  // for the accumulators and the blocks in flight without spilling).
+  static constexpr bool kQInLds = NT == 4;
+  // Blocks in flight per wave (registers: 2 * kLoads uint4 each), the most
+  // that fit beside the accumulators without spilling.
+  static constexpr int kDepth = NT == 4 ? (D == 128 ? 1 : 2) : (HP == 2 && D == 128 ? 2 : 3);
   static constexpr int kQSteps = D / 32;               // QK MFMAs per row tile
   static constexpr int kDTiles = D / 16;               // O^T tiles per row tile
-  // Combine: each wave's O as fp32 rows padded by 16 bytes (so the 16 rows
-  // a lane group writes fall in different banks), then (max, sum) per row.
+  // LDS: [stage of wave 0 .. 3][Q rows (kQInLds)]; the combine reuses it:
+  // each wave's O as fp32 rows padded by 16 bytes (so the 16 rows a lane
+  // group writes fall in different banks), then (max, sum) per row; rows
+  // of head h of the item after those of head h - 1.
+  static constexpr size_t kQOff = static_cast<size_t>(kWaves) * kStage;
   static constexpr int kORow = D * 4 + 16;
+  static constexpr int kAllRows = HP * kRows;
   static constexpr size_t kCombine =
-      static_cast<size_t>(kWaves) * kRows * kORow + kWaves * kRows * 8;
+      static_cast<size_t>(kWaves) * kAllRows * kORow + kWaves * kAllRows * 8;
   static constexpr int kTpr = D / 8;                   // combine threads per row
   static constexpr int kRowsPerPass = kThreads / kTpr;
   // The next ticket, broadcast through LDS past the combine area (written
-  // and read only while no DMA is in flight).
+  // and read outside the loop).
   static constexpr size_t kTicket = kCombine;
-  static constexpr size_t kLds = kRingBytes > kCombine + 16 ? kRingBytes : kCombine + 16;
-  static_assert(kBlockBytes % 1024 == 0 && kQBytes % 1024 == 0, "DMA split");
-  static_assert(kStages >= 2 && (kStages - 1) * kLoadsPerStage <= 56, "vmcnt range");
-  static_assert(kStages <= 10, "wait_stages cases");
-  static_assert(kLds <= 160 * 1024 / kWgsPerCu, "LDS per CU");
-  static_assert(kStages * kWaves * kStage == 160 * 1024, "the whole LDS");
-  static_assert(kLastStage + kQBytes <= kRingBytes, "Q rows in the last stages");
+  static constexpr size_t kLoopLds = kQOff + (kQInLds ? kQBytes : 0);
+  static constexpr size_t kLds = kLoopLds > kCombine + 16 ? kLoopLds : kCombine + 16;
+  static_assert(kBlockBytes % 1024 == 0, "1 KiB per load instruction");
+  static_assert(kLds <= 160 * 1024, "LDS per CU");
+  static_assert(!kQInLds || HP == 1, "four row tiles take one head");
 };
 
-// 16-byte chunk swizzles (XOR on the chunk index, per row).  K and Q rows:
-// 16 lanes read one chunk of 16 consecutive rows; V rows: 16 lanes read two
-// adjacent chunks of 4 rows each (transpose reads), 64 lanes 16 rows.
-template <int D>
+// 16-byte chunk swizzles, XOR on the chunk index inside each 256-byte bank
+// period, per row of a K/V stage (kPiece bytes; chunk p = head * kChunks +
+// chunk).  K: 16 lanes read one chunk of 16 consecutive rows; V: 16 lanes
+// read two adjacent chunks of 4 rows each (transpose reads), 64 lanes 16
+// rows.  With rows of >= 256 bytes every row starts a bank period; with
+// 128-byte rows two rows share one.
+template <int kPiece>
 __device__ __forceinline__ int k_swz(int row) {
-  constexpr int kRowsPerBank = 256 / (D * 2);
-  return (row / kRowsPerBank) % (D / 8);
+  return kPiece >= 256 ? row % 16 : (row / 2) % (kPiece / 16);
 }
-template <int D>
+template <int kPiece>
 __device__ __forceinline__ int v_swz(int row) {
-  constexpr int kRowsPerBank = 256 / (D * 2);
-  return 2 * ((row / kRowsPerBank) % (D / 16));
+  return kPiece >= 256 ? 2 * (row % 8) : 2 * ((row / 2) % (kPiece / 32));
 }
 
 struct VerifyParams {
@@ -158,11 +161,13 @@ struct VerifyParams {
   int partition_tokens;      // keys per partition (a multiple of 64)
   int num_partitions;
   // Work items (partition * num_seqs + b), heaviest first, from the plan
-  // kernel.  Ticket t is item order[t / Hkv] for KV head t % Hkv; the
-  // workgroups draw tickets from `counter` (zeroed by the plan kernel).
+  // kernel.  With HP KV heads per ticket, ticket t is item order[t / (Hkv /
+  // HP)] for KV heads HP * (t % (Hkv / HP)) ..; the workgroups draw tickets
+  // from `counter` (zeroed by the plan kernel).
   const int32_t* order;
   int* counter;
   int num_tickets;
+  int heads_per_item;
   // Partials (num_partitions > 1): slot ((b * max_seqlen_q + i) * Hq + h) *
   // num_partitions + partition.
   float* ws_max;
@@ -195,12 +200,12 @@ __device__ __forceinline__ int item_weight(const VerifyParams& p, int item) {
   return w < kPlanBins ? w : kPlanBins - 1;
 }
 
-// One work ticket: (sequence, partition, KV head).  Returns the next
+// One work ticket: (sequence, partition, HP KV heads).  Returns the next
 // ticket, drawn while the combine runs (no DMA in flight then).
-template <int D, int G, int NT>
+template <int D, int G, int NT, int HP>
 __device__ __forceinline__ int verify_item(const VerifyParams& p, int ticket, char* smem) {
-  using S = VerifyShape<D, NT>;
-  // Stages, stage-major; reused by the final combine.
+  using S = VerifyShape<D, NT, HP>;
+  constexpr int kP = S::kPiece;
   const int tid = threadIdx.x;
   int* s_ticket = reinterpret_cast<int*>(smem + S::kTicket);
   auto next_ticket = [&]() __attribute__((always_inline)) {
@@ -208,11 +213,12 @@ __device__ __forceinline__ int verify_item(const VerifyParams& p, int ticket, ch
     __syncthreads();
     return *s_ticket;
   };
-  // The Hkv tickets of one item are consecutive: workgroups running at the
-  // same time read adjacent 256-byte pieces of the same cache rows.
-  const int kvh = ticket % p.num_kv_heads;
+  // The tickets of one item are consecutive: workgroups running at the same
+  // time read adjacent pieces of the same cache rows.
+  const int groups = p.num_kv_heads / HP;
+  const int kvh0 = (ticket % groups) * HP;
   const int n_items = p.num_seqs * p.num_partitions;
-  const int item = load_uniform_i32(p.order, ticket / p.num_kv_heads);
+  const int item = load_uniform_i32(p.order, ticket / groups);
   if (item < 0 || item >= n_items) return next_ticket();   // uniform
   const int part = item / p.num_seqs;
   const int b = item % p.num_seqs;
@@ -231,94 +237,95 @@ __device__ __forceinline__ int verify_item(const VerifyParams& p, int ticket, ch
   const int g = lane / 16;     // lane group: keys 4g .. 4g + 3 of S^T
   const int nbw = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
 
-  char* qlds = smem + S::kLastStage;
-  auto stage = [&](int slot) __attribute__((always_inline)) {
-    return smem + (slot * kWaves + wave) * S::kStage;
-  };
   const int64_t row_stride = static_cast<int64_t>(p.num_kv_heads) * S::kRow;
   const int64_t blk_bytes = row_stride * kBlock;
   const int32_t* btab = p.block_tables + static_cast<int64_t>(b) * p.max_blocks_per_seq;
   const int nblk_ctx = (lk + kBlock - 1) / kBlock;
 
-  // ---- DMA source offsets.  Load u of a block moves its rows r = (1024 u
-  // + 16 l) / kRow; lane l's 16 bytes land at byte 16 l of that KiB and hold
-  // chunk pos ^ swizzle(r) of row r.
-  uint32_t dma_k_off[S::kDmaPerBlock], dma_v_off[S::kDmaPerBlock];
+  // ---- load offsets.  Load u of a block brings rows r = (1024 u + 16 l)
+  // / kPiece of the block; lane l's 16 bytes go to slot pos of row r in the
+  // stage and are the piece's chunk pos ^ swizzle(r).
+  uint32_t k_src[S::kLoads], v_src[S::kLoads];
 #pragma unroll
-  for (int u = 0; u < S::kDmaPerBlock; ++u) {
+  for (int u = 0; u < S::kLoads; ++u) {
     const int byte = u * 1024 + lane * 16;
-    const int r = byte / S::kRow;
-    const int pos = (byte % S::kRow) / 16;
-    const int64_t base = r * row_stride + kvh * S::kRow;
-    dma_k_off[u] = static_cast<uint32_t>(base + (pos ^ k_swz<D>(r)) * 16);
-    dma_v_off[u] = static_cast<uint32_t>(base + (pos ^ v_swz<D>(r)) * 16);
+    const int r = byte / kP;
+    const int pos = (byte % kP) / 16;
+    const int64_t base = r * row_stride + kvh0 * S::kRow;
+    k_src[u] = static_cast<uint32_t>(base + (pos ^ k_swz<kP>(r)) * 16);
+    v_src[u] = static_cast<uint32_t>(base + (pos ^ v_swz<kP>(r)) * 16);
   }
   // Block ids are scalar loads (wave-uniform indices), clamped to the
   // context's blocks; an id outside the pool reads block 0 instead.
   auto block_id = [&](int jb) __attribute__((always_inline)) {
     return load_uniform_i32(btab, min(kb0 + wave + kWaves * jb, nblk_ctx - 1));
   };
-  auto dma_block = [&](int blk, int slot) __attribute__((always_inline)) {
+  constexpr int kL = S::kLoads;
+  uint4 rb[S::kDepth][2 * kL];   // blocks in flight: K loads, then V loads
+  auto load_block = [&](int blk, uint4 (&r)[2 * kL]) __attribute__((always_inline)) {
     blk = blk >= 0 && blk < p.num_blocks ? blk : 0;
     const int64_t off = static_cast<int64_t>(blk) * blk_bytes;
-    char* st = stage(slot);
+    const char* kb = p.k_cache + off;
+    const char* vb = p.v_cache + off;
 #pragma unroll
-    for (int u = 0; u < S::kDmaPerBlock; ++u) {
-      dma16(p.k_cache + off, dma_k_off[u], st + u * 1024);
-      dma16(p.v_cache + off, dma_v_off[u], st + S::kBlockBytes + u * 1024);
+    for (int u = 0; u < kL; ++u) {
+      r[u] = ld16_nt(kb + k_src[u]);
+      r[kL + u] = ld16_nt(vb + v_src[u]);
     }
   };
-  // Wait until at most `ahead` stages of this wave are still in flight.
-  auto wait_stages = [&](int ahead) __attribute__((always_inline)) {
-    constexpr int L = S::kLoadsPerStage;
-    switch (ahead) {
-      case 0: wait_vm<0>(); break;
-      case 1: wait_vm<L>(); break;
-      case 2: wait_vm<(S::kStages > 2 ? 2 * L : 0)>(); break;
-      case 3: wait_vm<(S::kStages > 3 ? 3 * L : 0)>(); break;
-      case 4: wait_vm<(S::kStages > 4 ? 4 * L : 0)>(); break;
-      case 5: wait_vm<(S::kStages > 5 ? 5 * L : 0)>(); break;
-      case 6: wait_vm<(S::kStages > 6 ? 6 * L : 0)>(); break;
-      case 7: wait_vm<(S::kStages > 7 ? 7 * L : 0)>(); break;
-      default: wait_vm<(S::kStages > 8 ? 8 * L : 0)>(); break;
+  char* st = smem + wave * S::kStage;   // this wave's stage
+  auto store_block = [&](const uint4 (&r)[2 * kL]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kL; ++u) {
+      *reinterpret_cast<uint4*>(st + u * 1024 + lane * 16) = r[u];
+      *reinterpret_cast<uint4*>(st + S::kBlockBytes + u * 1024 + lane * 16) = r[kL + u];
     }
   };
-
-  // ---- Q rows: the workgroup's DMA loads 1 KiB pieces of the packed rows
-  // (wave w takes pieces w, w + 4, ...) into the Q area; rows past G * Lq
-  // repeat row 0 (finite values, results never written).
+  // ---- prologue: blocks 0 .. kDepth - 1 in flight.
+#pragma unroll
+  for (int d = 0; d < S::kDepth; ++d)
+    if (d < nbw) load_block(block_id(d), rb[d]);
+  int next_id = nbw > S::kDepth ? block_id(S::kDepth) : 0;
+  // ---- Q^T, the B operand of S^T: lane (g, j) holds dimensions 32 s + 8 g
+  // .. + 7 of row 16 n + j of head hp; rows past G * Lq repeat row 0
+  // (finite values, results never written).  In registers, or (four row
+  // tiles) in LDS, where wave w writes row tile w.
+  uint4 qb[S::kQInLds ? 1 : HP][S::kQSteps][S::kQInLds ? 1 : NT];
+  char* qlds = smem + S::kQOff;
   {
     const char* qbase = p.q + static_cast<int64_t>(q0) * p.num_heads * S::kRow;
-    for (int u = wave; u < S::kQDma; u += kWaves) {
-      const int byte = u * 1024 + lane * 16;
-      const int m = byte / S::kRow;
-      const int pos = (byte % S::kRow) / 16;
+    auto q_row = [&](int hp, int m) __attribute__((always_inline)) {
       const int mm = m < G * lq ? m : 0;
-      const uint32_t off = static_cast<uint32_t>(
-          ((mm / G) * p.num_heads + kvh * G + mm % G) * S::kRow +
-          (pos ^ k_swz<D>(m)) * 16);
-      dma16(qbase, off, qlds + u * 1024);
+      return qbase + ((mm / G) * p.num_heads + (kvh0 + hp) * G + mm % G) * S::kRow;
+    };
+    if constexpr (S::kQInLds) {
+      const int m = wave * 16 + j;
+      const char* qrow = q_row(0, m);
+#pragma unroll
+      for (int s = 0; s < S::kQSteps; ++s)
+        *reinterpret_cast<uint4*>(qlds + m * S::kRow + ((4 * s + g) ^ k_swz<S::kRow>(m)) * 16) =
+            ld16(qrow + (32 * s + 8 * g) * 2);
+      __syncthreads();
+    } else {
+#pragma unroll
+      for (int hp = 0; hp < HP; ++hp)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const char* qrow = q_row(hp, n * 16 + j);
+#pragma unroll
+          for (int s = 0; s < S::kQSteps; ++s) qb[hp][s][n] = ld16(qrow + (32 * s + 8 * g) * 2);
+        }
     }
   }
-  // ---- ring prologue: stages 0 .. kStages - 2.
-  const int npro = min(S::kStages - 1, nbw);
-  for (int jb = 0; jb < npro; ++jb) dma_block(block_id(jb), jb);
-  int next_id = nbw > S::kStages - 1 ? block_id(S::kStages - 1) : 0;
-  // Q loads were issued before the prologue: they are done once only the
-  // prologue's loads remain.
-  wait_stages(npro);
-  lds_barrier();
-  uint4 qb[S::kQSteps][NT];
-#pragma unroll
-  for (int s = 0; s < S::kQSteps; ++s)
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
+  auto q_op = [&](int hp, int s, int n) __attribute__((always_inline)) {
+    if constexpr (S::kQInLds) {
       const int m = n * 16 + j;
-      qb[s][n] = *reinterpret_cast<const uint4*>(
-          qlds + m * S::kRow + ((4 * s + g) ^ k_swz<D>(m)) * 16);
+      return *reinterpret_cast<const uint4*>(qlds + m * S::kRow +
+                                             ((4 * s + g) ^ k_swz<S::kRow>(m)) * 16);
+    } else {
+      return qb[hp][s][n];
     }
-  // The loop's first DMA goes to the last stages, which hold the Q rows.
-  lds_barrier();
+  };
 
   // Row constants: the last key each of this lane's rows may see.
   int lim[NT];
@@ -329,29 +336,31 @@ __device__ __forceinline__ int verify_item(const VerifyParams& p, int ticket, ch
   }
   const int min_lim = p.causal ? lk - lq : lk - 1;   // over the real rows
 
-  // LDS read offsets inside a stage.  K (A of S^T): row j, chunk 4 s + g.
-  const int k_off = j * S::kRow;
-  const int k_x = k_swz<D>(j) * 16;
+  // LDS read offsets inside a stage.  K (A of S^T): row j, chunk hp *
+  // kChunks + 4 s + g.
+  const int k_off = j * kP;
+  const int k_x = k_swz<kP>(j) * 16;
   // V^T (A of O^T, transpose reads): lane (g, s') reads row 4 g + s' / 4,
-  // dimensions 16 dt + 4 (s' % 4) .. + 3; lane (g, i) receives V[4 g + e]
-  // [16 dt + i] for e = 0..3.
+  // dimensions 16 dt + 4 (s' % 4) .. + 3 of head hp; lane (g, i) receives
+  // V[4 g + e][16 dt + i] for e = 0..3.  The swizzle is even, so it keeps
+  // the chunk pair (2 dt, 2 dt + 1) together.
   const int v_row = 4 * g + j / 4;
-  const int v_off = S::kBlockBytes + v_row * S::kRow + ((j % 4) / 2) * 16 + (j % 2) * 8;
-  const int v_x = v_swz<D>(v_row) * 16;
+  const int v_off = S::kBlockBytes + v_row * kP + ((j % 4) / 2) * 16 + (j % 2) * 8;
+  const int v_x = v_swz<kP>(v_row) * 16;
 
-  f32x4_v oacc[S::kDTiles][NT];
+  f32x4_v oacc[HP][S::kDTiles][NT];
+  float run_max[HP][NT], run_sum[HP][NT];
 #pragma unroll
-  for (int dt = 0; dt < S::kDTiles; ++dt)
+  for (int hp = 0; hp < HP; ++hp)
 #pragma unroll
-    for (int n = 0; n < NT; ++n) oacc[dt][n] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-  float run_max[NT], run_sum[NT];
+    for (int n = 0; n < NT; ++n) {
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    run_max[n] = -INFINITY;   // reference max of the row (scaled, log2)
-    run_sum[n] = 0.f;         // this lane's share of the row sum
-  }
+      for (int dt = 0; dt < S::kDTiles; ++dt) oacc[hp][dt][n] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+      run_max[hp][n] = -INFINITY;   // reference max of the row (scaled, log2)
+      run_sum[hp][n] = 0.f;         // this lane's share of the row sum
+    }
 
-  auto compute = [&](int kb, char* st) __attribute__((always_inline)) {
+  auto compute = [&](int kb) __attribute__((always_inline)) {
     const int kbase = kb * kBlock;
     // V rows past Lk: zeros (this wave's own stage; LDS ops of one wave run
     // in order, so the transpose reads below see them).
@@ -359,137 +368,158 @@ __device__ __forceinline__ int verify_item(const VerifyParams& p, int ticket, ch
 #pragma unroll
       for (int u = 0; u < S::kBlockBytes / 16 / kWave; ++u) {
         const int c = u * kWave + lane;
-        if (kbase + c / S::kChunks >= lk)
+        if (kbase + c / (kP / 16) >= lk)
           *reinterpret_cast<uint4*>(st + S::kBlockBytes + c * 16) = make_uint4(0, 0, 0, 0);
       }
     }
-    // ---- S^T = K Q^T
-    f32x4_v sacc[NT];
+    const bool masked = kbase + kBlock - 1 > min_lim || kbase + kBlock > lk;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) sacc[n] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+    for (int hp = 0; hp < HP; ++hp) {
+      // ---- S^T = K Q^T
+      f32x4_v sacc[NT];
 #pragma unroll
-    for (int s = 0; s < S::kQSteps; ++s) {
-      const uint4 a = *reinterpret_cast<const uint4*>(st + k_off + (((4 * s + g) * 16) ^ k_x));
+      for (int n = 0; n < NT; ++n) sacc[n] = f32x4_v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int n = 0; n < NT; ++n) sacc[n] = mfma_qk(a, qb[s][n], sacc[n]);
-    }
-    // ---- mask: key 4 g + r of the block against each row's limit
-    if (kbase + kBlock - 1 > min_lim || kbase + kBlock > lk) {
+      for (int s = 0; s < S::kQSteps; ++s) {
+        const uint4 a = *reinterpret_cast<const uint4*>(
+            st + k_off + (((hp * S::kChunks + 4 * s + g) * 16) ^ k_x));
 #pragma unroll
-      for (int n = 0; n < NT; ++n)
+        for (int n = 0; n < NT; ++n) sacc[n] = mfma_qk(a, q_op(hp, s, n), sacc[n]);
+      }
+      // ---- mask: key 4 g + r of the block against each row's limit
+      if (masked) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          sacc[n][r] = kbase + 4 * g + r <= lim[n] ? sacc[n][r] : -INFINITY;
-    }
-    // ---- online softmax.  Fast path: weights against the reference max,
-    // summed over the bfloat16-rounded values the PV step uses; a lane
-    // share <= 2^13 means every weight is.  The exact path (max over the
-    // row's 16 keys, rescale of O) runs on a row's first visible block and
-    // where its max grows by more than 2^8.
-    uint2 pb[NT];
-    float psum[NT];
-    auto weights = [&](int n) __attribute__((always_inline)) {
-      const float neg = run_max[n] == -INFINITY ? 0.f : -run_max[n];
-      const float w0 = fast_exp2(fmaf(sacc[n][0], p.scale_log2, neg));
-      const float w1 = fast_exp2(fmaf(sacc[n][1], p.scale_log2, neg));
-      const float w2 = fast_exp2(fmaf(sacc[n][2], p.scale_log2, neg));
-      const float w3 = fast_exp2(fmaf(sacc[n][3], p.scale_log2, neg));
-      pb[n] = make_uint2(pack_bf16x2(w0, w1), pack_bf16x2(w2, w3));
-      psum[n] = dot2_bf16(pb[n].y, kBf16PairOne, dot2_bf16(pb[n].x, kBf16PairOne, 0.f));
-    };
-    bool exact = false;
+        for (int n = 0; n < NT; ++n)
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      weights(n);
-      exact = exact || run_max[n] == -INFINITY || !(psum[n] <= 8192.f);
-    }
-    if (__any(exact)) {
+          for (int r = 0; r < 4; ++r)
+            sacc[n][r] = kbase + 4 * g + r <= lim[n] ? sacc[n][r] : -INFINITY;
+      }
+      // ---- online softmax.  Fast path: weights against the reference
+      // max, summed over the bfloat16-rounded values the PV step uses; a
+      // lane share <= 2^13 means every weight is.  The exact path (max over
+      // the row's 16 keys, rescale of O) runs on a row's first visible
+      // block and where its max grows by more than 2^8.
+      uint2 pb[NT];
+      float psum[NT];
+      auto weights = [&](int n) __attribute__((always_inline)) {
+        const float neg = run_max[hp][n] == -INFINITY ? 0.f : -run_max[hp][n];
+        const float w0 = fast_exp2(fmaf(sacc[n][0], p.scale_log2, neg));
+        const float w1 = fast_exp2(fmaf(sacc[n][1], p.scale_log2, neg));
+        const float w2 = fast_exp2(fmaf(sacc[n][2], p.scale_log2, neg));
+        const float w3 = fast_exp2(fmaf(sacc[n][3], p.scale_log2, neg));
+        pb[n] = make_uint2(pack_bf16x2(w0, w1), pack_bf16x2(w2, w3));
+        psum[n] = dot2_bf16(pb[n].y, kBf16PairOne, dot2_bf16(pb[n].x, kBf16PairOne, 0.f));
+      };
+      bool exact = false;
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        float t = fmaxf(fmaxf(sacc[n][0], sacc[n][1]), fmaxf(sacc[n][2], sacc[n][3]));
-        t = fmaxf(t, __shfl_xor(t, 16, kWave));
-        t = fmaxf(t, swap_halves(t)) * p.scale_log2;
-        const bool grow = t > run_max[n] + 8.f;
-        if (__any(grow)) {
-          const float nm = grow ? t : run_max[n];
-          const float alpha = run_max[n] == -INFINITY ? 0.f : fast_exp2(run_max[n] - nm);
-          run_max[n] = nm;
-          run_sum[n] *= alpha;
+        weights(n);
+        exact = exact || run_max[hp][n] == -INFINITY || !(psum[n] <= 8192.f);
+      }
+      if (__any(exact)) {
 #pragma unroll
-          for (int dt = 0; dt < S::kDTiles; ++dt) oacc[dt][n] *= alpha;
-          weights(n);
+        for (int n = 0; n < NT; ++n) {
+          float t = fmaxf(fmaxf(sacc[n][0], sacc[n][1]), fmaxf(sacc[n][2], sacc[n][3]));
+          t = fmaxf(t, __shfl_xor(t, 16, kWave));
+          t = fmaxf(t, swap_halves(t)) * p.scale_log2;
+          const bool grow = t > run_max[hp][n] + 8.f;
+          if (__any(grow)) {
+            const float nm = grow ? t : run_max[hp][n];
+            const float alpha =
+                run_max[hp][n] == -INFINITY ? 0.f : fast_exp2(run_max[hp][n] - nm);
+            run_max[hp][n] = nm;
+            run_sum[hp][n] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < S::kDTiles; ++dt) oacc[hp][dt][n] *= alpha;
+            weights(n);
+          }
         }
       }
-    }
 #pragma unroll
-    for (int n = 0; n < NT; ++n) run_sum[n] += psum[n];
-    // ---- O^T += V^T P^T
+      for (int n = 0; n < NT; ++n) run_sum[hp][n] += psum[n];
+      // ---- O^T += V^T P^T
 #pragma unroll
-    for (int dt = 0; dt < S::kDTiles; ++dt) {
-      const uint2 a = lds_read_tr16(st + v_off + ((dt * 32) ^ v_x));
+      for (int dt = 0; dt < S::kDTiles; ++dt) {
+        const uint2 a =
+            lds_read_tr16(st + v_off + (((hp * S::kChunks + 2 * dt) * 16) ^ v_x));
 #pragma unroll
-      for (int n = 0; n < NT; ++n) oacc[dt][n] = mfma_pv(a, pb[n], oacc[dt][n]);
+        for (int n = 0; n < NT; ++n) oacc[hp][dt][n] = mfma_pv(a, pb[n], oacc[hp][dt][n]);
+      }
     }
   };
 
-  // ---- main loop: block jb of this wave lives in stage jb % kStages.
-  for (int jb = 0; jb < nbw; ++jb) {
-    wait_stages(min(S::kStages - 2, nbw - 1 - jb));
-    const int nj = jb + S::kStages - 1;
-    if (nj < nbw) {
-      // stage (jb - 1) % kStages: computed last iteration, its reads done
-      wait_lgkm();
-      dma_block(next_id, nj % S::kStages);
-      next_id = block_id(nj + 1);
+  // ---- main loop: block jb arrives in rb[jb % kDepth]; it goes to the
+  // wave's LDS stage, the block kDepth further on is loaded into the freed
+  // registers, and the stage is computed.  (LDS operations of one wave run
+  // in order: the stores of block jb + 1 follow the reads of block jb.)
+  for (int jb0 = 0; jb0 < nbw; jb0 += S::kDepth) {
+#pragma unroll
+    for (int d = 0; d < S::kDepth; ++d) {
+      const int jb = jb0 + d;
+      if (jb < nbw) {
+        store_block(rb[d]);
+        if (jb + S::kDepth < nbw) {
+          load_block(next_id, rb[d]);
+          next_id = block_id(jb + S::kDepth + 1);
+        }
+        // keep the loads here: the compiler may otherwise sink them to
+        // their use
+        __asm__ volatile("" ::: "memory");
+        compute(kb0 + wave + kWaves * jb);
+      }
     }
-    compute(kb0 + wave + kWaves * jb, stage(jb % S::kStages));
   }
 
   // ---- combine the four waves.  Every wave is past its loop (and so past
-  // its last LDS read of the rings and of Q) after this barrier.
-  float total[NT];
+  // its last LDS read of the stages and of Q) after this barrier.
+  float total[HP][NT];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    float t = run_sum[n] + __shfl_xor(run_sum[n], 16, kWave);
-    total[n] = t + swap_halves(t);
-  }
+  for (int hp = 0; hp < HP; ++hp)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      float t = run_sum[hp][n] + __shfl_xor(run_sum[hp][n], 16, kWave);
+      total[hp][n] = t + swap_halves(t);
+    }
   __syncthreads();
   int next = 0;
   if (tid == 0) next = atomicAdd(p.counter, 1);
+  float2* ml = reinterpret_cast<float2*>(smem + kWaves * S::kAllRows * S::kORow);
   {
-    char* ow = smem + static_cast<size_t>(wave) * S::kRows * S::kORow;
-    float2* ml = reinterpret_cast<float2*>(smem + kWaves * S::kRows * S::kORow);
+    char* ow = smem + static_cast<size_t>(wave) * S::kAllRows * S::kORow;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const int m = n * 16 + j;
+    for (int hp = 0; hp < HP; ++hp)
 #pragma unroll
-      for (int dt = 0; dt < S::kDTiles; ++dt)
-        *reinterpret_cast<float4*>(ow + m * S::kORow + (dt * 16 + 4 * g) * 4) =
-            make_float4(oacc[dt][n][0], oacc[dt][n][1], oacc[dt][n][2], oacc[dt][n][3]);
-      if (g == 0) ml[wave * S::kRows + m] = make_float2(run_max[n], total[n]);
-    }
+      for (int n = 0; n < NT; ++n) {
+        const int m = hp * S::kRows + n * 16 + j;
+#pragma unroll
+        for (int dt = 0; dt < S::kDTiles; ++dt)
+          *reinterpret_cast<float4*>(ow + m * S::kORow + (dt * 16 + 4 * g) * 4) =
+              make_float4(oacc[hp][dt][n][0], oacc[hp][dt][n][1], oacc[hp][dt][n][2],
+                          oacc[hp][dt][n][3]);
+        if (g == 0) ml[wave * S::kAllRows + m] = make_float2(run_max[hp][n], total[hp][n]);
+      }
   }
   __syncthreads();
-  const float2* ml = reinterpret_cast<const float2*>(smem + kWaves * S::kRows * S::kORow);
   const int c = tid % S::kTpr;   // dimensions 8 c .. 8 c + 7
 #pragma unroll
-  for (int m0 = 0; m0 < S::kRows; m0 += S::kRowsPerPass) {
-    const int m = m0 + tid / S::kTpr;
-    if (m >= S::kRows || m >= G * lq) continue;
+  for (int r0 = 0; r0 < S::kAllRows; r0 += S::kRowsPerPass) {
+    const int rr = r0 + tid / S::kTpr;   // head rr / kRows of the item, row rr % kRows
+    const int m = rr % S::kRows;
+    if (rr >= S::kAllRows || m >= G * lq) continue;
     float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, ml[w * S::kRows + m].x);
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, ml[w * S::kAllRows + rr].x);
     float l = 0.f, o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = 0.f;
     if (mx != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float2 st = ml[w * S::kRows + m];
+        const float2 st = ml[w * S::kAllRows + rr];
         const float a = fast_exp2(st.x - mx);   // 0 for a wave that saw nothing
         l = fmaf(a, st.y, l);
-        const char* src = smem + static_cast<size_t>(w) * S::kRows * S::kORow +
-                          m * S::kORow + c * 32;
+        const char* src = smem + static_cast<size_t>(w) * S::kAllRows * S::kORow +
+                          rr * S::kORow + c * 32;
         const float4 x = *reinterpret_cast<const float4*>(src);
         const float4 y = *reinterpret_cast<const float4*>(src + 16);
         o[0] = fmaf(a, x.x, o[0]); o[1] = fmaf(a, x.y, o[1]);
@@ -500,7 +530,7 @@ __device__ __forceinline__ int verify_item(const VerifyParams& p, int ticket, ch
     }
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int i = m / G;
-    const int head = kvh * G + m % G;
+    const int head = (kvh0 + rr / S::kRows) * G + m % G;
     if (p.num_partitions == 1) {
       uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) +
                        ((static_cast<int64_t>(q0) + i) * p.num_heads + head) * D + c * 8;
@@ -542,11 +572,10 @@ __device__ __forceinline__ int verify_item(const VerifyParams& p, int ticket, ch
 // until none are left: the XCDs of one chip do not stream at the same rate,
 // and a fixed share of the work per XCD (the dispatcher deals workgroups to
 // the XCDs round robin) would leave the fast ones idle at the end.
-template <int D, int G, int NT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
-    VerifyShape<D, NT>::kWgsPerCu, VerifyShape<D, NT>::kWgsPerCu))) void
+template <int D, int G, int NT, int HP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 verify_kernel(VerifyParams p) {
-  using S = VerifyShape<D, NT>;
+  using S = VerifyShape<D, NT, HP>;
   extern __shared__ __align__(16) char smem[];
   int* s_ticket = reinterpret_cast<int*>(smem + S::kTicket);
   if (threadIdx.x == 0) *s_ticket = atomicAdd(p.counter, 1);
@@ -554,7 +583,7 @@ verify_kernel(VerifyParams p) {
   int t = *s_ticket;
   while (t < p.num_tickets) {
     __syncthreads();   // every thread has read the ticket
-    t = verify_item<D, G, NT>(p, __builtin_amdgcn_readfirstlane(t), smem);
+    t = verify_item<D, G, NT, HP>(p, __builtin_amdgcn_readfirstlane(t), smem);
   }
 }
 
@@ -603,40 +632,25 @@ __global__ __launch_bounds__(kPlanThreads) void verify_plan_kernel(
       order, bins, wave_sum);
 }
 
-// Compute units of the current device (looked up once per device).
-int device_cus() {
-  static std::atomic<int> cus[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = cus[dev].load(std::memory_order_relaxed);
-  if (n <= 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cus[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
-template <int D, int G, int NT>
+template <int D, int G, int NT, int HP>
 hipError_t launch_nt(const VerifyParams& prm, const VerifyPlan& plan, hipStream_t s) {
-  using S = VerifyShape<D, NT>;
+  using S = VerifyShape<D, NT, HP>;
   static bool raised = false;   // once per kernel instantiation
   if (!raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&verify_kernel<D, G, NT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&verify_kernel<D, G, NT, HP>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(S::kLds));
     if (e != hipSuccess) return e;
     raised = true;
   }
   // As many workgroups as the chip holds at once (fewer for a small launch).
-  const int64_t slots = static_cast<int64_t>(device_cus()) * S::kWgsPerCu;
+  const int64_t slots = device_cus();
   const int64_t wgs = prm.num_tickets < slots ? prm.num_tickets : slots;
   hipLaunchKernelGGL(verify_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, prm,
                      const_cast<int32_t*>(prm.order));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((verify_kernel<D, G, NT>), dim3(static_cast<unsigned>(wgs)),
+  hipLaunchKernelGGL((verify_kernel<D, G, NT, HP>), dim3(static_cast<unsigned>(wgs)),
                      dim3(kThreads), S::kLds, s, prm);
   e = hipGetLastError();
   if (e != hipSuccess || plan.num_partitions == 1) return e;
@@ -650,9 +664,10 @@ hipError_t launch_nt(const VerifyParams& prm, const VerifyPlan& plan, hipStream_
 template <int D, int G>
 hipError_t launch_g(const VerifyParams& prm, const VerifyPlan& plan, hipStream_t s) {
   switch (plan.row_tiles) {
-    case 1: return launch_nt<D, G, 1>(prm, plan, s);
-    case 2: return launch_nt<D, G, 2>(prm, plan, s);
-    case 4: return launch_nt<D, G, 4>(prm, plan, s);
+    case 1: return plan.heads_per_item == 2 ? launch_nt<D, G, 1, 2>(prm, plan, s)
+                                            : launch_nt<D, G, 1, 1>(prm, plan, s);
+    case 2: return launch_nt<D, G, 2, 1>(prm, plan, s);
+    case 4: return launch_nt<D, G, 4, 1>(prm, plan, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -678,6 +693,21 @@ constexpr int kMinPartitionTokens = 256;
 
 }  // namespace
 
+int device_cus() {
+  constexpr int kMaxDeviceIds = 64;
+  static std::atomic<int> cus[kMaxDeviceIds];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDeviceIds) return 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 VerifyPlan plan_verify(int num_seqs, int num_heads, int num_kv_heads,
                        int head_dim, int max_seqlen_q, int max_seqlen_k) {
   VerifyPlan plan{};
@@ -690,7 +720,10 @@ VerifyPlan plan_verify(int num_seqs, int num_heads, int num_kv_heads,
     return plan;
   plan.use = true;
   plan.row_tiles = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
-  const int64_t groups = static_cast<int64_t>(num_seqs) * num_kv_heads;
+  // Two KV heads per work item (512-byte reads at D = 128) where the
+  // registers allow: one row tile.
+  plan.heads_per_item = (num_kv_heads % 2 == 0 && plan.row_tiles == 1) ? 2 : 1;
+  const int64_t groups = static_cast<int64_t>(num_seqs) * (num_kv_heads / plan.heads_per_item);
   int64_t parts = groups >= kTargetWorkgroups
                       ? 1
                       : (kTargetWorkgroups + groups - 1) / groups;
@@ -720,7 +753,7 @@ VerifyPlan plan_verify(int num_seqs, int num_heads, int num_kv_heads,
 hipError_t launch_verify(const PrefillArgs& a, const VerifyPlan& plan,
                          hipStream_t stream) {
   const int64_t wgs = static_cast<int64_t>(a.num_seqs) * plan.num_partitions *
-                      a.num_kv_heads;
+                      (a.num_kv_heads / plan.heads_per_item);
   const int64_t merges = static_cast<int64_t>(a.num_seqs) * a.max_seqlen_q * a.num_heads;
   if (wgs > 0x7fffffff || merges > 0x7fffffff) return hipErrorNotSupported;
   VerifyParams prm{};
@@ -752,6 +785,7 @@ hipError_t launch_verify(const PrefillArgs& a, const VerifyPlan& plan,
   prm.order = reinterpret_cast<const int32_t*>(ws + plan.off_order);
   prm.counter = reinterpret_cast<int*>(ws + plan.off_counter);
   prm.num_tickets = static_cast<int>(wgs);
+  prm.heads_per_item = plan.heads_per_item;
   const int g = a.num_heads / a.num_kv_heads;
   if (a.head_dim == 128) return launch_d<128>(prm, plan, g, stream);
   return launch_d<64>(prm, plan, g, stream);
