@@ -141,13 +141,14 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache,
                          void* stream);
 
 /*
- * Bytes of workspace pa_decode needs for these sizes (0 when one context
- * partition covers max_context_len and no merge pass is needed, and 0 for a
- * non-positive size, which pa_decode rejects).  The
- * workspace holds the partitions' partial results and, for large grids, a
- * longest-first work order that a one-workgroup plan kernel writes at the
- * start of each call (every call rewrites it, so calls that share a
- * workspace on one stream are safe).
+ * Bytes of workspace pa_decode needs for these sizes, either element type
+ * (the larger need of the two; 0 when one context partition covers
+ * max_context_len and no merge pass is needed, and 0 for a non-positive
+ * size, which pa_decode rejects).  The workspace holds the partitions'
+ * partial results and, for large grids, a longest-first work order (and a
+ * work counter) that a one-workgroup plan kernel writes at the start of
+ * each call (every call rewrites them, so calls that share a workspace on
+ * one stream are safe).
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads,
                                  int32_t num_kv_heads, int32_t head_dim,
@@ -166,7 +167,12 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads,
  * Split-context: the context is cut into fixed partitions processed in
  * parallel, each keeping its own running max and sum; a second pass merges
  * the partitions (the merge is skipped when one partition covers
- * max_context_len).
+ * max_context_len).  A large bf16 batch (one the decode kernel would split
+ * into partitions, with >= 1024 (sequence, KV-head-pair) work items) runs
+ * instead on the kernel of pa_prefill_varlen's small-row path (one query
+ * row per sequence, MFMA dot products, persistent workgroups, no
+ * partitions); all other calls run on the decode kernel (vector dot
+ * products).  Both compute the same softmax; results agree to rounding.
  *
  *   out, q         device, [num_seqs, num_heads, head_dim]
  *   k_cache,
@@ -206,10 +212,13 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache,
  * allocates nothing; on its first call on a device it looks up that
  * device's array address once (hipGetSymbolAddress).
  *
- * Limit: sizes for which pa_decode_workspace_bytes(num_seqs, num_heads,
- * num_kv_heads, head_dim, max_context_len) exceeds 33,554,432 return
- * PA_ERR_SCRATCH_LIMIT and launch nothing (256 sequences x 32 query heads
- * of head_dim 128 at max_context_len 8192 need about 17 MB).
+ * Limit: calls whose kernel needs more than 33,554,432 bytes of workspace
+ * return PA_ERR_SCRATCH_LIMIT and launch nothing.  For fp32 that need is
+ * pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+ * max_context_len) (256 sequences x 32 query heads of head_dim 128 at
+ * max_context_len 8192 need about 17 MB); a bf16 call that runs on the
+ * small-row kernel needs only its schedule (4 bytes per sequence), which
+ * the same query bounds.
  *
  * Every call on one GPU shares that GPU's array, which keeps the last
  * call's contents (nothing needs to start at zero: each call writes what

@@ -186,4 +186,10 @@ VerifyPlan plan_verify(int num_seqs, int num_heads, int num_kv_heads,
 hipError_t launch_verify(const PrefillArgs& a, const VerifyPlan& plan,
                          hipStream_t stream);
 
+// bfloat16 decode on the same kernel: one query row per sequence, keys
+// 0 .. context_lens[b] - 1.  The plan is plan_verify(num_seqs, num_heads,
+// num_kv_heads, head_dim, 1, max_context_len).
+hipError_t launch_verify_decode(const DecodeArgs& a, const VerifyPlan& plan,
+                                hipStream_t stream);
+
 }  // namespace pa

@@ -168,6 +168,9 @@ struct VerifyParams {
   int* counter;
   int num_tickets;
   int heads_per_item;
+  // Decode (one query row per sequence): row b of q, keys 0 .. L_b - 1 with
+  // L_b = context_lens[b]; cu_q / cu_k are not read then.
+  const int32_t* context_lens;
   // Partials (num_partitions > 1): slot ((b * max_seqlen_q + i) * Hq + h) *
   // num_partitions + partition.
   float* ws_max;
@@ -185,6 +188,12 @@ __device__ __forceinline__ int partition_blocks(const VerifyParams& p,
 }
 
 __device__ __forceinline__ SeqExtent verify_extent(const VerifyParams& p, int b) {
+  if (p.context_lens != nullptr) {
+    int lk = p.context_lens[b];
+    lk = lk < 0 ? 0 : (lk > p.max_seqlen_k ? p.max_seqlen_k : lk);
+    if (lk > p.max_blocks_per_seq * kBlock) lk = p.max_blocks_per_seq * kBlock;
+    return {b, 1, lk};
+  }
   return seq_extent(p.cu_q, p.cu_k, b, p.max_seqlen_q, p.max_seqlen_k, p.total_q,
                     p.max_blocks_per_seq);
 }
@@ -750,12 +759,57 @@ VerifyPlan plan_verify(int num_seqs, int num_heads, int num_kv_heads,
   return plan;
 }
 
+namespace {
+
+hipError_t launch_plan(VerifyParams& prm, const VerifyPlan& plan, void* workspace,
+                       int head_dim, hipStream_t stream) {
+  const int64_t tickets = static_cast<int64_t>(prm.num_seqs) * plan.num_partitions *
+                          (prm.num_kv_heads / plan.heads_per_item);
+  const int64_t merges = static_cast<int64_t>(prm.num_seqs) * prm.max_seqlen_q * prm.num_heads;
+  if (tickets > 0x7fffffff || merges > 0x7fffffff) return hipErrorNotSupported;
+  prm.partition_tokens = plan.partition_tokens;
+  prm.num_partitions = plan.num_partitions;
+  char* ws = static_cast<char*>(workspace);
+  if (plan.num_partitions > 1) {
+    prm.ws_max = reinterpret_cast<float*>(ws + plan.off_max);
+    prm.ws_sum = reinterpret_cast<float*>(ws + plan.off_sum);
+    prm.ws_acc_h = reinterpret_cast<uint16_t*>(ws + plan.off_acc);
+  }
+  prm.order = reinterpret_cast<const int32_t*>(ws + plan.off_order);
+  prm.counter = reinterpret_cast<int*>(ws + plan.off_counter);
+  prm.num_tickets = static_cast<int>(tickets);
+  prm.heads_per_item = plan.heads_per_item;
+  const int g = prm.num_heads / prm.num_kv_heads;
+  if (head_dim == 128) return launch_d<128>(prm, plan, g, stream);
+  return launch_d<64>(prm, plan, g, stream);
+}
+
+}  // namespace
+
+hipError_t launch_verify_decode(const DecodeArgs& a, const VerifyPlan& plan,
+                                hipStream_t stream) {
+  VerifyParams prm{};
+  prm.out = a.out;
+  prm.q = static_cast<const char*>(a.q);
+  prm.total_q = a.num_seqs;
+  prm.k_cache = static_cast<const char*>(a.k_cache);
+  prm.v_cache = static_cast<const char*>(a.v_cache);
+  prm.num_blocks = a.num_blocks;
+  prm.context_lens = a.context_lens;
+  prm.max_seqlen_q = 1;
+  prm.max_seqlen_k = a.max_context_len;
+  prm.block_tables = a.block_tables;
+  prm.max_blocks_per_seq = a.max_blocks_per_seq;
+  prm.num_seqs = a.num_seqs;
+  prm.num_heads = a.num_heads;
+  prm.num_kv_heads = a.num_kv_heads;
+  prm.scale_log2 = a.scale * kLog2e;
+  prm.causal = 1;
+  return launch_plan(prm, plan, a.workspace, a.head_dim, stream);
+}
+
 hipError_t launch_verify(const PrefillArgs& a, const VerifyPlan& plan,
                          hipStream_t stream) {
-  const int64_t wgs = static_cast<int64_t>(a.num_seqs) * plan.num_partitions *
-                      (a.num_kv_heads / plan.heads_per_item);
-  const int64_t merges = static_cast<int64_t>(a.num_seqs) * a.max_seqlen_q * a.num_heads;
-  if (wgs > 0x7fffffff || merges > 0x7fffffff) return hipErrorNotSupported;
   VerifyParams prm{};
   prm.out = a.out;
   prm.q = static_cast<const char*>(a.q);
@@ -774,21 +828,7 @@ hipError_t launch_verify(const PrefillArgs& a, const VerifyPlan& plan,
   prm.num_kv_heads = a.num_kv_heads;
   prm.scale_log2 = a.scale * kLog2e;
   prm.causal = a.causal ? 1 : 0;
-  prm.partition_tokens = plan.partition_tokens;
-  prm.num_partitions = plan.num_partitions;
-  char* ws = static_cast<char*>(a.workspace);
-  if (plan.num_partitions > 1) {
-    prm.ws_max = reinterpret_cast<float*>(ws + plan.off_max);
-    prm.ws_sum = reinterpret_cast<float*>(ws + plan.off_sum);
-    prm.ws_acc_h = reinterpret_cast<uint16_t*>(ws + plan.off_acc);
-  }
-  prm.order = reinterpret_cast<const int32_t*>(ws + plan.off_order);
-  prm.counter = reinterpret_cast<int*>(ws + plan.off_counter);
-  prm.num_tickets = static_cast<int>(wgs);
-  prm.heads_per_item = plan.heads_per_item;
-  const int g = a.num_heads / a.num_kv_heads;
-  if (a.head_dim == 128) return launch_d<128>(prm, plan, g, stream);
-  return launch_d<64>(prm, plan, g, stream);
+  return launch_plan(prm, plan, a.workspace, a.head_dim, stream);
 }
 
 }  // namespace pa

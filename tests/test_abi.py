@@ -103,20 +103,25 @@ def _decode_noalloc(lib, **kw):
     (dict(out=None), 1), (dict(cl=None), 1), (dict(bt=None), 1),
     (dict(q=MISALIGNED), 3),
     (dict(b=0), 0),                                # empty batch: no-op
-    # 64 sequences x 64 query heads over 2^20-token contexts: ~272 MB of
-    # partials, past the 32 MiB static scratch -> rejected, nothing launched
-    (dict(b=64, hq=64, hkv=8, d=128, maxlen=1 << 20, dtype=_lib.PA_BF16), 6),
+    # 64 sequences x 64 query heads over 2^20-token contexts, fp32: ~272 MB
+    # of partials, past the 32 MiB static scratch -> rejected, nothing
+    # launched
+    (dict(b=64, hq=64, hkv=8, d=128, maxlen=1 << 20, dtype=_lib.PA_F32), 6),
 ])
 def test_decode_noalloc_validation(kw, code, no_device):
     assert _decode_noalloc(_lib.load(), **kw) == code
 
 
 def test_decode_noalloc_limit_matches_workspace_query():
-    """The static scratch is 32 MiB: sizes whose pa_decode workspace fits
-    are the ones pa_decode_noalloc accepts."""
+    """The static scratch is 32 MiB.  The workspace query covers either
+    element type (the larger need): sizes whose query fits are accepted
+    for both; past it, fp32 is rejected while bfloat16, whose split-context
+    partials are binary16 rows of the small-row kernel, may still fit."""
     lib = _lib.load()
     big = lib.pa_decode_workspace_bytes(64, 64, 8, 128, 1 << 20)
     assert big > 32 << 20
+    assert _decode_noalloc(lib, b=64, hq=64, hkv=8, d=128, maxlen=1 << 20,
+                           dtype=_lib.PA_F32) == 6
     fits = lib.pa_decode_workspace_bytes(256, 32, 8, 128, 8192)
     assert 0 < fits <= 32 << 20
 

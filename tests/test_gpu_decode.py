@@ -211,3 +211,23 @@ def test_large_values_split_context():
     assert big > 65504, "the case must exceed the binary16 range"
     err = float(np.max(np.abs(got - want)))
     assert err <= big * 2.0 ** -7, (err, big)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (16, 8, 64), (12, 3, 128),
+                                      (64, 8, 128)])
+def test_large_bf16_batch(hq, hkv, d):
+    """bf16 batches large enough that the small-row attention kernel covers
+    every context without partitions (>= 1024 (sequence, KV head pair)
+    work items) run on it, one query row per sequence: two KV heads per
+    item where Hkv is even, one where it is odd (Hkv = 3).  Contexts from 1
+    token to 3,000 with block and partition edges; 24 sequences checked."""
+    say("decode large bf16 batch", hq, hkv, d)
+    per_seq = hkv // 2 if hkv % 2 == 0 else hkv
+    n = -(-1024 // per_seq) + 3
+    rng = np.random.default_rng(hq * 100 + hkv + d)
+    lens = rng.integers(1, 3000, n, endpoint=True)
+    lens[:9] = [1, 15, 16, 17, 511, 512, 513, 1024, 3000]
+    lay = wl.decode_layout(lens.tolist(), 16, seed=hq + d)
+    case = DecodeCase(lay, hq, hkv, d, "bf16", seed=hkv + d)
+    seqs = sorted(set(range(9)) | set(sample_seqs(lens, 15, seed=d)))
+    _check(case, seqs=seqs)

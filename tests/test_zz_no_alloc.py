@@ -72,7 +72,9 @@ def test_noalloc_matches_decode_two_calls():
 
 def test_noalloc_single_partition_and_limit():
     """Contexts that fit one partition need no scratch; sizes past the
-    static scratch are refused with PA_ERR_SCRATCH_LIMIT before launch."""
+    static scratch (fp32: 64 sequences x 64 query heads over 2^20-token
+    contexts, ~272 MB of partials) are refused with PA_ERR_SCRATCH_LIMIT
+    before launch."""
     say("noalloc single partition")
     c = DecodeCase(wl.decode_layout([7, 16, 33, 100], 16, seed=77), 8, 2, 64,
                    "f32", seed=78)
@@ -81,8 +83,8 @@ def test_noalloc_single_partition_and_limit():
     assert bits_equal(wl.host_bits(ref), wl.host_bits(na))
     from paged_kv_cache_slot_amd import _lib
     with pytest.raises(_lib.PaError, match="SCRATCH_LIMIT"):
-        q = torch.zeros((64, 64, 128), dtype=torch.bfloat16, device="cuda")
-        kc = torch.zeros((1, 16, 8, 128), dtype=torch.bfloat16, device="cuda")
+        q = torch.zeros((64, 64, 128), dtype=torch.float32, device="cuda")
+        kc = torch.zeros((1, 16, 8, 128), dtype=torch.float32, device="cuda")
         bt = torch.zeros((64, 1), dtype=torch.int32, device="cuda")
         cl = torch.zeros(64, dtype=torch.int32, device="cuda")
         ops.decode_noalloc(q, kc, kc, bt, cl, 1 << 20)
