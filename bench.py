@@ -13,8 +13,9 @@ rows over 0..8192 cached tokens, and pa_decode of 192 rows; it is reported in
 Prints one JSON line.  ``value`` is the step's algorithmic HBM throughput in
 TB/s (KV bytes the decode must read + q/out/block ids + the store's bytes,
 over the step time); ``tokens_per_s`` is sequences decoded per second for
-this one layer.  ``roofline`` covers pa_decode (partition + merge kernels)
-timed with HIP events on its stream inside the timed region;
+this one layer.  ``roofline`` covers pa_decode (for this batch: the plan
+kernel and the persistent small-row attention kernel, one query row per
+sequence) timed with HIP events on its stream inside the timed region;
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
 sequences on the host cores.
 
@@ -143,8 +144,11 @@ def committed_traffic(summary, sources):
     return None
 
 
-DECODE_SOURCES = ("decode.hip", "pa_device.h", "pa_internal.h")
-PREFILL_SOURCES = ("prefill.hip", "pa_device.h", "pa_internal.h")
+# The 8B-shaped decode runs on the small-row attention kernel (api.cpp
+# routes large bf16 batches there).
+DECODE_SOURCES = ("verify.hip", "pa_tile.h", "pa_device.h", "pa_internal.h",
+                  "api.cpp")
+PREFILL_SOURCES = ("prefill.hip", "pa_tile.h", "pa_device.h", "pa_internal.h")
 
 
 def decode_bytes(lens, hq, hkv, d, elem, bs=16):
@@ -1130,8 +1134,9 @@ def main():
         "step_ms_stats": step_stats,
         "decode_ms_stats": dec_stats,
         "flush_mb_between_steps": args.flush_mb,
-        "roofline": {"kernel": "pa_decode (decode_partition_kernel + "
-                               "decode_merge_kernel)",
+        "roofline": {"kernel": "pa_decode (large bf16 batch: verify_plan_kernel "
+                               "+ verify_kernel, one query row per sequence, "
+                               "two KV heads per work item)",
                      "bound": "hbm", "achieved": round(dec_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
