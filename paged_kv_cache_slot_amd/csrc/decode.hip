@@ -224,6 +224,10 @@ struct DecodeParams {
   int prefix_chunk_tokens;
   int prefix_chunks;     // prefix slots per (sequence, head)
   int force_partials;    // write partials even with one partition
+  // Shared-prefix decode whose suffixes fit one partition: the partition
+  // kernel merges the prefix partials (complete before it starts) with its
+  // own result and writes the output; no suffix partial, no merge kernel.
+  int merge_prefix;
   float v_scale;         // output factor (E4M3 cache: V = code * v_scale)
   // Longest-first schedule (null: natural order): entry r is the (part *
   // num_seqs + b) item workgroups r * Hkv .. r * Hkv + Hkv - 1 take.
@@ -237,6 +241,13 @@ __device__ __forceinline__ int suffix_start(const DecodeParams& p, int b,
   int st = p.prefix_lens[b];
   st = st < 0 ? 0 : (st > len ? len : st);
   return st - st % kBlock;
+}
+
+// Prefix partials of a sequence whose partitions start at `start`.
+__device__ __forceinline__ int prefix_partials(const DecodeParams& p, int start) {
+  if (start <= 0 || p.prefix_chunks <= 0) return 0;
+  const int n = (start + p.prefix_chunk_tokens - 1) / p.prefix_chunk_tokens;
+  return n > p.prefix_chunks ? p.prefix_chunks : n;
 }
 
 __device__ __forceinline__ int clamp_len(const DecodeParams& p, int b) {
@@ -279,6 +290,39 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16(uint32_t w) {
 __device__ __forceinline__ uint4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
   return make_uint4(e4m3x2_to_bf16<false>(lo), e4m3x2_to_bf16<true>(lo),
                     e4m3x2_to_bf16<false>(hi), e4m3x2_to_bf16<true>(hi));
+}
+
+// Merged output of one (sequence, query head) at dimension d: weights
+// 2^(m_p - m*) rescale each partial's sum and output; the result is their
+// ratio.  Slots 0 .. np - 1 hold this call's partitions, slots
+// num_partitions .. num_partitions + npre - 1 the prefix partials; (m0,
+// l0, o0) is a partial already in registers (empty by default).
+template <typename T, int D>
+__device__ __forceinline__ float merge_head(const DecodeParams& p, int64_t head,
+                                            int d, int np, int npre,
+                                            float m0 = -INFINITY, float l0 = 0.f,
+                                            float o0 = 0.f) {
+  const float* mx = p.ws_max + head * p.ws_stride;
+  const float* sm = p.ws_sum + head * p.ws_stride;
+  const float* ac = p.ws_acc + head * p.ws_stride * D + d;
+  const uint16_t* ach = p.ws_acc_h + head * p.ws_stride * D + d;
+  auto slot = [&](int i) { return i < np ? i : p.num_partitions + (i - np); };
+  // Partial k as (sum l, unnormalised output l * o): fp32 acc for fp32 I/O,
+  // binary16 o (scaled by 2^-16 where l is stored negated) for bfloat16.
+  return merge_partials<8>(np + npre, [&](int i, float& m, float& l, float& acc)
+                                          __attribute__((always_inline)) {
+    const int k = slot(i);
+    m = mx[k];
+    const float lraw = sm[k];
+    if constexpr (sizeof(T) == 2) {
+      const float o = f16_to_f32(ach[static_cast<int64_t>(k) * D]);
+      l = fabsf(lraw);
+      acc = l * (lraw < 0.f ? o * kPartialGrow : o);
+    } else {
+      l = lraw;
+      acc = ac[static_cast<int64_t>(k) * D];
+    }
+  }, m0, l0, o0);
 }
 
 template <typename T, int D, int G, int C, bool F8>
@@ -326,12 +370,16 @@ decode_partition_kernel(
 
   if (t0 >= len) {
     // Nothing to attend.  A single-partition launch owns the output row and
-    // writes zeros for an empty context (batch padding); otherwise the merge
+    // writes zeros for an empty context (batch padding); with the prefix
+    // merge the output is the prefix partials' alone; otherwise the merge
     // pass never reads this partition.
-    if (single && part == 0) {
-      T* out = reinterpret_cast<T*>(p.out) +
-               (static_cast<int64_t>(b) * p.num_heads + head0) * D;
-      for (int i = tid; i < G * D; i += kThreads) store_out<T>(out + i, 0.f);
+    if (part == 0 && (single || p.merge_prefix)) {
+      const int npre = single ? 0 : prefix_partials(p, t0);
+      for (int i = tid; i < G * D; i += kThreads) {
+        const int64_t head = static_cast<int64_t>(b) * p.num_heads + head0 + i / D;
+        const float o = npre > 0 ? merge_head<T, D>(p, head, i % D, 0, npre) : 0.f;
+        store_out<T>(reinterpret_cast<T*>(p.out) + head * D + i % D, o * p.v_scale);
+      }
     }
     return;
   }
@@ -739,6 +787,17 @@ decode_partition_kernel(
         store_out<T>(out + e * kWave + lane, l > 0.f ? ov[e] / l * p.v_scale : 0.f);
       continue;
     }
+    if (p.merge_prefix) {
+      // This partition (the whole suffix) joins the prefix partials.
+      const int npre = prefix_partials(p, t0);
+      T* out = reinterpret_cast<T*>(p.out) + head * D;
+#pragma unroll
+      for (int e = 0; e < D / kWave; ++e)
+        store_out<T>(out + e * kWave + lane,
+                     merge_head<T, D>(p, head, e * kWave + lane, 0, npre, s_mrun[h], l,
+                                      ov[e]) * p.v_scale);
+      continue;
+    }
     const int64_t slot = head * p.ws_stride + part;
     if constexpr (sizeof(T) == 2) {
       // Normalised binary16 partial (see kPartialBig).
@@ -767,8 +826,8 @@ decode_partition_kernel(
   }
 }
 
-// Merge the partitions of one (sequence, query head): weights 2^(m_p - m*)
-// rescale each partition's sum and output; the result is their ratio.
+// Merge pass: one workgroup per (query head, sequence), one thread per
+// dimension.
 template <typename T, int D>
 __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
   const int partition_tokens = p.partition_tokens;
@@ -779,40 +838,9 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
   const int start = suffix_start(p, b, len);
   int np = (len - start + partition_tokens - 1) / partition_tokens;
   np = np > p.num_partitions ? p.num_partitions : np;   // bound violated
-  int npre = 0;                      // prefix partials of this sequence
-  if (start > 0 && p.prefix_chunks > 0) {
-    npre = (start + p.prefix_chunk_tokens - 1) / p.prefix_chunk_tokens;
-    npre = npre > p.prefix_chunks ? p.prefix_chunks : npre;
-  }
   const int64_t head = static_cast<int64_t>(b) * p.num_heads + h;
   T* out = reinterpret_cast<T*>(p.out) + head * D + d;
-  const float* mx = p.ws_max + head * p.ws_stride;
-  const float* sm = p.ws_sum + head * p.ws_stride;
-  const float* ac = p.ws_acc + head * p.ws_stride * D + d;
-  const uint16_t* ach = p.ws_acc_h + head * p.ws_stride * D + d;
-  // Partial k as (sum l, unnormalised output l * o): fp32 acc for fp32 I/O,
-  // binary16 o (scaled by 2^-16 where l is stored negated) for bfloat16.
-  auto load_partial = [&](int k, float& l, float& acc) __attribute__((always_inline)) {
-    const float lraw = sm[k];
-    if constexpr (sizeof(T) == 2) {
-      const float o = f16_to_f32(ach[static_cast<int64_t>(k) * D]);
-      l = fabsf(lraw);
-      acc = l * (lraw < 0.f ? o * kPartialGrow : o);
-    } else {
-      l = lraw;
-      acc = ac[static_cast<int64_t>(k) * D];
-    }
-  };
-  // Slots 0 .. np - 1 (this call's partitions), then num_partitions ..
-  // num_partitions + npre - 1 (the prefix partials).
-  auto slot = [&](int i) { return i < np ? i : p.num_partitions + (i - np); };
-  const float o = merge_partials<8>(np + npre, [&](int i, float& m, float& l, float& acc)
-                                                   __attribute__((always_inline)) {
-    const int k = slot(i);
-    m = mx[k];
-    load_partial(k, l, acc);
-  });
-  store_out<T>(out, o * p.v_scale);
+  store_out<T>(out, merge_head<T, D>(p, head, d, np, prefix_partials(p, start)) * p.v_scale);
 }
 
 // Longest-first schedule of the (sequence, partition) items: one workgroup
@@ -862,7 +890,9 @@ hipError_t launch_typed(const DecodeParams& prm, int num_seqs, int num_kv_heads,
   hipLaunchKernelGGL((decode_partition_kernel<T, D, G, C, F8>), grid,
                      dim3(kThreads), 0, stream, prm);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || (prm.num_partitions == 1 && !prm.force_partials)) return e;
+  if (e != hipSuccess || (prm.num_partitions == 1 && !prm.force_partials) ||
+      prm.merge_prefix)
+    return e;
   hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(num_heads, num_seqs),
                      dim3(D), 0, stream, prm);
   return hipGetLastError();
@@ -1093,6 +1123,7 @@ hipError_t launch_decode_suffix(const DecodeArgs& a, const SharedPrefixPlan& pla
   prm.prefix_chunk_tokens = plan.prefix_chunk_tokens;
   prm.prefix_chunks = plan.prefix_chunks;
   prm.force_partials = 1;
+  prm.merge_prefix = plan.suffix.num_partitions == 1 ? 1 : 0;
   char* ws = static_cast<char*>(a.workspace);
   prm.ws_max = reinterpret_cast<float*>(ws + plan.off_max);
   prm.ws_sum = reinterpret_cast<float*>(ws + plan.off_sum);

@@ -137,20 +137,24 @@ __device__ __forceinline__ uint16_t partial_f16(float o, bool big) {
 // output a_k; the result is sum_k 2^(m_k - m) a_k / sum_k 2^(m_k - m) l_k
 // with m the largest m_k, or 0 when no partial saw a key.  load(k, m, l, a)
 // fetches partial k.  The loads of a group of kGroup partials are issued
-// together (one memory round trip per group); the group's max then becomes
-// the reference, rescaling what earlier groups summed.  With n <= kGroup
-// this is the plain two-pass merge: max over all, then weighted sums.
+// together (one memory round trip per group): slots past n load partial
+// n - 1 again, unconditionally, and are then masked out.  The group's max
+// becomes the reference, rescaling what earlier groups summed.  With
+// n <= kGroup this is the plain two-pass merge: max over all, then
+// weighted sums.  (m, l, o) may start as a partial already in registers.
 template <int kGroup, typename LoadFn>
-__device__ __forceinline__ float merge_partials(int n, LoadFn load) {
-  float m = -INFINITY, l = 0.f, o = 0.f;
+__device__ __forceinline__ float merge_partials(int n, LoadFn load,
+                                                float m = -INFINITY,
+                                                float l = 0.f, float o = 0.f) {
   for (int i0 = 0; i0 < n; i0 += kGroup) {
     float mv[kGroup], sv[kGroup], av[kGroup];
 #pragma unroll
     for (int u = 0; u < kGroup; ++u) {
-      mv[u] = -INFINITY;
-      sv[u] = 0.f;
-      av[u] = 0.f;
-      if (i0 + u < n) load(i0 + u, mv[u], sv[u], av[u]);
+      const bool in = i0 + u < n;
+      load(in ? i0 + u : n - 1, mv[u], sv[u], av[u]);
+      mv[u] = in ? mv[u] : -INFINITY;
+      sv[u] = in ? sv[u] : 0.f;
+      av[u] = in ? av[u] : 0.f;
     }
     float gm = m;
 #pragma unroll

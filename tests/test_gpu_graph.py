@@ -73,3 +73,51 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert bits_equal(got_d, wl.host_bits(dout)), f"decode, replay {r}"
         assert bits_equal(got_p, wl.host_bits(pout)), f"prefill, replay {r}"
+
+
+def test_graph_shared_prefix():
+    """The shared-prefix decode (prefix pass on MFMA, then the suffix
+    partitions, which merge the prefix partials) captured in a graph:
+    replays must equal eager calls bit for bit."""
+    from paged_kv_cache_slot_amd import metadata as pm
+    from tests.gpu_harness import dev_i32
+    from tests.test_gpu_shared_prefix import _grouped_layout
+    say("graph capture: shared-prefix decode")
+    rng = np.random.default_rng(97)
+    spec = [(40, (640 + rng.integers(1, 300, 12)).tolist()), (0, [90, 700]),
+            (9, (144 + rng.integers(1, 80, 5)).tolist())]
+    case = DecodeCase(_grouped_layout(spec, 98), 32, 8, 128, "bf16", seed=99)
+    sp = pm.shared_prefix_inputs(case.tables, case.lens, case.bs)
+    assert sp["groups"].shape[0] == 2
+    pl, gr = dev_i32(sp["prefix_lens"]), dev_i32(sp["groups"].reshape(-1, 2))
+    ws = torch.empty(max(ops.shared_prefix_workspace_bytes(
+        len(case.lens), 32, 8, 128, sp["max_suffix_len"], sp["max_prefix_len"],
+        sp["groups"].shape[0], sp["max_group_size"]), 1),
+        dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(case.q)
+
+    def calls():
+        case.run_store()
+        ops.decode_shared_prefix(case.q, case.kc, case.vc, case.block_tables,
+                                 case.context_lens, pl, gr, sp["max_suffix_len"],
+                                 sp["max_prefix_len"], sp["max_group_size"],
+                                 scale=case.scale, out=out, workspace=ws)
+
+    calls()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    torch.cuda.synchronize()
+    for r in range(3):
+        case.q.copy_(wl.make_values(tuple(case.q.shape), "bf16", 400 + r, "cuda"))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = wl.host_bits(out).copy()
+        assert np.isfinite(out.float().cpu().numpy()).all(), f"replay {r}"
+        out.fill_(float("nan"))
+        calls()
+        torch.cuda.synchronize()
+        assert bits_equal(got, wl.host_bits(out)), f"replay {r}"

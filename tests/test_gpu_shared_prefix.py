@@ -89,6 +89,18 @@ def test_long_prefix_many_chunks():
     assert sp["max_prefix_len"] == 960
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_long_suffixes_merge_pass(dtype):
+    """Suffixes longer than one 512-token partition: the suffix partials
+    and the prefix partials meet in the merge pass (short suffixes merge
+    the prefix partials inside the partition kernel instead)."""
+    say("shared prefix long suffixes", dtype)
+    spec = [(20, [1000, 2100, 340, 800]), (0, [1500]), (6, [97, 700])]
+    case = DecodeCase(_grouped_layout(spec, 79), 32, 8, 128, dtype, seed=80)
+    sp = _run(case, expect_groups=[(0, 4), (5, 2)])
+    assert sp["max_suffix_len"] > 512
+
+
 def test_empty_suffix_member():
     """A member whose whole context is the shared prefix (its new token is
     the last slot of the last shared block): its suffix is empty and only
