@@ -232,6 +232,9 @@ struct DecodeParams {
   // Longest-first schedule (null: natural order): entry r is the (part *
   // num_seqs + b) item workgroups r * Hkv .. r * Hkv + Hkv - 1 take.
   const int32_t* order;
+  // Longest-first without a plan kernel (plain decode, at most 64
+  // sequences): each wave ranks its item itself (ranked_item).
+  int inline_rank;
 };
 
 // First token of the partitions: 0, or the block-aligned shared prefix.
@@ -256,6 +259,50 @@ __device__ __forceinline__ int clamp_len(const DecodeParams& p, int b) {
   len = len > p.max_context_len ? p.max_context_len : len;
   const int cap = p.max_blocks_per_seq * kBlock;
   return len > cap ? cap : len;
+}
+
+// The item of rank r in a longest-first order of the (sequence, partition)
+// items, found by one wave from the context lengths of at most 64
+// sequences (lane b holds sequence b's), with the length of the item's
+// sequence; item -1 past the last non-empty one.  Full partitions come
+// first (sequence-major), then each sequence's last, partial one by
+// decreasing length (ties by sequence), then the empty ones.  Every lane of
+// the wave must call it; the result is wave-uniform.
+struct RankedItem {
+  int item, len;
+};
+__device__ __forceinline__ RankedItem ranked_item(const DecodeParams& p, int r) {
+  const int lane = __lane_id();
+  const int pt = p.partition_tokens;
+  const int len = lane < p.num_seqs ? clamp_len(p, lane) : 0;
+  const int full = min(len / pt, p.num_partitions);
+  int incl = full;                                   // inclusive scan of `full`
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += y;
+  }
+  const int num_full = __shfl(incl, kWave - 1, kWave);
+  if (r < num_full) {
+    const uint64_t m = __ballot(incl > r && incl - full <= r);
+    const int b = __ffsll(static_cast<unsigned long long>(m)) - 1;
+    const int part = r - __builtin_amdgcn_readlane(incl - full, b);
+    return {part * p.num_seqs + b, __builtin_amdgcn_readlane(len, b)};
+  }
+  // A partial last partition has len % pt tokens (len <= num_partitions * pt).
+  const int w = (lane < p.num_seqs && len % pt != 0) ? len % pt : -1;
+  if (r - num_full >= __popcll(__ballot(w >= 0))) return {-1, 0};   // empty
+  int rank = 0;
+#pragma unroll 1
+  for (int k = 0; k < kWave; ++k) {                  // uniform
+    const int wk = __builtin_amdgcn_readlane(w, k);
+    rank += (wk > w || (wk == w && k < lane)) ? 1 : 0;
+  }
+  const uint64_t m = __ballot(w >= 0 && rank == r - num_full);
+  if (m == 0) return {-1, 0};
+  const int b = __ffsll(static_cast<unsigned long long>(m)) - 1;
+  const int lb = __builtin_amdgcn_readlane(len, b);
+  return {(lb / pt) * p.num_seqs + b, lb};
 }
 
 // A bounds-checked view of one cache block: a buffer resource whose size is
@@ -351,7 +398,13 @@ decode_partition_kernel(
   // are dispatched before the sparse late ones.
   const int kvh = blockIdx.x % p.num_kv_heads;
   int rest = blockIdx.x / p.num_kv_heads;
-  if (p.order != nullptr) {
+  int ranked_len = -1;
+  if (p.inline_rank) {
+    const RankedItem it = ranked_item(p, rest);
+    if (it.item < 0) return;                                          // uniform
+    rest = __builtin_amdgcn_readfirstlane(it.item);
+    ranked_len = __builtin_amdgcn_readfirstlane(it.len);
+  } else if (p.order != nullptr) {
     rest = load_uniform_i32(p.order, rest);
     if (rest < 0 || rest >= p.num_seqs * p.num_partitions) return;   // uniform
   }
@@ -362,7 +415,7 @@ decode_partition_kernel(
   const int lane = tid % kWave;
   const bool single = p.num_partitions == 1 && !p.force_partials;
 
-  const int len = clamp_len(p, b);
+  const int len = ranked_len >= 0 ? ranked_len : clamp_len(p, b);
   const int t0 = suffix_start(p, b, len) + part * p.partition_tokens;
   const int head0 = kvh * G;
   const int row_stride = p.num_kv_heads * S::kCacheRow;   // bytes per slot
@@ -826,6 +879,73 @@ decode_partition_kernel(
   }
 }
 
+// The same for plain decode with at most 8 partitions: every slot's loads
+// are issued together with the context length's, not after it.  Slots past
+// the sequence's partitions hold stale values from other calls; they are
+// dropped by index (selects, never arithmetic on them).
+template <typename T, int D>
+__device__ __forceinline__ float merge_head_all(const DecodeParams& p, int64_t head,
+                                                int d, int b) {
+  constexpr int kMax = 8;
+  const float* mx = p.ws_max + head * p.ws_stride;
+  const float* sm = p.ws_sum + head * p.ws_stride;
+  // All loads first, in one round trip: the outputs per slot (clamped to
+  // the partitions), then maxima and sums as 8 contiguous slots (two wide
+  // scalar loads; past this head's partitions they are the next head's
+  // slots, or the next workspace array after the last head -- inside the
+  // workspace), then the context length.
+  uint16_t oh[kMax];
+  float of[kMax];
+#pragma unroll
+  for (int u = 0; u < kMax; ++u) {
+    const int k = u < p.num_partitions ? u : p.num_partitions - 1;
+    if constexpr (sizeof(T) == 2)
+      oh[u] = p.ws_acc_h[(head * p.ws_stride + k) * D + d];
+    else
+      of[u] = p.ws_acc[(head * p.ws_stride + k) * D + d];
+  }
+  // Read as vector loads (an opaque per-lane zero offset): all of them are
+  // counted by vmcnt and issue together with the outputs'.
+  int z = 0;
+  __asm__ volatile("" : "+v"(z));
+  float mv[kMax], lr[kMax];
+#pragma unroll
+  for (int u = 0; u < kMax; ++u) {
+    mv[u] = mx[u + z];
+    lr[u] = sm[u + z];
+  }
+  const int len = clamp_len(p, b);
+  // Scheduling fence: every load above issues before the arithmetic below.
+  __builtin_amdgcn_sched_barrier(0);
+  float lv[kMax], av[kMax];
+#pragma unroll
+  for (int u = 0; u < kMax; ++u) {
+    if constexpr (sizeof(T) == 2) {
+      const float o = f16_to_f32(oh[u]);
+      lv[u] = fabsf(lr[u]);
+      av[u] = lv[u] * (lr[u] < 0.f ? o * kPartialGrow : o);
+    } else {
+      lv[u] = lr[u];
+      av[u] = of[u];
+    }
+  }
+  int np = (len + p.partition_tokens - 1) / p.partition_tokens;
+  np = np > p.num_partitions ? p.num_partitions : np;
+  float gm = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kMax; ++u) gm = fmaxf(gm, u < np ? mv[u] : -INFINITY);
+  if (gm == -INFINITY) return 0.f;
+  float l = 0.f, o = 0.f;
+#pragma unroll
+  for (int u = 0; u < kMax; ++u) {
+    const bool in = u < np;
+    const float w = in ? fast_exp2(mv[u] - gm) : 0.f;
+    l = fmaf(w, in ? lv[u] : 0.f, l);
+    o = fmaf(w, in ? av[u] : 0.f, o);
+  }
+  return l > 0.f ? o / l : 0.f;
+}
+
 // Merge pass: one workgroup per (query head, sequence), one thread per
 // dimension.
 template <typename T, int D>
@@ -834,6 +954,12 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int d = threadIdx.x;
+  if (p.prefix_lens == nullptr && p.num_partitions <= 8) {
+    const int64_t head = static_cast<int64_t>(b) * p.num_heads + h;
+    store_out<T>(reinterpret_cast<T*>(p.out) + head * D + d,
+                 merge_head_all<T, D>(p, head, d, b) * p.v_scale);
+    return;
+  }
   const int len = clamp_len(p, b);
   const int start = suffix_start(p, b, len);
   int np = (len - start + partition_tokens - 1) / partition_tokens;
@@ -928,6 +1054,7 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 // workgroups.  Appends the order array to a multi-partition plan's
 // workspace; returns whether the plan uses one.
 constexpr int64_t kOrderMinWorkgroups = 4096;
+constexpr int kInlineRankSeqs = kWave;
 bool plan_order(DecodePlan& plan, int num_seqs, int num_kv_heads) {
   const int64_t wgs = static_cast<int64_t>(num_seqs) * num_kv_heads * plan.num_partitions;
   plan.use_order = plan.num_partitions > 1 && wgs >= kOrderMinWorkgroups;
@@ -983,7 +1110,13 @@ DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads,
   plan.off_acc = plan.off_sum + align256(slots * sizeof(float));
   plan.workspace_bytes =
       plan.off_acc + align256(slots * static_cast<size_t>(head_dim) * sizeof(float));
-  plan_order(plan, num_seqs, num_kv_heads);
+  // Up to 64 sequences each wave ranks its own item (no plan kernel, no
+  // order array; it costs a workgroup the one load its context length
+  // costs anyway); larger batches get the plan kernel.
+  if (num_seqs <= kInlineRankSeqs)
+    plan.inline_rank = true;
+  else
+    plan_order(plan, num_seqs, num_kv_heads);
   return plan;
 }
 
@@ -1019,6 +1152,7 @@ SharedPrefixPlan plan_shared_prefix(int num_seqs, int num_heads,
       plan.off_acc + align256(slots * static_cast<size_t>(head_dim) * sizeof(float));
   plan.suffix.off_order = 0;
   plan.suffix.use_order = false;
+  plan.suffix.inline_rank = false;   // the items start at the shared prefix
   if (plan_order(plan.suffix, num_seqs, num_kv_heads)) {
     plan.suffix.off_order = plan.workspace_bytes;
     plan.workspace_bytes += align256(static_cast<size_t>(num_seqs) *
@@ -1054,6 +1188,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan,
     prm.ws_acc = reinterpret_cast<float*>(ws + plan.off_acc);
     prm.ws_acc_h = reinterpret_cast<uint16_t*>(ws + plan.off_acc);
     if (plan.use_order) prm.order = reinterpret_cast<int32_t*>(ws + plan.off_order);
+    prm.inline_rank = plan.inline_rank ? 1 : 0;
   }
   return dispatch_decode(prm, a, stream);
 }

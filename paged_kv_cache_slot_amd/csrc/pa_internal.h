@@ -41,6 +41,7 @@ struct DecodePlan {
   size_t off_max, off_sum, off_acc;  // byte offsets inside the workspace
   bool use_order;        // longest-first schedule of (sequence, partition)
   size_t off_order;      // its int32 [num_seqs * num_partitions] array
+  bool inline_rank;      // longest first, each workgroup ranking its own item
 };
 
 DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads,

@@ -141,7 +141,7 @@ def _plan_partitions(lib, b, hq, hkv, d, maxlen):
         a = lambda x: (x + 255) // 256 * 256
         slots = b * hq * np_
         n = 2 * a(slots * 4) + a(slots * d * 4)
-        if np_ > 1 and b * hkv * np_ >= 4096:   # longest-first schedule
+        if np_ > 1 and b * hkv * np_ >= 4096 and b > 64:   # plan's order
             n += a(b * np_ * 4)
         return n
     return [n for n in range(1, maxlen // 512 + 2) if size(n) == ws]
@@ -231,3 +231,45 @@ def test_large_bf16_batch(hq, hkv, d):
     case = DecodeCase(lay, hq, hkv, d, "bf16", seed=hkv + d)
     seqs = sorted(set(range(9)) | set(sample_seqs(lens, 15, seed=d)))
     _check(case, seqs=seqs)
+
+
+@pytest.mark.parametrize("dtype,b,hq,hkv,d,longest", [
+    ("bf16", 64, 16, 8, 128, 4096),    # exactly 64 sequences, 8 partitions
+    ("f32", 40, 32, 8, 64, 8192),      # 40 + 3 padding rows, 16 partitions
+])
+def test_self_ranked_schedule(dtype, b, hq, hkv, d, longest):
+    """Up to 64 sequences, each wave of the partition kernel finds its own
+    (sequence, partition) item in the longest-first order (no plan kernel):
+    full partitions, then partial ones by length (ties among equal
+    lengths), then empty ones.  The workspace starts as all-ones bytes, so
+    a partition no workgroup computed would merge as NaN; every row is
+    checked, twice in a row on the same workspace."""
+    from paged_kv_cache_slot_amd import _lib, ops
+    lib = _lib.load()
+    rows = b + (3 if b < 64 else 0)
+    np_ = -(-longest // 512)
+    assert _plan_partitions(lib, rows, hq, hkv, d, longest) == [np_], \
+        "the plan no longer takes 512-token partitions here"
+    say("decode self-ranked schedule", dtype, b)
+    rng = np.random.default_rng(b + hq)
+    lens = rng.integers(1, longest, b, endpoint=True)
+    lens[:12] = [longest, 1, 511, 512, 513, 1024, 700, 700, 700, 1536, 2048,
+                 longest - 1]
+    lay = wl.decode_layout(lens.tolist(), 16, seed=b + d)
+    case = DecodeCase(lay, hq, hkv, d, dtype, seed=b + hkv,
+                      extra_pad=rows - b)
+    case.run_store()
+    ws = torch.full((ops.decode_workspace_bytes(rows, hq, hkv, d,
+                                                case.max_context_len),),
+                    255, dtype=torch.uint8, device="cuda")
+    first = case.run_decode(workspace=ws)
+    second = case.run_decode(workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(first, second)
+    ek, ev = case.oracle_store()
+    want = case.oracle_decode(ek, ev)
+    got = f64(second)
+    assert np.all(np.isfinite(got))
+    assert np.all(got[b:] == 0.0)
+    err = np.max(np.abs(got - want))
+    assert err <= TOL[dtype], f"max abs err {err}"
