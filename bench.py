@@ -418,8 +418,8 @@ def run_prefix(steps, warmup, dev, flush, cpu_s=0.0, check=True):
         "kernel": "pa_decode (every sequence reads its whole context)",
         "shared_prefix": {
             "kernel": "pa_decode_shared_prefix (shared blocks read once per "
-                      "group: prefix partials on MFMA + suffix partitions + "
-                      "merge)",
+                      "group: prefix partials on MFMA, then the suffix "
+                      "partitions, which merge them)",
             "groups": ng,
             "decode_us": round(shared * 1e3, 2),
             "unique_tbs": round(unique / (shared * 1e-3) / 1e12, 4),
@@ -639,7 +639,8 @@ def run_small(steps, warmup, dev, flush, cpu_s=0.0, check=True):
         "decode_tbs": round(dbytes / (dec * 1e-3) / 1e12, 4),
         "frac_of_hbm_peak": round(dbytes / (dec * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(b / (dec * 1e-3), 1),
-        "kernel": "pa_decode (plan + decode_partition_kernel + decode_merge_kernel)",
+        "kernel": "pa_decode (decode_partition_kernel, items ranked by the "
+                  "workgroups, + decode_merge_kernel)",
     }
 
 

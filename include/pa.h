@@ -145,10 +145,11 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache,
  * (the larger need of the two; 0 when one context partition covers
  * max_context_len and no merge pass is needed, and 0 for a non-positive
  * size, which pa_decode rejects).  The workspace holds the partitions'
- * partial results and, for large grids, a longest-first work order (and a
- * work counter) that a one-workgroup plan kernel writes at the start of
- * each call (every call rewrites them, so calls that share a workspace on
- * one stream are safe).
+ * partial results and, for large grids of more than 64 sequences, a
+ * longest-first work order (and a work counter) that a one-workgroup plan
+ * kernel writes at the start of each call (every call rewrites them, so
+ * calls that share a workspace on one stream are safe).  Up to 64
+ * sequences the workgroups find their place in that order themselves.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads,
                                  int32_t num_kv_heads, int32_t head_dim,
