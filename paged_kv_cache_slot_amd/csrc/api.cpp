@@ -457,11 +457,10 @@ pa_status pa_decode_fp8(void* out, const void* q, const void* k_cache,
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) ||
       !aligned16(v_cache))
     return PA_ERR_UNSUPPORTED;
-  // The E4M3 cache is read by the decode kernel.
-  const pa::DecodePlan plan = pa::plan_decode(num_seqs, num_heads, num_kv_heads,
-                                              head_dim, max_context_len);
-  if (plan.workspace_bytes > 0 &&
-      (!workspace || workspace_bytes < plan.workspace_bytes))
+  // Same route as a bfloat16 cache: large batches on the small-row kernel.
+  const DecodeRoute route = route_decode(num_seqs, num_heads, num_kv_heads,
+                                         head_dim, max_context_len, true);
+  if (route.bytes > 0 && (!workspace || workspace_bytes < route.bytes))
     return PA_ERR_WORKSPACE;
   pa::DecodeArgs a{};
   a.out = out;
@@ -483,7 +482,9 @@ pa_status pa_decode_fp8(void* out, const void* q, const void* k_cache,
   a.fp8_cache = true;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
-  hipError_t e = pa::launch_decode(a, plan, static_cast<hipStream_t>(stream));
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = route.use_rows ? pa::launch_verify_decode(a, route.rows, hs)
+                                : pa::launch_decode(a, route.decode, hs);
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -327,18 +327,6 @@ __device__ __forceinline__ uint2 buf_ld8_nt(__amdgpu_buffer_rsrc_t r,
   return make_uint2(v[0], v[1]);
 }
 
-// Eight E4M3 codes (bytes of lo, then hi) -> eight bfloat16 (exact; E4M3
-// values are a subset of bfloat16's).
-template <bool kHigh>
-__device__ __forceinline__ uint32_t e4m3x2_to_bf16(uint32_t w) {
-  return __builtin_bit_cast(uint32_t,
-                            __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHigh));
-}
-__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
-  return make_uint4(e4m3x2_to_bf16<false>(lo), e4m3x2_to_bf16<true>(lo),
-                    e4m3x2_to_bf16<false>(hi), e4m3x2_to_bf16<true>(hi));
-}
-
 // Merged output of one (sequence, query head) at dimension d: weights
 // 2^(m_p - m*) rescale each partial's sum and output; the result is their
 // ratio.  Slots 0 .. np - 1 hold this call's partitions, slots

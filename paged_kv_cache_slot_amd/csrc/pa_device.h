@@ -178,6 +178,19 @@ __device__ __forceinline__ float merge_partials(int n, LoadFn load,
   return (m == -INFINITY || !(l > 0.f)) ? 0.f : o / l;
 }
 
+// Two E4M3 codes (bytes 0-1, or 2-3 with kHigh, of w) -> two bfloat16, and
+// eight codes (bytes of lo, then hi) -> eight bfloat16 (exact; E4M3 values
+// are a subset of bfloat16's).
+template <bool kHigh>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHigh));
+}
+__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  return make_uint4(e4m3x2_to_bf16<false>(lo), e4m3x2_to_bf16<true>(lo),
+                    e4m3x2_to_bf16<false>(hi), e4m3x2_to_bf16<true>(hi));
+}
+
 // 16-byte global load / store.
 __device__ __forceinline__ uint4 ld16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);

@@ -85,14 +85,16 @@ __device__ __forceinline__ f32x4_v mfma_pv(uint2 a, uint2 b, f32x4_v c) {
 }
 
 // HP KV heads per work item: their rows are adjacent in every cache row, so
-// one item reads HP * 2D contiguous bytes per token.
-template <int D, int NT, int HP>
+// one item reads HP * 2D contiguous bytes per token (HP * D with an 8-bit
+// E4M3 cache, F8, whose codes are widened to bfloat16 on the way to LDS).
+template <int D, int NT, int HP, bool F8 = false>
 struct VerifyShape {
-  static constexpr int kRow = D * 2;                   // bytes of one head's row
+  static constexpr int kRow = D * 2;                   // bytes of one head's row in LDS
   static constexpr int kChunks = kRow / 16;            // 16-byte chunks per head row
-  static constexpr int kPiece = HP * kRow;             // bytes per token read
-  static constexpr int kBlockBytes = kBlock * kPiece;  // one block of the HP heads
-  static constexpr int kLoads = kBlockBytes / 1024;    // 16-byte loads per lane, K or V
+  static constexpr int kPiece = HP * kRow;             // LDS bytes per token
+  static constexpr int kSrcPiece = F8 ? HP * D : kPiece;   // cache bytes per token
+  static constexpr int kBlockBytes = kBlock * kPiece;  // one block of the HP heads in LDS
+  static constexpr int kLoads = kBlock * kSrcPiece / 1024;   // 16-byte loads per lane, K or V
   static constexpr int kStage = 2 * kBlockBytes;       // K block, then V block
   static constexpr int kRows = NT * 16;                // packed query rows per head
   static constexpr int kQBytes = HP * kRows * kRow;    // [head][row][kRow]
@@ -100,8 +102,12 @@ struct VerifyShape {
   // for the accumulators and the blocks in flight without spilling).
   static constexpr bool kQInLds = NT == 4;
   // Blocks in flight per wave (registers: 2 * kLoads uint4 each), the most
-  // that fit beside the accumulators without spilling.
-  static constexpr int kDepth = NT == 4 ? (D == 128 ? 1 : 2) : (HP == 2 && D == 128 ? 2 : 3);
+  // that fit beside the accumulators without spilling.  E4M3 blocks take
+  // half the registers but keep the same depth: deeper (twice as many
+  // blocks) measured slower, the register pressure serialising the LDS
+  // reads.
+  static constexpr int kDepth =
+      NT == 4 ? (D == 128 ? 1 : 2) : (HP == 2 && D == 128 ? 2 : 3);
   static constexpr int kQSteps = D / 32;               // QK MFMAs per row tile
   static constexpr int kDTiles = D / 16;               // O^T tiles per row tile
   // LDS: [stage of wave 0 .. 3][Q rows (kQInLds)]; the combine reuses it:
@@ -120,7 +126,7 @@ struct VerifyShape {
   static constexpr size_t kTicket = kCombine;
   static constexpr size_t kLoopLds = kQOff + (kQInLds ? kQBytes : 0);
   static constexpr size_t kLds = kLoopLds > kCombine + 16 ? kLoopLds : kCombine + 16;
-  static_assert(kBlockBytes % 1024 == 0, "1 KiB per load instruction");
+  static_assert(kBlock * kSrcPiece % 1024 == 0, "1 KiB per load instruction");
   static_assert(kLds <= 160 * 1024, "LDS per CU");
   static_assert(!kQInLds || HP == 1, "four row tiles take one head");
 };
@@ -176,6 +182,7 @@ struct VerifyParams {
   float* ws_max;
   float* ws_sum;             // negative: the partial is stored scaled
   uint16_t* ws_acc_h;        // binary16 acc / sum, D per slot
+  float v_scale;             // output factor (E4M3 cache: V = code * v_scale)
 };
 
 // Keys of sequence extent e that partition `part` reads: [key0, key1).  The
@@ -211,9 +218,9 @@ __device__ __forceinline__ int item_weight(const VerifyParams& p, int item) {
 
 // One work ticket: (sequence, partition, HP KV heads).  Returns the next
 // ticket, drawn while the combine runs (no DMA in flight then).
-template <int D, int G, int NT, int HP>
+template <int D, int G, int NT, int HP, bool F8>
 __device__ __forceinline__ int verify_item(const VerifyParams& p, int ticket, char* smem) {
-  using S = VerifyShape<D, NT, HP>;
+  using S = VerifyShape<D, NT, HP, F8>;
   constexpr int kP = S::kPiece;
   const int tid = threadIdx.x;
   int* s_ticket = reinterpret_cast<int*>(smem + S::kTicket);
@@ -246,28 +253,40 @@ __device__ __forceinline__ int verify_item(const VerifyParams& p, int ticket, ch
   const int g = lane / 16;     // lane group: keys 4g .. 4g + 3 of S^T
   const int nbw = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
 
-  const int64_t row_stride = static_cast<int64_t>(p.num_kv_heads) * S::kRow;
+  constexpr int kSrc = S::kSrcPiece;
+  const int64_t row_stride = static_cast<int64_t>(p.num_kv_heads) * (kSrc / HP);
   const int64_t blk_bytes = row_stride * kBlock;
   const int32_t* btab = p.block_tables + static_cast<int64_t>(b) * p.max_blocks_per_seq;
   const int nblk_ctx = (lk + kBlock - 1) / kBlock;
 
   // ---- load offsets.  Load u of a block brings rows r = (1024 u + 16 l)
-  // / kPiece of the block; lane l's 16 bytes go to slot pos of row r in the
-  // stage and are the piece's chunk pos ^ swizzle(r).
+  // / kSrc of the block.  bfloat16: lane l's 16 bytes go to slot pos of row
+  // r in the stage and are the piece's chunk pos ^ swizzle(r).  E4M3: lane
+  // l's 16 codes are chunk pos of the code row; widened they are bfloat16
+  // chunks 2 pos and 2 pos + 1, which go to slots (2 pos) ^ swizzle(r) and
+  // (2 pos + 1) ^ swizzle(r) (the swizzles keep a chunk pair together in one
+  // 256-byte bank period).
   uint32_t k_src[S::kLoads], v_src[S::kLoads];
 #pragma unroll
   for (int u = 0; u < S::kLoads; ++u) {
     const int byte = u * 1024 + lane * 16;
-    const int r = byte / kP;
-    const int pos = (byte % kP) / 16;
-    const int64_t base = r * row_stride + kvh0 * S::kRow;
-    k_src[u] = static_cast<uint32_t>(base + (pos ^ k_swz<kP>(r)) * 16);
-    v_src[u] = static_cast<uint32_t>(base + (pos ^ v_swz<kP>(r)) * 16);
+    const int r = byte / kSrc;
+    const int pos = (byte % kSrc) / 16;
+    const int64_t base = r * row_stride + kvh0 * (kSrc / HP);
+    if constexpr (F8) {
+      k_src[u] = static_cast<uint32_t>(base + pos * 16);
+      v_src[u] = k_src[u];
+    } else {
+      k_src[u] = static_cast<uint32_t>(base + (pos ^ k_swz<kP>(r)) * 16);
+      v_src[u] = static_cast<uint32_t>(base + (pos ^ v_swz<kP>(r)) * 16);
+    }
   }
   // Block ids are scalar loads (wave-uniform indices), clamped to the
-  // context's blocks; an id outside the pool reads block 0 instead.
+  // partition's last block (past the wave's last block the loads repeat it:
+  // a cache hit); an id outside the pool reads block 0 instead.
+  const int kb_last = kb0 + nblk - 1;
   auto block_id = [&](int jb) __attribute__((always_inline)) {
-    return load_uniform_i32(btab, min(kb0 + wave + kWaves * jb, nblk_ctx - 1));
+    return load_uniform_i32(btab, min(kb0 + wave + kWaves * jb, kb_last));
   };
   constexpr int kL = S::kLoads;
   uint4 rb[S::kDepth][2 * kL];   // blocks in flight: K loads, then V loads
@@ -286,45 +305,86 @@ __device__ __forceinline__ int verify_item(const VerifyParams& p, int ticket, ch
   auto store_block = [&](const uint4 (&r)[2 * kL]) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kL; ++u) {
-      *reinterpret_cast<uint4*>(st + u * 1024 + lane * 16) = r[u];
-      *reinterpret_cast<uint4*>(st + S::kBlockBytes + u * 1024 + lane * 16) = r[kL + u];
+      if constexpr (F8) {
+        const int byte = u * 1024 + lane * 16;
+        const int row = byte / kSrc;
+        const int pos = (byte % kSrc) / 16;
+        char* kr = st + row * kP;
+        char* vr = st + S::kBlockBytes + row * kP;
+        const int kx = k_swz<kP>(row), vx = v_swz<kP>(row);
+        *reinterpret_cast<uint4*>(kr + ((2 * pos) ^ kx) * 16) = e4m3x8_to_bf16(r[u].x, r[u].y);
+        *reinterpret_cast<uint4*>(kr + ((2 * pos + 1) ^ kx) * 16) = e4m3x8_to_bf16(r[u].z, r[u].w);
+        *reinterpret_cast<uint4*>(vr + ((2 * pos) ^ vx) * 16) =
+            e4m3x8_to_bf16(r[kL + u].x, r[kL + u].y);
+        *reinterpret_cast<uint4*>(vr + ((2 * pos + 1) ^ vx) * 16) =
+            e4m3x8_to_bf16(r[kL + u].z, r[kL + u].w);
+      } else {
+        *reinterpret_cast<uint4*>(st + u * 1024 + lane * 16) = r[u];
+        *reinterpret_cast<uint4*>(st + S::kBlockBytes + u * 1024 + lane * 16) = r[kL + u];
+      }
     }
   };
-  // ---- prologue: blocks 0 .. kDepth - 1 in flight.
-#pragma unroll
-  for (int d = 0; d < S::kDepth; ++d)
-    if (d < nbw) load_block(block_id(d), rb[d]);
-  int next_id = nbw > S::kDepth ? block_id(S::kDepth) : 0;
   // ---- Q^T, the B operand of S^T: lane (g, j) holds dimensions 32 s + 8 g
   // .. + 7 of row 16 n + j of head hp; rows past G * Lq repeat row 0
   // (finite values, results never written).  In registers, or (four row
-  // tiles) in LDS, where wave w writes row tile w.
+  // tiles) in LDS, where wave w writes row tile w.  Its loads go out ahead
+  // of the first K/V blocks.
   uint4 qb[S::kQInLds ? 1 : HP][S::kQSteps][S::kQInLds ? 1 : NT];
   char* qlds = smem + S::kQOff;
-  {
-    const char* qbase = p.q + static_cast<int64_t>(q0) * p.num_heads * S::kRow;
-    auto q_row = [&](int hp, int m) __attribute__((always_inline)) {
-      const int mm = m < G * lq ? m : 0;
-      return qbase + ((mm / G) * p.num_heads + (kvh0 + hp) * G + mm % G) * S::kRow;
-    };
-    if constexpr (S::kQInLds) {
-      const int m = wave * 16 + j;
-      const char* qrow = q_row(0, m);
+  const char* qbase = p.q + static_cast<int64_t>(q0) * p.num_heads * S::kRow;
+  auto q_row = [&](int hp, int m) __attribute__((always_inline)) {
+    const int mm = m < G * lq ? m : 0;
+    return qbase + ((mm / G) * p.num_heads + (kvh0 + hp) * G + mm % G) * S::kRow;
+  };
+  if constexpr (S::kQInLds) {
+    const char* qrow = q_row(0, wave * 16 + j);
+#pragma unroll
+    for (int s = 0; s < S::kQSteps; ++s) qb[0][s][0] = ld16(qrow + (32 * s + 8 * g) * 2);
+  } else {
+#pragma unroll
+    for (int hp = 0; hp < HP; ++hp)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const char* qrow = q_row(hp, n * 16 + j);
+#pragma unroll
+        for (int s = 0; s < S::kQSteps; ++s) qb[hp][s][n] = ld16(qrow + (32 * s + 8 * g) * 2);
+      }
+  }
+  __asm__ volatile("" ::: "memory");
+
+  // ---- prologue: blocks 0 .. kDepth - 1 in flight, all kDepth loaded
+  // (past the wave's last block they repeat one of the context's blocks,
+  // never stored).  Q has then arrived once at most the K/V loads are
+  // outstanding: the explicit waits (on both paths) say so, and spare the
+  // loop's uses of Q a wait for every load in flight.
+  if (nbw > 0) {
+#pragma unroll
+    for (int d = 0; d < S::kDepth; ++d) load_block(block_id(d), rb[d]);
+    constexpr int kKV = S::kDepth * 2 * kL;
+    static_assert(kKV < 64, "vmcnt is six bits");
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((kKV & 15) | (7 << 4) | (15 << 8) | ((kKV >> 4) << 14));
+  } else {
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0): Q only
+  }
+  if constexpr (!S::kQInLds) {
+#pragma unroll
+    for (int hp = 0; hp < HP; ++hp)
 #pragma unroll
       for (int s = 0; s < S::kQSteps; ++s)
-        *reinterpret_cast<uint4*>(qlds + m * S::kRow + ((4 * s + g) ^ k_swz<S::kRow>(m)) * 16) =
-            ld16(qrow + (32 * s + 8 * g) * 2);
-      __syncthreads();
-    } else {
 #pragma unroll
-      for (int hp = 0; hp < HP; ++hp)
+        for (int n = 0; n < NT; ++n)
+          __asm__ volatile("" : "+v"(qb[hp][s][n].x), "+v"(qb[hp][s][n].y),
+                                "+v"(qb[hp][s][n].z), "+v"(qb[hp][s][n].w));
+  }
+  int next_id = block_id(S::kDepth);
+  if constexpr (S::kQInLds) {
+    const int m = wave * 16 + j;
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          const char* qrow = q_row(hp, n * 16 + j);
-#pragma unroll
-          for (int s = 0; s < S::kQSteps; ++s) qb[hp][s][n] = ld16(qrow + (32 * s + 8 * g) * 2);
-        }
-    }
+    for (int s = 0; s < S::kQSteps; ++s)
+      *reinterpret_cast<uint4*>(qlds + m * S::kRow + ((4 * s + g) ^ k_swz<S::kRow>(m)) * 16) =
+          qb[0][s][0];
+    __syncthreads();
   }
   auto q_op = [&](int hp, int s, int n) __attribute__((always_inline)) {
     if constexpr (S::kQInLds) {
@@ -388,12 +448,19 @@ __device__ __forceinline__ int verify_item(const VerifyParams& p, int ticket, ch
       f32x4_v sacc[NT];
 #pragma unroll
       for (int n = 0; n < NT; ++n) sacc[n] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+      // All of the head's K fragments are read before its MFMAs (the fence
+      // keeps the compiler from interleaving them again): one LDS latency
+      // per head instead of one per MFMA.
+      uint4 ka[S::kQSteps];
+#pragma unroll
+      for (int s = 0; s < S::kQSteps; ++s)
+        ka[s] = *reinterpret_cast<const uint4*>(
+            st + k_off + (((hp * S::kChunks + 4 * s + g) * 16) ^ k_x));
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < S::kQSteps; ++s) {
-        const uint4 a = *reinterpret_cast<const uint4*>(
-            st + k_off + (((hp * S::kChunks + 4 * s + g) * 16) ^ k_x));
 #pragma unroll
-        for (int n = 0; n < NT; ++n) sacc[n] = mfma_qk(a, q_op(hp, s, n), sacc[n]);
+        for (int n = 0; n < NT; ++n) sacc[n] = mfma_qk(ka[s], q_op(hp, s, n), sacc[n]);
       }
       // ---- mask: key 4 g + r of the block against each row's limit
       if (masked) {
@@ -447,12 +514,16 @@ __device__ __forceinline__ int verify_item(const VerifyParams& p, int ticket, ch
 #pragma unroll
       for (int n = 0; n < NT; ++n) run_sum[hp][n] += psum[n];
       // ---- O^T += V^T P^T
+      // (the V^T fragments likewise, all before the MFMAs)
+      uint2 va[S::kDTiles];
+#pragma unroll
+      for (int dt = 0; dt < S::kDTiles; ++dt)
+        va[dt] = lds_read_tr16(st + v_off + (((hp * S::kChunks + 2 * dt) * 16) ^ v_x));
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int dt = 0; dt < S::kDTiles; ++dt) {
-        const uint2 a =
-            lds_read_tr16(st + v_off + (((hp * S::kChunks + 2 * dt) * 16) ^ v_x));
 #pragma unroll
-        for (int n = 0; n < NT; ++n) oacc[hp][dt][n] = mfma_pv(a, pb[n], oacc[hp][dt][n]);
+        for (int n = 0; n < NT; ++n) oacc[hp][dt][n] = mfma_pv(va[dt], pb[n], oacc[hp][dt][n]);
       }
     }
   };
@@ -461,21 +532,21 @@ __device__ __forceinline__ int verify_item(const VerifyParams& p, int ticket, ch
   // wave's LDS stage, the block kDepth further on is loaded into the freed
   // registers, and the stage is computed.  (LDS operations of one wave run
   // in order: the stores of block jb + 1 follow the reads of block jb.)
+  // Every step stores and loads, also the last group's steps past the
+  // wave's last block (which load the partition's last block again and
+  // compute nothing): with no load skipped, every wait for a block counts
+  // exactly the kDepth - 1 blocks loaded after it.
   for (int jb0 = 0; jb0 < nbw; jb0 += S::kDepth) {
 #pragma unroll
     for (int d = 0; d < S::kDepth; ++d) {
       const int jb = jb0 + d;
-      if (jb < nbw) {
-        store_block(rb[d]);
-        if (jb + S::kDepth < nbw) {
-          load_block(next_id, rb[d]);
-          next_id = block_id(jb + S::kDepth + 1);
-        }
-        // keep the loads here: the compiler may otherwise sink them to
-        // their use
-        __asm__ volatile("" ::: "memory");
-        compute(kb0 + wave + kWaves * jb);
-      }
+      store_block(rb[d]);
+      load_block(next_id, rb[d]);
+      next_id = block_id(jb + S::kDepth + 1);
+      // keep the loads here: the compiler may otherwise sink them to
+      // their use
+      __asm__ volatile("" ::: "memory");
+      if (jb < nbw) compute(kb0 + wave + kWaves * jb);
     }
   }
 
@@ -537,7 +608,7 @@ __device__ __forceinline__ int verify_item(const VerifyParams& p, int ticket, ch
         o[6] = fmaf(a, y.z, o[6]); o[7] = fmaf(a, y.w, o[7]);
       }
     }
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float inv = (l > 0.f ? 1.f / l : 0.f) * p.v_scale;
     const int i = m / G;
     const int head = (kvh0 + rr / S::kRows) * G + m % G;
     if (p.num_partitions == 1) {
@@ -581,10 +652,10 @@ __device__ __forceinline__ int verify_item(const VerifyParams& p, int ticket, ch
 // until none are left: the XCDs of one chip do not stream at the same rate,
 // and a fixed share of the work per XCD (the dispatcher deals workgroups to
 // the XCDs round robin) would leave the fast ones idle at the end.
-template <int D, int G, int NT, int HP>
+template <int D, int G, int NT, int HP, bool F8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 verify_kernel(VerifyParams p) {
-  using S = VerifyShape<D, NT, HP>;
+  using S = VerifyShape<D, NT, HP, F8>;
   extern __shared__ __align__(16) char smem[];
   int* s_ticket = reinterpret_cast<int*>(smem + S::kTicket);
   if (threadIdx.x == 0) *s_ticket = atomicAdd(p.counter, 1);
@@ -592,7 +663,7 @@ verify_kernel(VerifyParams p) {
   int t = *s_ticket;
   while (t < p.num_tickets) {
     __syncthreads();   // every thread has read the ticket
-    t = verify_item<D, G, NT, HP>(p, __builtin_amdgcn_readfirstlane(t), smem);
+    t = verify_item<D, G, NT, HP, F8>(p, __builtin_amdgcn_readfirstlane(t), smem);
   }
 }
 
@@ -641,12 +712,12 @@ __global__ __launch_bounds__(kPlanThreads) void verify_plan_kernel(
       order, bins, wave_sum);
 }
 
-template <int D, int G, int NT, int HP>
+template <int D, int G, int NT, int HP, bool F8>
 hipError_t launch_nt(const VerifyParams& prm, const VerifyPlan& plan, hipStream_t s) {
-  using S = VerifyShape<D, NT, HP>;
+  using S = VerifyShape<D, NT, HP, F8>;
   static bool raised = false;   // once per kernel instantiation
   if (!raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&verify_kernel<D, G, NT, HP>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&verify_kernel<D, G, NT, HP, F8>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(S::kLds));
     if (e != hipSuccess) return e;
@@ -659,7 +730,7 @@ hipError_t launch_nt(const VerifyParams& prm, const VerifyPlan& plan, hipStream_
                      const_cast<int32_t*>(prm.order));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((verify_kernel<D, G, NT, HP>), dim3(static_cast<unsigned>(wgs)),
+  hipLaunchKernelGGL((verify_kernel<D, G, NT, HP, F8>), dim3(static_cast<unsigned>(wgs)),
                      dim3(kThreads), S::kLds, s, prm);
   e = hipGetLastError();
   if (e != hipSuccess || plan.num_partitions == 1) return e;
@@ -670,25 +741,33 @@ hipError_t launch_nt(const VerifyParams& prm, const VerifyPlan& plan, hipStream_
   return hipGetLastError();
 }
 
-template <int D, int G>
+// An E4M3 cache comes only with one query row per sequence (the decode
+// route): one row tile.
+template <int D, int G, bool F8>
 hipError_t launch_g(const VerifyParams& prm, const VerifyPlan& plan, hipStream_t s) {
-  switch (plan.row_tiles) {
-    case 1: return plan.heads_per_item == 2 ? launch_nt<D, G, 1, 2>(prm, plan, s)
-                                            : launch_nt<D, G, 1, 1>(prm, plan, s);
-    case 2: return launch_nt<D, G, 2, 1>(prm, plan, s);
-    case 4: return launch_nt<D, G, 4, 1>(prm, plan, s);
-    default: return hipErrorInvalidValue;
+  if constexpr (F8) {
+    if (plan.row_tiles != 1) return hipErrorInvalidValue;
+    return plan.heads_per_item == 2 ? launch_nt<D, G, 1, 2, true>(prm, plan, s)
+                                    : launch_nt<D, G, 1, 1, true>(prm, plan, s);
+  } else {
+    switch (plan.row_tiles) {
+      case 1: return plan.heads_per_item == 2 ? launch_nt<D, G, 1, 2, false>(prm, plan, s)
+                                              : launch_nt<D, G, 1, 1, false>(prm, plan, s);
+      case 2: return launch_nt<D, G, 2, 1, false>(prm, plan, s);
+      case 4: return launch_nt<D, G, 4, 1, false>(prm, plan, s);
+      default: return hipErrorInvalidValue;
+    }
   }
 }
 
-template <int D>
+template <int D, bool F8 = false>
 hipError_t launch_d(const VerifyParams& prm, const VerifyPlan& plan, int g,
                     hipStream_t s) {
   switch (g) {
-    case 1: return launch_g<D, 1>(prm, plan, s);
-    case 2: return launch_g<D, 2>(prm, plan, s);
-    case 4: return launch_g<D, 4>(prm, plan, s);
-    case 8: return launch_g<D, 8>(prm, plan, s);
+    case 1: return launch_g<D, 1, F8>(prm, plan, s);
+    case 2: return launch_g<D, 2, F8>(prm, plan, s);
+    case 4: return launch_g<D, 4, F8>(prm, plan, s);
+    case 8: return launch_g<D, 8, F8>(prm, plan, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -762,7 +841,7 @@ VerifyPlan plan_verify(int num_seqs, int num_heads, int num_kv_heads,
 namespace {
 
 hipError_t launch_plan(VerifyParams& prm, const VerifyPlan& plan, void* workspace,
-                       int head_dim, hipStream_t stream) {
+                       int head_dim, bool fp8_cache, hipStream_t stream) {
   const int64_t tickets = static_cast<int64_t>(prm.num_seqs) * plan.num_partitions *
                           (prm.num_kv_heads / plan.heads_per_item);
   const int64_t merges = static_cast<int64_t>(prm.num_seqs) * prm.max_seqlen_q * prm.num_heads;
@@ -780,6 +859,10 @@ hipError_t launch_plan(VerifyParams& prm, const VerifyPlan& plan, void* workspac
   prm.num_tickets = static_cast<int>(tickets);
   prm.heads_per_item = plan.heads_per_item;
   const int g = prm.num_heads / prm.num_kv_heads;
+  if (fp8_cache) {
+    if (head_dim != 128) return hipErrorNotSupported;
+    return launch_d<128, true>(prm, plan, g, stream);
+  }
   if (head_dim == 128) return launch_d<128>(prm, plan, g, stream);
   return launch_d<64>(prm, plan, g, stream);
 }
@@ -803,9 +886,12 @@ hipError_t launch_verify_decode(const DecodeArgs& a, const VerifyPlan& plan,
   prm.num_seqs = a.num_seqs;
   prm.num_heads = a.num_heads;
   prm.num_kv_heads = a.num_kv_heads;
-  prm.scale_log2 = a.scale * kLog2e;
+  // E4M3 cache: K = code * k_scale joins the logit scale, V = code *
+  // v_scale the output (both 1 otherwise).
+  prm.scale_log2 = a.scale * a.k_scale * kLog2e;
+  prm.v_scale = a.v_scale;
   prm.causal = 1;
-  return launch_plan(prm, plan, a.workspace, a.head_dim, stream);
+  return launch_plan(prm, plan, a.workspace, a.head_dim, a.fp8_cache, stream);
 }
 
 hipError_t launch_verify(const PrefillArgs& a, const VerifyPlan& plan,
@@ -827,8 +913,9 @@ hipError_t launch_verify(const PrefillArgs& a, const VerifyPlan& plan,
   prm.num_heads = a.num_heads;
   prm.num_kv_heads = a.num_kv_heads;
   prm.scale_log2 = a.scale * kLog2e;
+  prm.v_scale = 1.f;
   prm.causal = a.causal ? 1 : 0;
-  return launch_plan(prm, plan, a.workspace, a.head_dim, stream);
+  return launch_plan(prm, plan, a.workspace, a.head_dim, false, stream);
 }
 
 }  // namespace pa

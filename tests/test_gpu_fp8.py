@@ -128,6 +128,30 @@ def test_decode_fp8_full_size_sampled():
                  lay=lay)
 
 
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (16, 8), (8, 8), (24, 3)])
+def test_decode_fp8_large_batch(hq, hkv):
+    """Batches with >= 1024 (sequence, KV head pair) work items run on the
+    small-row attention kernel, which widens the codes to bfloat16 on their
+    way to LDS: two KV heads per item where Hkv is even, one where it is
+    odd (Hkv = 3, GQA 8).  Contexts from 1 to 3,000 tokens with block
+    edges, a NaN-poisoned pool; one-token contexts return code * v_scale
+    exactly (power-of-two scales)."""
+    say("decode fp8 large batch", hq, hkv)
+    per_seq = hkv // 2 if hkv % 2 == 0 else hkv
+    n = -(-1024 // per_seq) + 3
+    rng = np.random.default_rng(hq * 10 + hkv)
+    lens = rng.integers(1, 3000, n, endpoint=True)
+    lens[:9] = [1, 15, 16, 17, 511, 512, 513, 1024, 3000]
+    lens[-1] = 1
+    lay = wl.decode_layout(lens.tolist(), 16, seed=hq + hkv)
+    seqs = sorted(set(range(9)) | {n - 1} |
+                  set(sample_seqs(lens, 15, seed=hkv)))
+    got, want = _decode_case(None, hq, hkv, 1 / 16, 1 / 8, seed=hq + 7,
+                             seqs=seqs, lay=lay)
+    one = [i for i, b in enumerate(seqs) if lens[b] == 1]
+    assert one and np.array_equal(got[one], want[one])
+
+
 def test_store_then_decode_fp8():
     """One decode step end to end: quantise each sequence's new row into its
     slot, then decode; both the caches and the outputs match the oracle's
