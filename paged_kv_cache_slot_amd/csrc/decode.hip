@@ -65,10 +65,6 @@ constexpr int kWaves = 4;            // waves per workgroup
 constexpr int kThreads = kWaves * kWave;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr uint32_t kBf16PairOne = 0x3F803F80u;   // (1.0, 1.0) as bfloat16
-// Word 3 of a raw (unswizzled, untyped) gfx9 buffer resource.
-constexpr int kBufferRsrcWord3 = 0x00020000;
-// Cache-policy bits of a buffer load: non-temporal (streamed, used once).
-constexpr int kCacheNT = 2;
 
 // How a wave covers one 16-token block of one KV head: kLpr lanes share a
 // row (token), each lane takes kCpl 16-byte chunks of it, and one load
@@ -303,22 +299,6 @@ __device__ __forceinline__ RankedItem ranked_item(const DecodeParams& p, int r) 
   const int b = __ffsll(static_cast<unsigned long long>(m)) - 1;
   const int lb = __builtin_amdgcn_readlane(len, b);
   return {(lb / pt) * p.num_seqs + b, lb};
-}
-
-// A bounds-checked view of one cache block: a buffer resource whose size is
-// the bytes of the block's valid tokens.  Loads past that size return zeros
-// without touching memory, so a block past the context, a block id outside
-// the pool and the slots past the context of a partial block all read as
-// zero, and every load instruction can be issued unconditionally.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const char* base,
-                                                            int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes,
-                                           kBufferRsrcWord3);
-}
-__device__ __forceinline__ uint4 buf_ld16_nt(__amdgpu_buffer_rsrc_t r,
-                                             uint32_t off) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCacheNT);
-  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 __device__ __forceinline__ uint2 buf_ld8_nt(__amdgpu_buffer_rsrc_t r,

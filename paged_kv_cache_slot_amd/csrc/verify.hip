@@ -282,24 +282,31 @@ __device__ __forceinline__ int verify_item(const VerifyParams& p, int ticket, ch
     }
   }
   // Block ids are scalar loads (wave-uniform indices), clamped to the
-  // partition's last block (past the wave's last block the loads repeat it:
-  // a cache hit); an id outside the pool reads block 0 instead.
+  // partition's last block (steps past the wave's last block load nothing).
   const int kb_last = kb0 + nblk - 1;
   auto block_id = [&](int jb) __attribute__((always_inline)) {
     return load_uniform_i32(btab, min(kb0 + wave + kWaves * jb, kb_last));
   };
   constexpr int kL = S::kLoads;
   uint4 rb[S::kDepth][2 * kL];   // blocks in flight: K loads, then V loads
-  auto load_block = [&](int blk, uint4 (&r)[2 * kL]) __attribute__((always_inline)) {
-    blk = blk >= 0 && blk < p.num_blocks ? blk : 0;
-    const int64_t off = static_cast<int64_t>(blk) * blk_bytes;
-    const char* kb = p.k_cache + off;
-    const char* vb = p.v_cache + off;
+  // Step jb's block (id blk) through bounds-checked views of its valid
+  // tokens: rows past the context, a step past the wave's last block and a
+  // block id outside the pool read as zeros without touching memory.
+  // Returns 1 for an id outside the pool (whose keys are then masked).
+  auto load_block = [&](int jb, int blk, uint4 (&r)[2 * kL]) __attribute__((always_inline)) {
+    const bool in_pool = blk >= 0 && blk < p.num_blocks;
+    const int kbj = kb0 + wave + kWaves * jb;
+    const int ntok = jb < nbw && in_pool ? min(kBlock, lk - kbj * kBlock) : 0;
+    const int64_t off = static_cast<int64_t>(in_pool ? blk : 0) * blk_bytes;
+    const int bytes = ntok * static_cast<int>(row_stride);
+    const auto rk = block_rsrc(p.k_cache + off, bytes);
+    const auto rv = block_rsrc(p.v_cache + off, bytes);
 #pragma unroll
     for (int u = 0; u < kL; ++u) {
-      r[u] = ld16_nt(kb + k_src[u]);
-      r[kL + u] = ld16_nt(vb + v_src[u]);
+      r[u] = buf_ld16_nt(rk, k_src[u]);
+      r[kL + u] = buf_ld16_nt(rv, v_src[u]);
     }
+    return in_pool ? 0 : 1;
   };
   char* st = smem + wave * S::kStage;   // this wave's stage
   auto store_block = [&](const uint4 (&r)[2 * kL]) __attribute__((always_inline)) {
@@ -352,14 +359,14 @@ __device__ __forceinline__ int verify_item(const VerifyParams& p, int ticket, ch
   }
   __asm__ volatile("" ::: "memory");
 
-  // ---- prologue: blocks 0 .. kDepth - 1 in flight, all kDepth loaded
-  // (past the wave's last block they repeat one of the context's blocks,
-  // never stored).  Q has then arrived once at most the K/V loads are
+  // ---- prologue: blocks 0 .. kDepth - 1 in flight, all kDepth loads
+  // issued (past the wave's last block they read nothing).  Q has then arrived once at most the K/V loads are
   // outstanding: the explicit waits (on both paths) say so, and spare the
   // loop's uses of Q a wait for every load in flight.
+  int bad[S::kDepth];   // per block in flight: its id is outside the pool
   if (nbw > 0) {
 #pragma unroll
-    for (int d = 0; d < S::kDepth; ++d) load_block(block_id(d), rb[d]);
+    for (int d = 0; d < S::kDepth; ++d) bad[d] = load_block(d, block_id(d), rb[d]);
     constexpr int kKV = S::kDepth * 2 * kL;
     static_assert(kKV < 64, "vmcnt is six bits");
     __asm__ volatile("" ::: "memory");
@@ -429,19 +436,10 @@ __device__ __forceinline__ int verify_item(const VerifyParams& p, int ticket, ch
       run_sum[hp][n] = 0.f;         // this lane's share of the row sum
     }
 
-  auto compute = [&](int kb) __attribute__((always_inline)) {
+  // (V rows past Lk arrive as zeros, so P V never meets stale values.)
+  auto compute = [&](int kb, int bad_blk) __attribute__((always_inline)) {
     const int kbase = kb * kBlock;
-    // V rows past Lk: zeros (this wave's own stage; LDS ops of one wave run
-    // in order, so the transpose reads below see them).
-    if (kbase + kBlock > lk) {
-#pragma unroll
-      for (int u = 0; u < S::kBlockBytes / 16 / kWave; ++u) {
-        const int c = u * kWave + lane;
-        if (kbase + c / (kP / 16) >= lk)
-          *reinterpret_cast<uint4*>(st + S::kBlockBytes + c * 16) = make_uint4(0, 0, 0, 0);
-      }
-    }
-    const bool masked = kbase + kBlock - 1 > min_lim || kbase + kBlock > lk;
+    const bool masked = bad_blk || kbase + kBlock - 1 > min_lim || kbase + kBlock > lk;
 #pragma unroll
     for (int hp = 0; hp < HP; ++hp) {
       // ---- S^T = K Q^T
@@ -468,7 +466,7 @@ __device__ __forceinline__ int verify_item(const VerifyParams& p, int ticket, ch
         for (int n = 0; n < NT; ++n)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            sacc[n][r] = kbase + 4 * g + r <= lim[n] ? sacc[n][r] : -INFINITY;
+            sacc[n][r] = !bad_blk && kbase + 4 * g + r <= lim[n] ? sacc[n][r] : -INFINITY;
       }
       // ---- online softmax.  Fast path: weights against the reference
       // max, summed over the bfloat16-rounded values the PV step uses; a
@@ -532,21 +530,22 @@ __device__ __forceinline__ int verify_item(const VerifyParams& p, int ticket, ch
   // wave's LDS stage, the block kDepth further on is loaded into the freed
   // registers, and the stage is computed.  (LDS operations of one wave run
   // in order: the stores of block jb + 1 follow the reads of block jb.)
-  // Every step stores and loads, also the last group's steps past the
-  // wave's last block (which load the partition's last block again and
-  // compute nothing): with no load skipped, every wait for a block counts
-  // exactly the kDepth - 1 blocks loaded after it.
+  // Every step stores and issues its loads, also the last group's steps
+  // past the wave's last block (whose loads read nothing and which compute
+  // nothing): with no load skipped, every wait for a block counts exactly
+  // the kDepth - 1 blocks loaded after it.
   for (int jb0 = 0; jb0 < nbw; jb0 += S::kDepth) {
 #pragma unroll
     for (int d = 0; d < S::kDepth; ++d) {
       const int jb = jb0 + d;
+      const int bad_blk = bad[d];
       store_block(rb[d]);
-      load_block(next_id, rb[d]);
+      bad[d] = load_block(jb + S::kDepth, next_id, rb[d]);
       next_id = block_id(jb + S::kDepth + 1);
       // keep the loads here: the compiler may otherwise sink them to
       // their use
       __asm__ volatile("" ::: "memory");
-      if (jb < nbw) compute(kb0 + wave + kWaves * jb);
+      if (jb < nbw) compute(kb0 + wave + kWaves * jb, bad_blk);
     }
   }
 

@@ -273,3 +273,65 @@ def test_self_ranked_schedule(dtype, b, hq, hkv, d, longest):
     assert np.all(got[b:] == 0.0)
     err = np.max(np.abs(got - want))
     assert err <= TOL[dtype], f"max abs err {err}"
+
+
+@pytest.mark.parametrize("n_seqs", [8, 259])
+def test_out_of_pool_ids_contribute_nothing(n_seqs):
+    """A context block whose id lies outside [0, num_blocks) contributes
+    nothing: the row equals attention over the sequence's other tokens (a
+    row left with no key is zero).  8 sequences run on the decode kernel,
+    259 (>= 1024 (sequence, KV head pair) items) on the small-row kernel.
+    Bad ids: negative, num_blocks, far past it; a first, middle and last
+    (partial) block; every block of one sequence."""
+    import math
+
+    import oracle.attention as oa
+    from paged_kv_cache_slot_amd import metadata as pm
+    from paged_kv_cache_slot_amd import ops
+    from tests.gpu_harness import dev_i32
+    say("decode out-of-pool ids", n_seqs)
+    hq, hkv, d, bs = 32, 8, 128, 16
+    rng = np.random.default_rng(700 + n_seqs)
+    lens = rng.integers(1, 3000, n_seqs, endpoint=True)
+    lens[:5] = [40, 3000, 1000, 20, 517]
+    lay = wl.decode_layout(lens.tolist(), bs, seed=n_seqs)
+    kc, vc = wl.fill_pool(lay.num_blocks, bs, hkv, d, "bf16", 31, "cuda")
+    wl.poison_unused(kc, vc, wl.valid_slot_mask(lay.num_blocks, bs,
+                                                lay.tables, lay.lens))
+    q = wl.make_values((n_seqs, hq, d), "bf16", 32, "cuda")
+    meta = pm.decode_inputs(lay.tables, lay.lens, bs)
+    nb = lay.num_blocks
+    bt = meta["block_tables"].copy()
+    bad = {0: [(1, -3)],                    # middle block of 3
+           1: [(0, nb), (100, -1)],         # first and a middle block
+           2: [(62, nb + 1000)],            # last, partial block (1000 = 62*16 + 8)
+           3: [(0, -7), (1, nb)],           # every block: a zero row
+           4: [(32, 2 * nb)]}               # last block, 5 tokens
+    for b, entries in bad.items():
+        for j, v in entries:
+            assert j * bs < lens[b]
+            bt[b, j] = v
+    out = ops.decode(q, kc, vc, dev_i32(bt), dev_i32(meta["context_lens"]),
+                     meta["max_context_len"], scale=1.0 / math.sqrt(d))
+    torch.cuda.synchronize()
+    got = f64(out)
+    h_kc, h_vc, h_q = (wl.host_bits(x) for x in (kc, vc, q))
+    q64 = oa.to_f64(h_q, "bf16")
+    checked = sorted(set(bad) | set(sample_seqs(lens, 6, seed=n_seqs)))
+    for b in checked:
+        n = int(lens[b])
+        keys, vals = oa.gather_sequence_kv(h_kc, h_vc, lay.tables[b], n, "bf16")
+        keep = np.ones(n, bool)
+        for j, _ in bad.get(b, []):
+            keep[j * bs:(j + 1) * bs] = False
+        keys, vals = keys[keep], vals[keep]
+        want = np.zeros((hq, d))
+        for h in range(hq):
+            g = h // (hq // hkv)
+            o, _ = oa.attend(q64[b, h][None, :], keys[:, g, :], vals[:, g, :],
+                             1.0 / math.sqrt(d), [len(keys)])
+            want[h] = o[0]
+        assert np.all(np.isfinite(got[b])), b
+        err = float(np.max(np.abs(got[b] - want)))
+        assert err <= TOL["bf16"], (b, err)
+    assert np.all(got[3] == 0.0)
