@@ -107,14 +107,20 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache,
 
 namespace {
 
-// Which kernel a decode call runs.  A bfloat16 decode large enough that
-// the decode kernel splits its contexts into partitions while the small-row
-// attention kernel (one query row per sequence) needs none -- a batch with
-// >= 1024 (sequence, KV head pair) work items -- runs on the latter: it
-// streams the cache faster (8B-shaped step, 256 sequences: 744 -> 688 us)
-// and needs no merge pass.  Smaller bf16 batches, whose small-row plan would
-// split and merge (64 sequences: 109 -> 115 us, measured), every decode
-// without partitions, and every fp32 decode run on the decode kernel.
+// Which kernel a decode call runs.  A decode (bf16 q, bf16 or E4M3 cache)
+// that the decode kernel would split into partitions runs on the small-row
+// attention kernel (one query row per sequence) when that kernel's plan
+// needs no partitions -- a batch with >= 1024 (sequence, KV head pair) work
+// items -- or partitions of >= 2048 tokens: it streams the cache faster
+// (8B-shaped step 744 -> 688 us; 8-bit cache 415-448 -> 356-360 us; 192
+// sequences of U[256, 8192] in 2 partitions 550 -> 502 us; 48-160-sequence
+// batches with 2-8 partitions of 2,752-4,096 tokens 2-22 % faster).  With
+// shorter partitions its per-item start and combine weigh more (64
+// sequences in 4 partitions of 1,024: 102.6 -> 107.3 us; 128 sequences in
+// 2 of 1,280: 128 -> 152 us), so those, every decode without partitions
+// and every fp32 decode run on the decode kernel.
+constexpr int kRowsMinPartitionTokens = 2048;
+
 struct DecodeRoute {
   pa::DecodePlan decode;
   pa::VerifyPlan rows;
@@ -130,7 +136,8 @@ DecodeRoute route_decode(int num_seqs, int num_heads, int num_kv_heads,
   r.rows = pa::plan_verify(num_seqs, num_heads, num_kv_heads, head_dim, 1,
                            max_context_len);
   r.use_rows = bf16 && r.decode.workspace_bytes > 0 && r.rows.use &&
-               r.rows.num_partitions == 1;
+               (r.rows.num_partitions == 1 ||
+                r.rows.partition_tokens >= kRowsMinPartitionTokens);
   r.bytes = r.use_rows ? r.rows.workspace_bytes : r.decode.workspace_bytes;
   return r;
 }

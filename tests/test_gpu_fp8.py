@@ -152,6 +152,24 @@ def test_decode_fp8_large_batch(hq, hkv):
     assert one and np.array_equal(got[one], want[one])
 
 
+@pytest.mark.parametrize("b,hkv,longest,part", [(192, 8, 8192, 4096),
+                                                (100, 3, 12000, 3008)])
+def test_decode_fp8_partitioned_small_row(b, hkv, longest, part):
+    """8-bit caches on the small-row kernel with partitions of >= 2,048
+    tokens (partials and a merge; v_scale reaches the output through both):
+    contexts at partition and block edges, 1 token and the longest."""
+    say("decode fp8 partitioned small-row", b, hkv)
+    hq = 8 * hkv if hkv == 3 else 32
+    rng = np.random.default_rng(b * 3 + hkv)
+    lens = rng.integers(1, longest, b, endpoint=True)
+    edges = [longest, 1, part - 1, part, part + 1, 2 * part + 5, 16, 17]
+    lens[:len(edges)] = edges
+    lay = wl.decode_layout(lens.tolist(), 16, seed=b + 11)
+    seqs = sorted(set(range(len(edges))) | set(sample_seqs(lens, 8, seed=b)))
+    _decode_case(None, hq, hkv, 0.0371, 0.153, seed=b + 13, seqs=seqs,
+                 lay=lay)
+
+
 def test_store_then_decode_fp8():
     """One decode step end to end: quantise each sequence's new row into its
     slot, then decode; both the caches and the outputs match the oracle's
