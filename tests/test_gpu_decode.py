@@ -337,27 +337,28 @@ def test_out_of_pool_ids_contribute_nothing(n_seqs):
     assert np.all(got[3] == 0.0)
 
 
-@pytest.mark.parametrize("b,hq,hkv,longest,part", [
-    (192, 32, 8, 8192, 4096),    # 768 items: 2 partitions of 4,096
-    (48, 64, 8, 16384, 2752),    # GQA 8: 6 partitions of 2,752
-    (100, 24, 3, 12000, 3008),   # odd Hkv (one KV head per item): 4 of 3,008
+@pytest.mark.parametrize("b,hq,hkv,longest,part,d", [
+    (192, 32, 8, 8192, 4096, 128),   # 768 items: 2 partitions of 4,096
+    (48, 64, 8, 16384, 2752, 128),   # GQA 8: 6 partitions of 2,752
+    (100, 24, 3, 12000, 3008, 128),  # odd Hkv (one KV head per item): 4 of 3,008
+    (160, 16, 4, 10000, 2560, 64),   # D = 64: 4 partitions of 2,560
 ])
-def test_partitioned_small_row_route(b, hq, hkv, longest, part):
+def test_partitioned_small_row_route(b, hq, hkv, longest, part, d):
     """bf16 decode batches whose small-row plan splits contexts into
     partitions of >= 2,048 tokens run on that kernel with partials and a
     merge: contexts at partition and block edges, 1 token and the longest;
     the workspace starts as all-ones bytes, and two calls in a row agree."""
     from paged_kv_cache_slot_amd import ops
-    say("decode partitioned small-row route", b, hq, hkv)
+    say("decode partitioned small-row route", b, hq, hkv, d)
     rng = np.random.default_rng(b + hkv)
     lens = rng.integers(1, longest, b, endpoint=True)
     edges = [longest, 1, part - 1, part, part + 1, 2 * part, 2 * part + 17,
              15, 16, 17]
     lens[:len(edges)] = [min(e, longest) for e in edges]
     lay = wl.decode_layout(lens.tolist(), 16, seed=b + hq)
-    case = DecodeCase(lay, hq, hkv, 128, "bf16", seed=b + 3)
+    case = DecodeCase(lay, hq, hkv, d, "bf16", seed=b + 3)
     case.run_store()
-    ws = torch.full((ops.decode_workspace_bytes(b, hq, hkv, 128,
+    ws = torch.full((ops.decode_workspace_bytes(b, hq, hkv, d,
                                                 case.max_context_len),),
                     255, dtype=torch.uint8, device="cuda")
     first = case.run_decode(workspace=ws)
