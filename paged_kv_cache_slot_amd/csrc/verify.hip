@@ -1,5 +1,7 @@
 // Varlen attention of a few query rows per sequence over a paged context --
-// the shape of a speculative-decoding verify pass -- for gfx950, bfloat16.
+// the shape of a speculative-decoding verify pass, and of large decode
+// batches (one row per sequence) -- for gfx950, bfloat16 (the decode route
+// also over an 8-bit E4M3 cache).
 //
 // What it computes: exactly what the varlen prefill computes (sequence b
 // owns query rows cu_q[b] .. cu_q[b+1]-1, Lq of them, and its first Lk
@@ -25,17 +27,21 @@
 //    robin share per XCD would leave the fast XCDs idle for the last ~15 %
 //    of the launch;
 //  * wave w streams cache blocks w, w + 4, ... of its partition with 16-byte
-//    loads into registers, kDepth blocks ahead, and writes each block to
-//    its own LDS stage (16-byte chunks XOR-swizzled by row) right before
-//    computing it; waves never wait for each other inside the loop.  Loads
-//    into registers stream faster than LDS DMA here (~6.7 against ~6.3 TB/s
-//    measured on this access pattern);
+//    bounds-checked buffer loads into registers, kDepth blocks ahead, and
+//    writes each block to its own LDS stage (16-byte chunks XOR-swizzled by
+//    row; E4M3 codes widened to bfloat16 on the way) right before computing
+//    it; waves never wait for each other inside the loop.  Every loop step
+//    issues its loads (past the wave's last block they are sized to
+//    nothing), so each wait for a block counts exactly the blocks loaded
+//    after it.  Loads into registers stream faster than LDS DMA here (~6.7
+//    against ~6.3 TB/s measured on this access pattern);
 //  * with one row tile and an even number of KV heads a work item takes
 //    two adjacent KV heads: each token's read is then one 512-byte piece,
 //    which streams at the chip's full read rate (~7.2 TB/s measured, 6.7
 //    for 256-byte pieces);
-//  * per block: S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = 16 keys from
-//    LDS, B = Q^T held in registers), online softmax per lane (a lane holds
+//  * per block and head: S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = 16
+//    keys from LDS, all four fragments read before the MFMAs; B = Q^T held
+//    in registers), online softmax per lane (a lane holds
 //    four keys of one row), O^T += V^T P^T with v_mfma_f32_16x16x16_bf16
 //    (A = V^T by LDS transpose reads, B = P^T taken straight from the S^T
 //    accumulators, whose layout is already the B operand's);
@@ -45,9 +51,10 @@
 //  * the four waves' (max, sum, O) are combined through LDS at the end; a
 //    single partition writes the output, several write binary16 partials
 //    that a merge kernel combines with log-sum-exp weights;
-//  * masking by select: keys past a row's causal limit or past Lk get
-//    weight exactly 0, and V rows past Lk are zeroed in LDS (a NaN there
-//    would survive a multiplication by zero).
+//  * masking by select: keys past a row's causal limit or past Lk, and the
+//    keys of a block whose id lies outside the pool, get weight exactly 0;
+//    V rows past Lk and such blocks arrive as zeros from the bounds-checked
+//    loads (a NaN there would survive a multiplication by zero).
 #include <math.h>
 
 #include <atomic>
@@ -360,9 +367,10 @@ __device__ __forceinline__ int verify_item(const VerifyParams& p, int ticket, ch
   __asm__ volatile("" ::: "memory");
 
   // ---- prologue: blocks 0 .. kDepth - 1 in flight, all kDepth loads
-  // issued (past the wave's last block they read nothing).  Q has then arrived once at most the K/V loads are
-  // outstanding: the explicit waits (on both paths) say so, and spare the
-  // loop's uses of Q a wait for every load in flight.
+  // issued (past the wave's last block they read nothing).  Q has then
+  // arrived once at most the K/V loads are outstanding: the explicit waits
+  // (on both paths) say so, and spare the loop's uses of Q a wait for every
+  // load in flight.
   int bad[S::kDepth];   // per block in flight: its id is outside the pool
   if (nbw > 0) {
 #pragma unroll
