@@ -467,6 +467,9 @@ prefill_kernel(PrefillParams p) {
             a1[u] = *reinterpret_cast<const float*>(krow1 + off);
           }
         }
+        // (the fence keeps the compiler from moving the reads back next
+        // to their MFMAs, one LDS latency per MFMA pair)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           sacc[0] = M::run(a0[u], qb[s0 + u], sacc[0]);
@@ -569,6 +572,9 @@ prefill_kernel(PrefillParams p) {
         // with r = s % 16: one probability per lane.
         bop = sacc[s / 16][s % 16];
       }
+      // All D tiles' V^T operands of this key step are read before their
+      // MFMAs (fenced as above).
+      op_t av[S::kDTiles];
 #pragma unroll
       for (int dt = 0; dt < S::kDTiles; ++dt) {
         op_t a;
@@ -590,8 +596,11 @@ prefill_kernel(PrefillParams p) {
           a = *reinterpret_cast<const float*>(
               s_v + key * S::kRow + ((dim / 4) ^ v_swz<S::kChunks>(key)) * 16 + (dim % 4) * 4);
         }
-        oacc[dt] = M::run(a, bop, oacc[dt]);
+        av[dt] = a;
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int dt = 0; dt < S::kDTiles; ++dt) oacc[dt] = M::run(av[dt], bop, oacc[dt]);
     }
   };
 
