@@ -290,9 +290,11 @@ __device__ __forceinline__ int verify_item(const VerifyParams& p, int ticket, ch
   }
   // Block ids are scalar loads (wave-uniform indices), clamped to the
   // partition's last block (steps past the wave's last block load nothing).
+  // An empty partition (a single-partition item with Lk = 0) reads no id:
+  // its clamped index would lie before the row.
   const int kb_last = kb0 + nblk - 1;
   auto block_id = [&](int jb) __attribute__((always_inline)) {
-    return load_uniform_i32(btab, min(kb0 + wave + kWaves * jb, kb_last));
+    return nblk > 0 ? load_uniform_i32(btab, min(kb0 + wave + kWaves * jb, kb_last)) : 0;
   };
   constexpr int kL = S::kLoads;
   uint4 rb[S::kDepth][2 * kL];   // blocks in flight: K loads, then V loads

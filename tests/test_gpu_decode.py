@@ -372,3 +372,41 @@ def test_partitioned_small_row_route(b, hq, hkv, longest, part, d):
     assert np.all(np.isfinite(got[seqs]))
     err = float(np.max(np.abs(got[seqs] - want[seqs])))
     assert err <= TOL["bf16"], f"max abs err {err}"
+
+
+def test_small_row_route_empty_first_sequence():
+    """A large bf16 batch on the small-row kernel whose first sequence (and
+    another) has context 0: those rows are zero -- an empty item reads no
+    block id, not even the clamped one before its table row -- and the
+    others match the oracle."""
+    import math
+
+    import oracle.attention as oa
+    from paged_kv_cache_slot_amd import metadata as pm
+    from paged_kv_cache_slot_amd import ops
+    from tests.gpu_harness import dev_i32
+    say("decode small-row route, empty first sequence")
+    hq, hkv, d, n = 32, 8, 128, 259
+    rng = np.random.default_rng(811)
+    lens = rng.integers(1, 3000, n, endpoint=True)
+    lens[0] = 0
+    lens[7] = 0
+    lay = wl.decode_layout(lens.tolist(), 16, seed=812)
+    kc, vc = wl.fill_pool(lay.num_blocks, 16, hkv, d, "bf16", 813, "cuda")
+    wl.poison_unused(kc, vc, wl.valid_slot_mask(lay.num_blocks, 16, lay.tables,
+                                                lay.lens))
+    q = wl.make_values((n, hq, d), "bf16", 814, "cuda")
+    meta = pm.decode_inputs(lay.tables, lay.lens, 16)
+    out = ops.decode(q, kc, vc, dev_i32(meta["block_tables"]),
+                     dev_i32(meta["context_lens"]), meta["max_context_len"],
+                     scale=1.0 / math.sqrt(d))
+    torch.cuda.synchronize()
+    got = f64(out)
+    assert np.all(got[0] == 0.0) and np.all(got[7] == 0.0)
+    seqs = sorted({1, 2, n - 1} | {s + 1 for s in sample_seqs(lens[1:], 6, seed=815)})
+    want = oa.decode_attention(wl.host_bits(q), wl.host_bits(kc), wl.host_bits(vc),
+                               meta["block_tables"], meta["context_lens"],
+                               1.0 / math.sqrt(d), "bf16", seqs=seqs)
+    assert np.all(np.isfinite(got[seqs]))
+    err = float(np.max(np.abs(got[seqs] - want[seqs])))
+    assert err <= TOL["bf16"], err
