@@ -377,6 +377,8 @@ pa_status pa_decode_shared_prefix(
   pre.block_tables = block_tables;
   pre.max_blocks_per_seq = max_blocks_per_seq;
   pre.prefix_lens = prefix_lens;
+  pre.context_lens = context_lens;
+  pre.max_context_len = static_cast<int>(max_len);
   pre.groups = groups;
   pre.num_groups = num_groups;
   pre.max_group_size = max_group_size;

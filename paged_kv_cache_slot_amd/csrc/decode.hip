@@ -231,6 +231,9 @@ struct DecodeParams {
   // Longest-first without a plan kernel (plain decode, at most 64
   // sequences): each wave ranks its item itself (ranked_item).
   int inline_rank;
+  // Host side only: `order` was written by an earlier kernel on the same
+  // stream (the shared-prefix pass), so no plan kernel runs.
+  int order_ready;
 };
 
 // First token of the partitions: 0, or the block-aligned shared prefix.
@@ -975,7 +978,7 @@ hipError_t launch_typed(const DecodeParams& prm, int num_seqs, int num_kv_heads,
   const int64_t wgs = static_cast<int64_t>(prm.num_partitions) * num_kv_heads * num_seqs;
   if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
   dim3 grid(static_cast<unsigned>(wgs));
-  if (prm.order != nullptr) {
+  if (prm.order != nullptr && !prm.order_ready) {
     hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream,
                        prm, const_cast<int32_t*>(prm.order));
     hipError_t e = hipGetLastError();
@@ -1121,7 +1124,15 @@ SharedPrefixPlan plan_shared_prefix(int num_seqs, int num_heads,
   plan.suffix.off_order = 0;
   plan.suffix.use_order = false;
   plan.suffix.inline_rank = false;   // the items start at the shared prefix
-  if (plan_order(plan.suffix, num_seqs, num_kv_heads)) {
+  // When the prefix pass runs, its last workgroup writes the suffix
+  // schedule for free (the pass is on the critical path anyway); the suffix
+  // workgroups then start longest first even with one partition, where
+  // natural order left the longest suffixes to start late.  Otherwise the
+  // plain-decode rule (a plan kernel for large multi-partition grids).
+  plan.order_in_prefix = num_groups > 0 && max_group_size > 0 && plan.prefix_chunks > 0;
+  if (plan.order_in_prefix) plan.suffix.use_order = true;
+  else plan_order(plan.suffix, num_seqs, num_kv_heads);
+  if (plan.suffix.use_order) {
     plan.suffix.off_order = plan.workspace_bytes;
     plan.workspace_bytes += align256(static_cast<size_t>(num_seqs) *
                                      plan.suffix.num_partitions * sizeof(int32_t));
@@ -1232,8 +1243,10 @@ hipError_t launch_decode_suffix(const DecodeArgs& a, const SharedPrefixPlan& pla
   prm.ws_sum = reinterpret_cast<float*>(ws + plan.off_sum);
   prm.ws_acc = reinterpret_cast<float*>(ws + plan.off_acc);
   prm.ws_acc_h = reinterpret_cast<uint16_t*>(ws + plan.off_acc);
-  if (plan.suffix.use_order)
+  if (plan.suffix.use_order) {
     prm.order = reinterpret_cast<int32_t*>(ws + plan.suffix.off_order);
+    prm.order_ready = plan.order_in_prefix ? 1 : 0;
+  }
   return dispatch_decode(prm, a, stream);
 }
 

@@ -89,6 +89,9 @@ struct SharedPrefixPlan {
   int prefix_chunk_tokens;   // keys per prefix partial, multiple of 64
   int prefix_chunks;         // prefix partial slots per (sequence, head)
   int total_slots;           // suffix.num_partitions + prefix_chunks
+  // The prefix pass runs, and its last workgroup writes the suffix pass's
+  // longest-first schedule at suffix.off_order (no plan kernel).
+  bool order_in_prefix;
   size_t workspace_bytes;
   size_t off_max, off_sum, off_acc;  // [B, Hq, total_slots] (acc: x D)
 };
@@ -116,6 +119,8 @@ struct PrefixArgs {
   const int32_t* block_tables;
   int max_blocks_per_seq;
   const int32_t* prefix_lens;   // [num_seqs]
+  const int32_t* context_lens;  // [num_seqs]: for the suffix schedule
+  int max_context_len;          // the suffix pass's bound on context_lens
   const int32_t* groups;        // [num_groups, 2]: first sequence, count
   int num_groups;
   int max_group_size;

@@ -165,6 +165,19 @@ struct PrefillParams {
   uint16_t* ws_acc_h;  // same memory: binary16 acc / sum (bfloat16 I/O)
   int ws_stride;
   int slot0;
+  // Group mode: one more workgroup, the grid's last, writes the suffix
+  // pass's schedule instead of a partial (null: none).  Entry r of
+  // suffix_order is the (partition * order_seqs + b) item the suffix kernel's
+  // workgroups r * Hkv .. r * Hkv + Hkv - 1 take, longest first; the weight
+  // of an item is its suffix tokens in that partition, as the suffix kernel
+  // clamps them (context_lens[b] to order_max_len and the block table,
+  // starting at prefix_lens[b] rounded down to a block).
+  int32_t* suffix_order;
+  const int32_t* context_lens;
+  int order_seqs;
+  int order_parts;
+  int order_part_tokens;
+  int order_max_len;
 };
 
 // Keys an M-tile reads: the causal limit of its last row, or all lk.
@@ -187,6 +200,25 @@ __device__ __forceinline__ int item_weight(const SeqExtent& e, int item,
   if (m0 >= e.lq * group) return 0;
   const int w = (tile_key_end(e, group, m0, bm, causal) + kBN - 1) / kBN + 1;
   return w < kPlanBins ? w : kPlanBins - 1;
+}
+
+// Weight bin of suffix item `item` (16-token bins, the last one shared by
+// everything longer) for the suffix pass's longest-first schedule.
+constexpr int kSuffixBins = 1024;
+__device__ __forceinline__ int suffix_bin(const PrefillParams& p, int item) {
+  const int b = item % p.order_seqs;
+  const int part = item / p.order_seqs;
+  int len = p.context_lens[b];
+  len = len < 0 ? 0 : (len > p.order_max_len ? p.order_max_len : len);
+  const int cap = p.max_blocks_per_seq * kBlock;
+  len = len > cap ? cap : len;
+  int st = p.prefix_lens[b];
+  st = st < 0 ? 0 : (st > len ? len : st);
+  st -= st % kBlock;
+  int n = len - st - part * p.order_part_tokens;
+  n = n < 0 ? 0 : (n > p.order_part_tokens ? p.order_part_tokens : n);
+  const int bin = (n + kBlock - 1) / kBlock;
+  return bin < kSuffixBins ? bin : kSuffixBins - 1;
 }
 
 template <int kChunks>
@@ -255,6 +287,16 @@ prefill_kernel(PrefillParams p) {
   // with its own L2; with Hkv a multiple of 8 every M-tile of one (sequence,
   // KV head) group, which all read the same K/V tiles, runs on one XCD.
   const int lin = blockIdx.x;
+  if (p.suffix_order != nullptr && lin == static_cast<int>(gridDim.x) - 1) {
+    // The suffix pass's schedule (it starts after this kernel ends), built
+    // beside the prefix partials instead of by a plan kernel of its own.
+    // LDS: the bins, then the wave totals.
+    int* bins = reinterpret_cast<int*>(smem);
+    longest_first_order<S::kThreads, kSuffixBins, 2>(
+        p.order_seqs * p.order_parts, [&](int it) { return suffix_bin(p, it); },
+        p.suffix_order, bins, bins + kSuffixBins);
+    return;
+  }
   const int kvh = lin % p.num_kv_heads;
   const int rank = lin / p.num_kv_heads;
   const int tid = threadIdx.x;
@@ -798,7 +840,8 @@ hipError_t launch_typed(const PrefillParams& prm, const PrefillArgs& a,
   return launch_kernel<T, D, G>(pr, wgs, stream);
 }
 
-// Shared-prefix partials: group mode of the same kernel, natural order.
+// Shared-prefix partials: group mode of the same kernel, natural order;
+// with plan.order_in_prefix one more workgroup writes the suffix schedule.
 template <typename T, int D, int G>
 hipError_t launch_prefix_typed(const PrefillParams& prm, const PrefixArgs& a,
                                const SharedPrefixPlan& plan, hipStream_t stream) {
@@ -809,14 +852,25 @@ hipError_t launch_prefix_typed(const PrefillParams& prm, const PrefixArgs& a,
   pr.mtiles = m_tiles(a.max_group_size, G, S::kBM);
   const int64_t items = static_cast<int64_t>(a.num_groups) * plan.prefix_chunks;
   const int64_t wgs = items * pr.mtiles * a.num_kv_heads;
-  if (items > 0x7fffffff || wgs > 0x7fffffff) return hipErrorNotSupported;
+  if (items > 0x7fffffff || wgs + 1 > 0x7fffffff) return hipErrorNotSupported;
   pr.num_seqs = static_cast<int>(items);
   pr.order = nullptr;
   pr.rank_inline = 0;
   pr.group_mode = 1;
   pr.chunk_tiles = plan.prefix_chunk_tokens / kBN;
   pr.chunks = plan.prefix_chunks;
-  return launch_kernel<T, D, G>(pr, wgs, stream);
+  if (!plan.order_in_prefix) return launch_kernel<T, D, G>(pr, wgs, stream);
+  static_assert(kSuffixBins % S::kThreads == 0, "bins per thread");
+  static_assert((kSuffixBins + S::kThreads / kWave) * sizeof(int) <= S::kLds,
+                "schedule LDS");
+  pr.suffix_order = reinterpret_cast<int32_t*>(static_cast<char*>(a.workspace) +
+                                               plan.suffix.off_order);
+  pr.context_lens = a.context_lens;
+  pr.order_seqs = a.num_seqs;
+  pr.order_parts = plan.suffix.num_partitions;
+  pr.order_part_tokens = plan.suffix.partition_tokens;
+  pr.order_max_len = a.max_context_len;
+  return launch_kernel<T, D, G>(pr, wgs + 1, stream);
 }
 
 template <typename T, int D>

@@ -162,3 +162,50 @@ def test_large_values_prefix_partials():
     assert big > 65504
     err = float(np.max(np.abs(got - want)))
     assert err <= big * 2.0 ** -7, (err, big)
+
+
+@pytest.mark.parametrize("spec,seed", [
+    ([(3, [60, 49, 100, 200]), (0, [33]), (5, [81, 300, 97]), (0, [1, 17]),
+      (2, [40, 33])], 95),
+    ([(20, [1000, 2100, 340, 800]), (0, [1500]), (6, [97, 700])], 97),
+])
+def test_suffix_schedule_from_prefix_pass(spec, seed):
+    """The prefix pass's last workgroup writes the suffix pass's schedule
+    (the last array of the workspace): a permutation of the (partition,
+    sequence) items whose suffix tokens never increase, one or several
+    512-token partitions.  The output still matches the oracle."""
+    say("shared prefix suffix schedule", seed)
+    hq, hkv, d = 32, 8, 128
+    case = DecodeCase(_grouped_layout(spec, seed), hq, hkv, d, "bf16",
+                      seed=seed + 1)
+    case.run_store()
+    sp = pm.shared_prefix_inputs(case.tables, case.lens, case.bs)
+    b = len(case.lens)
+    ng = int(sp["groups"].shape[0])
+    need = ops.shared_prefix_workspace_bytes(
+        b, hq, hkv, d, sp["max_suffix_len"], sp["max_prefix_len"], ng,
+        sp["max_group_size"])
+    ws = torch.full((need,), 0xEE, dtype=torch.uint8, device=case.q.device)
+    out = ops.decode_shared_prefix(
+        case.q, case.kc, case.vc, case.block_tables, case.context_lens,
+        dev_i32(sp["prefix_lens"]), dev_i32(sp["groups"].reshape(-1, 2)),
+        sp["max_suffix_len"], sp["max_prefix_len"], sp["max_group_size"],
+        scale=case.scale, workspace=ws)
+    torch.cuda.synchronize()
+    part = 512
+    nparts = max(1, -(-int(sp["max_suffix_len"]) // part))
+    n = b * nparts
+    off = need - (n * 4 + 255) // 256 * 256
+    order = ws[off:off + n * 4].cpu().numpy().view(np.int32)
+    assert sorted(order.tolist()) == list(range(n)), order
+    lens = np.asarray(case.lens, dtype=np.int64)
+    start = np.asarray(sp["prefix_lens"], dtype=np.int64)
+    start -= start % case.bs
+    item = np.arange(n)
+    toks = np.clip(lens[item % b] - start[item % b] - (item // b) * part, 0, part)
+    bins = (toks + case.bs - 1) // case.bs
+    assert np.all(np.diff(bins[order]) <= 0), bins[order]
+    ek, ev = case.oracle_store()
+    want = case.oracle_decode(ek, ev)
+    err = float(np.max(np.abs(f64(out) - want)))
+    assert err <= TOL["bf16"], f"max abs err {err}"
