@@ -148,13 +148,13 @@ struct PrefillParams {
   int num_kv_heads;
   float scale_log2;
   int causal;
-  // Shared-prefix partials (group mode): item b = group * chunks + chunk;
-  // the group's members are query rows groups[2g] .. + groups[2g + 1] - 1,
-  // its keys the first prefix_lens[groups[2g]] tokens (rounded down to a
-  // block) of that first member's table, non-causal, tiles chunk *
-  // chunk_tiles .. + chunk_tiles - 1.  Output: partials in the decode
-  // workspace layout, slot slot0 + chunk of each (row, head).
-  int group_mode;
+  // Shared-prefix partials (group mode, the kGroup kernel): item b =
+  // group * chunks + chunk; the group's members are query rows groups[2g]
+  // .. + groups[2g + 1] - 1, its keys the first prefix_lens[groups[2g]]
+  // tokens (rounded down to a block) of that first member's table,
+  // non-causal, tiles chunk * chunk_tiles .. + chunk_tiles - 1.  Output:
+  // partials in the decode workspace layout, slot slot0 + chunk of each
+  // (row, head).
   const int32_t* groups;
   const int32_t* prefix_lens;
   int chunk_tiles;
@@ -270,7 +270,11 @@ __device__ __forceinline__ float bf16_weights(const f32x16_v (&s)[2], float scal
 // Two waves per SIMD (8-wave shapes): one wave's softmax overlaps the
 // other's MFMAs.  fp32 with D = 128 runs one wave per SIMD: no register cap
 // there (it would only spill).
-template <typename T, int D, int G>
+// kGroup: the shared-prefix partials (group mode), a kernel of its own, so
+// that the varlen kernel carries none of its code.  It requests the first
+// block ids and the Q rows before the prefix length arrives (neither
+// depends on it).
+template <typename T, int D, int G, bool kGroup>
 __global__ __launch_bounds__((PrefillShape<T, D>::kThreads)) __attribute__((amdgpu_waves_per_eu(
     PrefillShape<T, D>::kOccupancy, PrefillShape<T, D>::kOccupancy))) void
 prefill_kernel(PrefillParams p) {
@@ -287,7 +291,7 @@ prefill_kernel(PrefillParams p) {
   // with its own L2; with Hkv a multiple of 8 every M-tile of one (sequence,
   // KV head) group, which all read the same K/V tiles, runs on one XCD.
   const int lin = blockIdx.x;
-  if (p.suffix_order != nullptr && lin == static_cast<int>(gridDim.x) - 1) {
+  if (kGroup && p.suffix_order != nullptr && lin == static_cast<int>(gridDim.x) - 1) {
     // The suffix pass's schedule (it starts after this kernel ends), built
     // beside the prefix partials instead of by a plan kernel of its own.
     // LDS: the bins, then the wave totals.
@@ -330,7 +334,7 @@ prefill_kernel(PrefillParams p) {
   int kt0 = 0;              // first key tile of this workgroup
   int chunk = 0;            // group mode: which prefix partial
   int table_row = b;        // block-table row of the keys
-  if (p.group_mode) {
+  if constexpr (kGroup) {
     const int g = b / p.chunks;
     chunk = b % p.chunks;
     int first = p.groups[2 * g];
@@ -339,11 +343,7 @@ prefill_kernel(PrefillParams p) {
     cnt = cnt < 0 ? 0 : (cnt > p.max_seqlen_q ? p.max_seqlen_q : cnt);
     if (first >= p.total_q) cnt = 0;
     else if (first + cnt > p.total_q) cnt = static_cast<int>(p.total_q - first);
-    int pl = cnt > 0 ? p.prefix_lens[first] : 0;
-    pl = pl < 0 ? 0 : (pl > p.max_seqlen_k ? p.max_seqlen_k : pl);
-    if (pl > p.max_blocks_per_seq * kBlock) pl = p.max_blocks_per_seq * kBlock;
-    pl -= pl % kBlock;
-    ext = {first, cnt, pl};
+    ext = {first, cnt, 0};   // keys: the prefix length, loaded below
     kt0 = chunk * p.chunk_tiles;
     table_row = first;
   } else {
@@ -352,32 +352,19 @@ prefill_kernel(PrefillParams p) {
   }
   const int q0 = ext.q0;
   const int lq = ext.lq;
-  const int lk = ext.lk;
   const int mrows = lq * G;
   const int m0 = mtile * S::kBM;
   if (m0 >= mrows) return;                   // uniform over the workgroup
-
-  // Key tiles this workgroup reads: kt0 .. kt0 + ntiles - 1.
-  int ntiles = (tile_key_end(ext, G, m0, S::kBM, p.causal) + kBN - 1) / kBN;
-  if (p.group_mode) {
-    ntiles = min(ntiles - kt0, p.chunk_tiles);
-    if (ntiles <= 0) return;   // past this group's prefix: never merged
-  }
 
   // This lane's row: M row m -> query position i, head h.
   const int m = m0 + wave * 32 + j;
   const bool row_ok = m < mrows;
   const int i_pos = row_ok ? m / G : 0;
   const int h = m % G;
-  // Last key this row may see.
-  const int lim = row_ok ? (p.causal ? lk - lq + i_pos : lk - 1) : lk - 1;
-  // Smallest limit of the wave: tiles entirely below it need no mask.
-  const int wave_m0 = m0 + wave * 32;
-  const int wave_lim = p.causal ? lk - lq + min(wave_m0 / G, lq - 1) : lk - 1;
 
   // Q^T as the B operand: lane (j, hh) holds dims s * kK + hh * kPer + e.
   op_t qb[S::kQSteps];
-  {
+  auto load_q = [&]() __attribute__((always_inline)) {
     const char* qrow = p.q + ((static_cast<int64_t>(q0) + i_pos) * p.num_heads +
                               kvh * G + h) * S::kRow;
 #pragma unroll
@@ -390,7 +377,46 @@ prefill_kernel(PrefillParams p) {
                        : 0.f;
       }
     }
+  };
+  // A wave's rows of a tile lie in one cache block: block wave_blk of the
+  // tile's blocks.
+  const int wave_blk = wave * S::kDmaPerWave * S::kRowsPerDma / kBlock;
+  const int32_t* btab = p.block_tables +
+                        static_cast<int64_t>(table_row) * p.max_blocks_per_seq;
+  // Group mode: the ids of the first kStages tiles' blocks, requested with
+  // the Q rows before the prefix length is known (clamped to the table row
+  // instead of the context; a tile past the context reads block 0 anyway).
+  int blk_pre[S::kStages];
+  if constexpr (kGroup) {
+    load_q();
+#pragma unroll
+    for (int st = 0; st < S::kStages; ++st)
+      blk_pre[st] = p.max_blocks_per_seq > 0
+                        ? load_uniform_i32(btab, min((kt0 + st) * (kBN / kBlock) + wave_blk,
+                                                     p.max_blocks_per_seq - 1))
+                        : 0;
+    int pl = lq > 0 ? p.prefix_lens[q0] : 0;
+    pl = pl < 0 ? 0 : (pl > p.max_seqlen_k ? p.max_seqlen_k : pl);
+    if (pl > p.max_blocks_per_seq * kBlock) pl = p.max_blocks_per_seq * kBlock;
+    pl -= pl % kBlock;
+    ext.lk = pl;
   }
+  const int lk = ext.lk;
+
+  // Key tiles this workgroup reads: kt0 .. kt0 + ntiles - 1.
+  int ntiles = (tile_key_end(ext, G, m0, S::kBM, p.causal) + kBN - 1) / kBN;
+  if constexpr (kGroup) {
+    ntiles = min(ntiles - kt0, p.chunk_tiles);
+    if (ntiles <= 0) return;   // past this group's prefix: never merged
+  }
+
+  // Last key this row may see.
+  const int lim = row_ok ? (p.causal ? lk - lq + i_pos : lk - 1) : lk - 1;
+  // Smallest limit of the wave: tiles entirely below it need no mask.
+  const int wave_m0 = m0 + wave * 32;
+  const int wave_lim = p.causal ? lk - lq + min(wave_m0 / G, lq - 1) : lk - 1;
+
+  if constexpr (!kGroup) load_q();
 
   // Q must have arrived before the tile loop: a wait for it inside the loop
   // would also wait for the K/V loads in flight there.
@@ -404,8 +430,6 @@ prefill_kernel(PrefillParams p) {
 
   const int64_t row_stride = static_cast<int64_t>(p.num_kv_heads) * S::kRow;
   const int64_t blk_bytes = row_stride * kBlock;
-  const int32_t* btab = p.block_tables +
-                        static_cast<int64_t>(table_row) * p.max_blocks_per_seq;
   const int nblk_ctx = (lk + kBlock - 1) / kBlock;   // blocks the context owns
 
   // DMA load q of this wave moves tile rows r0 .. r0 + kRowsPerDma - 1 (one
@@ -431,7 +455,6 @@ prefill_kernel(PrefillParams p) {
   // (Only called with ntiles >= 1, so the context owns a block; the load
   // is unconditional, from a clamped index, so that nothing waits for it
   // before its use one iteration later.)
-  const int wave_blk = wave * S::kDmaPerWave * S::kRowsPerDma / kBlock;
   auto block_id = [&](int kt) __attribute__((always_inline)) {
     return load_uniform_i32(btab, min(kt * (kBN / kBlock) + wave_blk, nblk_ctx - 1));
   };
@@ -657,8 +680,11 @@ prefill_kernel(PrefillParams p) {
   // Local tile i is key tile kt0 + i and lives in stage i % kStages.
 #pragma unroll
   for (int st = 0; st < S::kStages - 1; ++st)
-    if (st < ntiles) dma_tile(kt0 + st, block_id(kt0 + st), kbuf(st), vbuf(st));
-  int next_blk = ntiles > 0 ? block_id(kt0 + S::kStages - 1) : 0;
+    if (st < ntiles)
+      dma_tile(kt0 + st, kGroup ? blk_pre[st] : block_id(kt0 + st), kbuf(st), vbuf(st));
+  int next_blk = ntiles > 0 ? (kGroup ? blk_pre[S::kStages - 1]
+                                      : block_id(kt0 + S::kStages - 1))
+                            : 0;
   for (int it = 0; it < ntiles; ++it) {
     const int ahead = min(S::kStages - 2, ntiles - 1 - it);   // tiles after it in flight
     if (S::kStages >= 3 && ahead >= 1)
@@ -679,7 +705,7 @@ prefill_kernel(PrefillParams p) {
   // of each 32-dim tile for its row.
   const float total = run_sum + swap_halves(run_sum);
   if (!row_ok) return;
-  if (p.group_mode) {
+  if constexpr (kGroup) {
     // A partial: its output (bf16 I/O: normalised, binary16; fp32 I/O: the
     // unnormalised fp32 sum), its reference max and its sum.
     const int64_t slot =
@@ -780,7 +806,7 @@ int m_tiles(int max_seqlen_q, int group, int bm) {
   return static_cast<int>((static_cast<int64_t>(max_seqlen_q) * group + bm - 1) / bm);
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool kGroup>
 hipError_t launch_kernel(const PrefillParams& pr, int64_t wgs, hipStream_t stream) {
   using S = PrefillShape<T, D>;
   const size_t lds = S::kLds;
@@ -788,13 +814,13 @@ hipError_t launch_kernel(const PrefillParams& pr, int64_t wgs, hipStream_t strea
     static bool raised = false;   // once per kernel instantiation
     if (!raised) {
       hipError_t e = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&prefill_kernel<T, D, G>),
+          reinterpret_cast<const void*>(&prefill_kernel<T, D, G, kGroup>),
           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
       if (e != hipSuccess) return e;
       raised = true;
     }
   }
-  hipLaunchKernelGGL((prefill_kernel<T, D, G>), dim3(static_cast<unsigned>(wgs)),
+  hipLaunchKernelGGL((prefill_kernel<T, D, G, kGroup>), dim3(static_cast<unsigned>(wgs)),
                      dim3(S::kThreads), lds, stream, pr);
   return hipGetLastError();
 }
@@ -837,7 +863,7 @@ hipError_t launch_typed(const PrefillParams& prm, const PrefillArgs& a,
     pr.order = order;
   }
   (void)lds;
-  return launch_kernel<T, D, G>(pr, wgs, stream);
+  return launch_kernel<T, D, G, false>(pr, wgs, stream);
 }
 
 // Shared-prefix partials: group mode of the same kernel, natural order;
@@ -856,10 +882,9 @@ hipError_t launch_prefix_typed(const PrefillParams& prm, const PrefixArgs& a,
   pr.num_seqs = static_cast<int>(items);
   pr.order = nullptr;
   pr.rank_inline = 0;
-  pr.group_mode = 1;
   pr.chunk_tiles = plan.prefix_chunk_tokens / kBN;
   pr.chunks = plan.prefix_chunks;
-  if (!plan.order_in_prefix) return launch_kernel<T, D, G>(pr, wgs, stream);
+  if (!plan.order_in_prefix) return launch_kernel<T, D, G, true>(pr, wgs, stream);
   static_assert(kSuffixBins % S::kThreads == 0, "bins per thread");
   static_assert((kSuffixBins + S::kThreads / kWave) * sizeof(int) <= S::kLds,
                 "schedule LDS");
@@ -870,7 +895,7 @@ hipError_t launch_prefix_typed(const PrefillParams& prm, const PrefixArgs& a,
   pr.order_parts = plan.suffix.num_partitions;
   pr.order_part_tokens = plan.suffix.partition_tokens;
   pr.order_max_len = a.max_context_len;
-  return launch_kernel<T, D, G>(pr, wgs + 1, stream);
+  return launch_kernel<T, D, G, true>(pr, wgs + 1, stream);
 }
 
 template <typename T, int D>
