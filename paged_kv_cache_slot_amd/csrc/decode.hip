@@ -343,6 +343,47 @@ __device__ __forceinline__ float merge_head(const DecodeParams& p, int64_t head,
   }, m0, l0, o0);
 }
 
+// The same merge (merge_partials, one group) over up to kPre prefix
+// partials already in registers: maxima pm, stored sums pl (negative: the
+// output is stored scaled), binary16 outputs po; (m, l, o) is this
+// partition's partial.  Slots past n are dropped by index.
+template <int kPre>
+__device__ __forceinline__ float merge_prefetched(int n, const float (&pm)[kPre],
+                                                  const float (&pl)[kPre],
+                                                  const uint16_t (&po)[kPre], float m,
+                                                  float l, float o) {
+  float mv[kPre], sv[kPre], av[kPre];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) {
+    const bool in = u < n;
+    const float lr = fabsf(pl[u]);
+    const float ov = f16_to_f32(po[u]);
+    mv[u] = in ? pm[u] : -INFINITY;
+    sv[u] = in ? lr : 0.f;
+    av[u] = in ? lr * (pl[u] < 0.f ? ov * kPartialGrow : ov) : 0.f;
+  }
+  float gm = m;
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) gm = fmaxf(gm, mv[u]);
+  if (gm != -INFINITY) {
+    if (gm > m) {
+      const float a = m == -INFINITY ? 0.f : fast_exp2(m - gm);
+      l *= a;
+      o *= a;
+      m = gm;
+    }
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      if (u < n) {
+        const float w = fast_exp2(mv[u] - m);
+        l = fmaf(w, sv[u], l);
+        o = fmaf(w, av[u], o);
+      }
+    }
+  }
+  return (m == -INFINITY || !(l > 0.f)) ? 0.f : o / l;
+}
+
 template <typename T, int D, int G, int C, bool F8>
 __global__ __launch_bounds__(kThreads) __attribute__((
     amdgpu_waves_per_eu(DecodeShape<T, D, G, C, F8>::kMinWaves, 8))) void
@@ -410,6 +451,40 @@ decode_partition_kernel(
   const int part_end = min(len, t0 + p.partition_tokens);
   const int32_t* brow = p.block_tables +
                         static_cast<int64_t>(b) * p.max_blocks_per_seq;
+
+  // Shared-prefix decode whose suffix is this one partition (bf16, one head
+  // per wave, at most kPre prefix partials): the prefix pass finished before
+  // this kernel started, so the loads of the partials this partition merges
+  // with at the end go out now, ahead of the K/V stream, instead of after
+  // it.  Wave w holds head head0 + w's; maxima and sums are uniform.  Only
+  // the shapes with registers to spare (3 waves per SIMD, G = 4): at 5
+  // waves per SIMD the G <= 2 shapes would spill.
+  constexpr bool kPrefetch = sizeof(T) == 2 && !F8 && G == 4 && G <= kWaves;
+  constexpr int kPre = 8;
+  constexpr int kDpl = D / kWave;   // output dimensions per lane
+  float pre_m[kPre], pre_l[kPre];
+  uint16_t pre_o[kDpl][kPre];
+  int npre_held = -1;               // partials held in registers (-1: none)
+  if constexpr (kPrefetch) {
+    if (p.merge_prefix && wave < G) {
+      const int npre = prefix_partials(p, t0);
+      if (npre >= 1 && npre <= kPre) {
+        const int64_t slot0 =
+            (static_cast<int64_t>(b) * p.num_heads + head0 + wave) * p.ws_stride +
+            p.num_partitions;
+#pragma unroll
+        for (int k = 0; k < kPre; ++k) {
+          const int64_t slot = slot0 + (k < npre ? k : npre - 1);
+          pre_m[k] = p.ws_max[slot];
+          pre_l[k] = p.ws_sum[slot];
+#pragma unroll
+          for (int e = 0; e < kDpl; ++e)
+            pre_o[e][k] = p.ws_acc_h[slot * D + e * kWave + lane];
+        }
+        npre_held = npre;
+      }
+    }
+  }
 
   // Running softmax state of the partition (max and sum per head) lives in
   // LDS; each lane keeps its share of the unnormalised output.
@@ -813,8 +888,16 @@ decode_partition_kernel(
     }
     if (p.merge_prefix) {
       // This partition (the whole suffix) joins the prefix partials.
-      const int npre = prefix_partials(p, t0);
       T* out = reinterpret_cast<T*>(p.out) + head * D;
+      if (kPrefetch && npre_held >= 0) {   // h == wave: one head per wave
+#pragma unroll
+        for (int e = 0; e < D / kWave; ++e)
+          store_out<T>(out + e * kWave + lane,
+                       merge_prefetched<kPre>(npre_held, pre_m, pre_l, pre_o[e],
+                                              s_mrun[h], l, ov[e]) * p.v_scale);
+        continue;
+      }
+      const int npre = prefix_partials(p, t0);
 #pragma unroll
       for (int e = 0; e < D / kWave; ++e)
         store_out<T>(out + e * kWave + lane,
