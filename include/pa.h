@@ -286,7 +286,8 @@ pa_status pa_prefill_varlen(void* out, const void* q, int64_t total_q,
 
 /* Bytes of workspace pa_decode_shared_prefix needs for these sizes (> 0
  * whenever num_seqs > 0): partial results, one slot per suffix partition and
- * per prefix chunk, for each (sequence, query head). */
+ * per prefix chunk, for each (sequence, query head), and the suffix pass's
+ * schedule (one int32 per (sequence, suffix partition)) where it uses one. */
 size_t pa_decode_shared_prefix_workspace_bytes(
     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
     int32_t head_dim, int32_t max_suffix_len, int32_t max_prefix_len,
