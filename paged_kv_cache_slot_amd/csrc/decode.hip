@@ -1176,8 +1176,11 @@ DecodePlan plan_decode(int num_seqs, int num_heads, int num_kv_heads,
 
 // Shared-prefix plan: the suffix partitions as for plain decode (over the
 // longest suffix), plus prefix partials of prefix_chunk_tokens keys each.
-// The chunk length aims at ~128 prefix workgroups in all (an M-tile of the
-// prefix pass holds 256 rows), and is at least two 64-key tiles.
+// The chunk length aims at ~128 (256-row M-tile, key chunk) pieces of the
+// prefix pass in all -- ~128 workgroups of the fp32 shapes, ~256 of the
+// bf16 group-mode kernel, whose M-tiles hold 128 rows -- and is at least
+// two 64-key tiles.  More, shorter chunks would shorten the pass but give
+// every suffix workgroup more partials to merge.
 SharedPrefixPlan plan_shared_prefix(int num_seqs, int num_heads,
                                     int num_kv_heads, int head_dim,
                                     int max_suffix_len, int max_prefix_len,

@@ -88,7 +88,7 @@ struct Mma<float> {
   }
 };
 
-template <typename T, int D>
+template <typename T, int D, bool kGroup = false>
 struct PrefillShape {
   static constexpr int kElem = ElemTraits<T>::kBytes;
   static constexpr int kRow = D * kElem;                  // bytes per key row
@@ -106,10 +106,14 @@ struct PrefillShape {
   // and with one workgroup per CU the LDS holds three K/V stages (tile
   // kt + 2 in flight while tile kt is computed).  fp32 with D = 128 needs
   // one wave per SIMD: 4 waves, two stages (128 KiB).
-  static constexpr int kWaves = (kBf16 || D == 64) ? 8 : 4;
+  // bf16 group mode (shared-prefix partials, a few key tiles per
+  // workgroup, too few workgroups of 256 rows to fill the chip): 4 waves
+  // and 128 rows, two stages (64 KiB), two workgroups per CU.
+  static constexpr bool kSmallGroup = kGroup && kBf16;
+  static constexpr int kWaves = kSmallGroup ? 4 : ((kBf16 || D == 64) ? 8 : 4);
   static constexpr int kStages = kWaves == 8 ? 3 : 2;
   static constexpr size_t kLds = 2 * kStages * static_cast<size_t>(kTile);
-  static constexpr int kOccupancy = kWaves == 8 ? 2 : 1;   // waves per SIMD
+  static constexpr int kOccupancy = (kWaves == 8 || kSmallGroup) ? 2 : 1;   // waves per SIMD
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kBM = kWaves * 32;                 // M rows per workgroup
   static constexpr int kRowsPerDma = 1024 / kRow;         // rows per 1 KiB DMA
@@ -275,10 +279,10 @@ __device__ __forceinline__ float bf16_weights(const f32x16_v (&s)[2], float scal
 // block ids and the Q rows before the prefix length arrives (neither
 // depends on it).
 template <typename T, int D, int G, bool kGroup>
-__global__ __launch_bounds__((PrefillShape<T, D>::kThreads)) __attribute__((amdgpu_waves_per_eu(
-    PrefillShape<T, D>::kOccupancy, PrefillShape<T, D>::kOccupancy))) void
+__global__ __launch_bounds__((PrefillShape<T, D, kGroup>::kThreads)) __attribute__((amdgpu_waves_per_eu(
+    PrefillShape<T, D, kGroup>::kOccupancy, PrefillShape<T, D, kGroup>::kOccupancy))) void
 prefill_kernel(PrefillParams p) {
-  using S = PrefillShape<T, D>;
+  using S = PrefillShape<T, D, kGroup>;
   using M = Mma<T>;
   typedef typename M::op_t op_t;
   extern __shared__ __align__(16) char smem[];
@@ -808,7 +812,7 @@ int m_tiles(int max_seqlen_q, int group, int bm) {
 
 template <typename T, int D, int G, bool kGroup>
 hipError_t launch_kernel(const PrefillParams& pr, int64_t wgs, hipStream_t stream) {
-  using S = PrefillShape<T, D>;
+  using S = PrefillShape<T, D, kGroup>;
   const size_t lds = S::kLds;
   if (lds > 65536) {
     static bool raised = false;   // once per kernel instantiation
@@ -871,7 +875,7 @@ hipError_t launch_typed(const PrefillParams& prm, const PrefillArgs& a,
 template <typename T, int D, int G>
 hipError_t launch_prefix_typed(const PrefillParams& prm, const PrefixArgs& a,
                                const SharedPrefixPlan& plan, hipStream_t stream) {
-  using S = PrefillShape<T, D>;
+  using S = PrefillShape<T, D, true>;
   if (a.num_groups <= 0 || plan.prefix_chunks <= 0 || a.max_group_size <= 0)
     return hipSuccess;
   PrefillParams pr = prm;
