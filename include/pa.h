@@ -255,7 +255,7 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads,
  *
  * Sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
  * (Lq rows) and Lk = cu_seqlens_k[b+1] - cu_seqlens_k[b] keys, the first Lk
- * tokens of its block table (history and this round's tokens, which the
+ * tokens of its block table (history and this step's tokens, which the
  * caller stored first).  With causal != 0 query row i sits at absolute
  * position Lk - Lq + i and sees keys 0 .. Lk - Lq + i (bottom-right
  * alignment: a chunk continues after its cached history); otherwise every

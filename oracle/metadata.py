@@ -78,12 +78,12 @@ def prefill_metadata(seqs, block_size):
     ``seqs`` is a list of dicts with keys ``block_table`` (list of physical
     block ids, may be empty for sequences that own no cache), ``num_cached``
     (tokens already in the cache) and ``num_scheduled`` (tokens computed this
-    round).
+    step).
 
     ModelRunner page, section 2 (prepare_prefill): the query side holds only
-    the tokens of this round, [start, end); the key side covers [0, end);
+    the tokens of this step, [start, end); the key side covers [0, end);
     cu_seqlens_q / cu_seqlens_k are running sums of those two lengths; the
-    slot of each token of this round follows the block table; a sequence
+    slot of each token of this step follows the block table; a sequence
     without a block table writes no slots; block tables are needed as soon as
     the key total exceeds the query total (a prefix-cache hit or a chunked
     resume).

@@ -100,7 +100,7 @@ def shared_prefix_inputs(tables, lens, block_size):
 
 def prefill_inputs(tables, num_cached, num_scheduled, block_size, width=None):
     """Chunked-prefill batch: sequence b computes tokens
-    [num_cached[b], num_cached[b] + num_scheduled[b]) this round.
+    [num_cached[b], num_cached[b] + num_scheduled[b]) this step.
 
     Returns dict(slot_mapping int32 [total_q], cu_seqlens_q / cu_seqlens_k
     int32 [B+1], max_seqlen_q, max_seqlen_k, block_tables int32 [B, W],

@@ -59,7 +59,7 @@ def test_non_causal():
 
 
 def test_empty_chunks_in_batch():
-    """Sequences with no query rows this round (cu_q[b+1] == cu_q[b])."""
+    """Sequences with no query rows this step (cu_q[b+1] == cu_q[b])."""
     say("prefill empty chunks")
     lay = wl.prefill_layout([10, 200, 0, 31], [0, 50, 9, 0], 16, seed=15)
     _check(PrefillCase(lay, 8, 2, 128, "bf16", seed=16))
