@@ -209,3 +209,16 @@ def test_suffix_schedule_from_prefix_pass(spec, seed):
     want = case.oracle_decode(ek, ev)
     err = float(np.max(np.abs(f64(out) - want)))
     assert err <= TOL["bf16"], f"max abs err {err}"
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (64, 8, 128), (32, 8, 64)])
+def test_group_spans_partial_mtile(hq, hkv, d):
+    """40 members sharing 10 blocks: G x 40 packed rows per KV head (160 or
+    320) fill one or two M-tiles of the group-mode kernel and part of the
+    next; suffixes of 1..120 tokens.  Sampled members against the oracle."""
+    say("shared prefix partial M-tile", hq, hkv, d)
+    rng = np.random.default_rng(99)
+    lens = [160 + int(x) for x in rng.integers(1, 121, size=40)]
+    case = DecodeCase(_grouped_layout([(10, lens)], 98), hq, hkv, d, "bf16",
+                      seed=97)
+    _run(case, seqs=[0, 1, 17, 31, 38, 39], expect_groups=[(0, 40)])
